@@ -1,0 +1,415 @@
+"""Float64 CPU oracle for the chunkwise Kimi Delta Attention (KDA) forward.
+
+TEST INFRASTRUCTURE ONLY. This module is the independent reference that the
+HIP path is checked against. Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import it; the product path never does.
+It shares no code, constants or helpers with the HIP library.
+
+Everything is computed in numpy float64. Inputs given in bf16 or fp32 are
+widened exactly, so the oracle sees the very values the GPU sees.
+
+Sources (the three pages this work is based on):
+  [Blog]     "KDA Doesn't Care About the Future" (drisspg.github.io), sections
+             "Chunkwise KDA in Broad Strokes", "Chunkwise Aqk",
+             "Trace Aqk back to the base recurrence".
+  [K3]       "KDAChunkwise" (Kimi K3 docs), sections "FP32 core and log-space
+             decay", "Constructing the triangular interaction system",
+             "Carrying one state between chunks", "Returning to the model
+             dimension".
+  [Tokamax]  Tokamax "chunk_kda_fwd design doc" (openxla.org), sections
+             3.5, 4.3.2, 9.1.2 (Paper Eq. 1), 9.1.3, 9.1.5 (Paper Eq. 6-7),
+             9.1.6 (Paper Eq. 8-9), 9.1.7, 9.1.8.
+
+Tensor conventions (token-major, the layout the HIP library uses too):
+  q, k, g : [B, T, H, K]   g is the natural-log decay, g <= 0
+  v       : [B, T, H, V]
+  beta    : [B, T, H]
+  initial_state / final_state : [N, H, K, V] with N = B (fixed length) or the
+  number of sequences (variable length, B == 1 and cu_seqlens = [N + 1]).
+
+The steps are small module-level functions on purpose: the test suite swaps
+single steps for plausible mistakes and checks that the pins catch them.
+
+Parity status:
+  kda_recurrent, kda_chunkwise, varlen handling, l2norm,
+  chunk_affine_summary     -> pinned (closed forms, invariants, exact recall,
+                              brute force and cross-checks in tests/).
+  kda_layer_ref            -> partly pinned: its convolution is pinned against
+                              numpy.convolve, its norm and gate by their
+                              defining properties, and causality end to end;
+                              the layer as a whole has no printed values to
+                              match ("parity unpinned" for the composition).
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.linalg import solve_triangular
+from scipy.special import expit
+
+__all__ = [
+    "l2norm",
+    "kda_recurrent",
+    "kda_chunkwise",
+    "chunk_terms",
+    "chunk_affine_summary",
+    "compose_affine",
+    "segments",
+    "kda_layer_ref",
+    "depthwise_causal_conv",
+    "silu",
+    "sigmoid",
+    "rms_norm",
+]
+
+
+# --------------------------------------------------------------------------
+# small elementwise pieces
+# --------------------------------------------------------------------------
+def l2norm(x, eps=1e-6):
+    """x / max(||x||_2, eps) over the last axis.
+
+    [K3] "FP32 core and log-space decay": q and k are unit-normalised along the
+    head dimension with F.normalize and eps=1e-6; [Tokamax] 3.1 lists the same
+    optional q/k L2 normalisation in preprocessing.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    n = np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+    return x / np.maximum(n, eps)
+
+
+def sigmoid(x):
+    return expit(np.asarray(x, dtype=np.float64))
+
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x * sigmoid(x)
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def segments(B, T, cu_seqlens):
+    """List of (batch_row, start, end) segments.
+
+    Fixed length: one segment [0, T) per batch row. Variable length
+    ([Tokamax] 9.1.7): B must be 1 and segment n is [cu[n], cu[n+1]).
+    """
+    if cu_seqlens is None:
+        return [(b, 0, T) for b in range(B)]
+    cu = [int(c) for c in np.asarray(cu_seqlens).reshape(-1)]
+    if B != 1:
+        raise ValueError("variable-length input requires B == 1")
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu[:-1], cu[1:])):
+        raise ValueError("cu_seqlens must be non-decreasing from 0 to T")
+    return [(0, cu[n], cu[n + 1]) for n in range(len(cu) - 1)]
+
+
+# --------------------------------------------------------------------------
+# Oracle R: token recurrence ([Tokamax] 9.1.2, Paper Eq. 1, delta-correction
+# form; [Blog] "Chunkwise KDA in Broad Strokes", steps 0-5)
+# --------------------------------------------------------------------------
+def decay_state(S, g_t):
+    """S_bar = Diag(alpha_t) S with alpha_t = exp(g_t), per key channel."""
+    return np.exp(g_t)[..., :, None] * S
+
+
+def prediction_error(S_bar, k_t, v_t):
+    """e_t = v_t - S_bar^T k_t  (read the value stored at key k_t)."""
+    return v_t - np.einsum("hkv,hk->hv", S_bar, k_t)
+
+
+def delta_write(S_bar, k_t, e_t, beta_t):
+    """S_t = S_bar + beta_t k_t e_t^T  (rank-1 correction at key k_t)."""
+    return S_bar + beta_t[:, None, None] * k_t[:, :, None] * e_t[:, None, :]
+
+
+def read_output(S_t, q_t, scale):
+    """o_t = scale * S_t^T q_t  (read after this token's write)."""
+    return scale * np.einsum("hkv,hk->hv", S_t, q_t)
+
+
+def kda_recurrent(q, k, v, g, beta, scale, initial_state=None, cu_seqlens=None,
+                  use_qk_l2norm=False, eps=1e-6):
+    """Token-by-token KDA recurrence, float64. Returns (o, final_state).
+
+    For each segment and head, S starts at initial_state (zeros if None) and
+    every token applies decay -> prediction error -> delta write -> read, the
+    order fixed by [Tokamax] 9.1.2 ("decay, then correct") and [Blog] steps
+    (0)-(5) (the read uses the state after the current token's write).
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if use_qk_l2norm:
+        q, k = l2norm(q, eps), l2norm(k, eps)
+    segs = segments(B, T, cu_seqlens)
+    o = np.zeros((B, T, H, V))
+    final = np.zeros((len(segs), H, K, V))
+    init = _f64(initial_state)
+    for n, (b, s0, s1) in enumerate(segs):
+        S = np.zeros((H, K, V)) if init is None else init[n].copy()
+        for t in range(s0, s1):
+            S_bar = decay_state(S, g[b, t])
+            e = prediction_error(S_bar, k[b, t], v[b, t])
+            S = delta_write(S_bar, k[b, t], e, beta[b, t])
+            o[b, t] = read_output(S, q[b, t], scale)
+        final[n] = S
+    return o, final
+
+
+# --------------------------------------------------------------------------
+# Oracle C: chunkwise form ([Tokamax] 9.1.3-9.1.6, Paper Eq. 6-9;
+# [K3] "Constructing the triangular interaction system",
+# "Carrying one state between chunks")
+# --------------------------------------------------------------------------
+def chunk_cumsum(g_chunk):
+    """Chunk-local inclusive cumulative log decay, natural log.
+
+    [Tokamax] 9.1.3: G^r sums the gates of positions 1..r of this chunk (the
+    current token included), restarted in every chunk. Kept in natural log
+    here; the pages' log2 form only rescales it.
+    """
+    return np.cumsum(g_chunk, axis=0)
+
+
+def decay_ratio(G):
+    """rho[i, j] = exp(G_i - G_j) for j <= i, 0 above the diagonal.
+
+    [Tokamax] 9.1.3 defines the ratio as the decay a write at j sees by
+    position i; [Blog] "Chunkwise Aqk" explains the j+1..i span. Masked
+    exponents are replaced before exp, so nothing non-finite is formed.
+    Shape: (c, c, H, K).
+    """
+    c = G.shape[0]
+    diff = G[:, None] - G[None, :]
+    causal = np.tril(np.ones((c, c), dtype=bool))
+    diff = np.where(causal[:, :, None, None], diff, -np.inf)
+    return np.exp(diff)
+
+
+def relation_qk(qc, kc, rho, scale):
+    """Aqk[h, i, j] = scale * sum_d q_{i,d} k_{j,d} rho[i,j,d], j <= i.
+
+    [Blog] "Chunkwise Aqk" (diagonal included); [Tokamax] 9.1.5 includes the
+    attention scale in Aqk.
+    """
+    return scale * np.einsum("ihd,jhd,ijhd->hij", qc, kc, rho)
+
+
+def relation_kk(kc, bc, rho):
+    """L[h, i, j] = beta_i * sum_d k_{i,d} k_{j,d} rho[i,j,d], j < i.
+
+    [Tokamax] 9.1.5: L = StrictTril(D_beta K+ (K-)^T); the beta of the later
+    position i multiplies row i ([K3]: "multiplied by the future position's
+    beta").
+    """
+    c = kc.shape[0]
+    strict = np.tril(np.ones((c, c)), -1)
+    return bc.T[:, :, None] * np.einsum("ihd,jhd,ijhd->hij", kc, kc, rho) * strict
+
+
+def solve_unit_lower(Lmat):
+    """A = (I + L)^{-1} for each head, L strictly lower triangular.
+
+    [Tokamax] 9.1.5 ("A_c = (I + L_c)^{-1}"), computed as an exact triangular
+    solve against the identity ([K3]: a batched triangular solve, not a
+    generic inverse).
+    """
+    H, c, _ = Lmat.shape
+    I = np.eye(c)
+    return np.stack([solve_triangular(I + Lmat[h], I, lower=True, unit_diagonal=True)
+                     for h in range(H)])
+
+
+def wy_factors(A, kc, vc, bc, G):
+    """W = A (D_beta K+), U = A (D_beta V) with K+ = k * exp(G).
+
+    [Tokamax] 9.1.5, Paper Eq. 6-7: M = (I + L)^{-1} D_beta, W = M K+,
+    U = M V; beta multiplies on the right of the inverse ([K3]: T_b is
+    T_UT Diag(beta), not Diag(beta) T_UT).
+    """
+    Kplus = kc * np.exp(G)
+    bK = (bc[..., None] * Kplus).transpose(1, 0, 2)  # (H, c, K)
+    bV = (bc[..., None] * vc).transpose(1, 0, 2)     # (H, c, V)
+    return A @ bK, A @ bV
+
+
+def gated_keys(kc, G):
+    """kg_r = k_r * exp(G_C - G_r): each write carried to the chunk end.
+
+    [Tokamax] 9.1.5 (bar K); [K3] "K_decay transports each within-chunk key
+    to the end of the chunk". Shape (H, c, K).
+    """
+    return (kc * np.exp(G[-1][None] - G)).transpose(1, 0, 2)
+
+
+def gated_queries(qc, G, scale):
+    """scale * q * exp(G): the read of the chunk-start state ([Tokamax] 9.1.6)."""
+    return (scale * qc * np.exp(G)).transpose(1, 0, 2)
+
+
+def chunk_terms(qc, kc, vc, gc, bc, scale):
+    """Everything one chunk contributes, independent of the incoming state.
+
+    Inputs are one chunk of one segment: qc, kc, gc (c, H, K), vc (c, H, V),
+    bc (c, H), with c <= chunk size. Returns a dict with G (natural log),
+    Aqk, L, A, W, U, kg, qg (head-first) and gamma = exp(G_C).
+    """
+    G = chunk_cumsum(gc)
+    rho = decay_ratio(G)
+    Aqk = relation_qk(qc, kc, rho, scale)
+    Lmat = relation_kk(kc, bc, rho)
+    A = solve_unit_lower(Lmat)
+    W, U = wy_factors(A, kc, vc, bc, G)
+    return {
+        "G": G.transpose(1, 0, 2), "Aqk": Aqk, "L": Lmat, "A": A, "W": W, "U": U,
+        "kg": gated_keys(kc, G), "qg": gated_queries(qc, G, scale),
+        "gamma": np.exp(G[-1]),
+    }
+
+
+def chunk_step(S, terms):
+    """One chunk of the ordered state recurrence, [Tokamax] 4.3.2 / 9.1.6.
+
+    V_new = U - W S (uses the chunk-start state); O = qg S + Aqk V_new;
+    S_next = Diag(gamma) S + kg^T V_new. Returns (O (H, c, V), S_next).
+    """
+    Vn = terms["U"] - terms["W"] @ S
+    O = terms["qg"] @ S + terms["Aqk"] @ Vn
+    S_next = terms["gamma"][:, :, None] * S + terms["kg"].transpose(0, 2, 1) @ Vn
+    return O, S_next
+
+
+def kda_chunkwise(q, k, v, g, beta, scale, chunk_size=64, initial_state=None,
+                  cu_seqlens=None, use_qk_l2norm=False, eps=1e-6, heads=None,
+                  return_terms=False):
+    """Chunkwise KDA forward, float64. Returns (o, final_state[, terms]).
+
+    Each segment is cut into chunks of `chunk_size` tokens starting at the
+    segment start; a short last chunk is processed with its real length, so
+    no chunk spans two segments ([Tokamax] 3.5, 9.1.7). `heads` restricts
+    the computation to a subset of heads (o and final_state then carry only
+    those heads, in the given order). With return_terms, the per-chunk
+    `chunk_terms` dicts are also returned as a list of (segment, start,
+    terms).
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    if heads is not None:
+        heads = list(heads)
+        q, k, v, g, beta = (x[:, :, heads] for x in (q, k, v, g, beta))
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    if use_qk_l2norm:
+        q, k = l2norm(q, eps), l2norm(k, eps)
+    segs = segments(B, T, cu_seqlens)
+    init = _f64(initial_state)
+    if init is not None and heads is not None:
+        init = init[:, heads]
+    o = np.zeros((B, T, H, V))
+    final = np.zeros((len(segs), H, K, V))
+    all_terms = []
+    for n, (b, s0, s1) in enumerate(segs):
+        S = np.zeros((H, K, V)) if init is None else init[n].copy()
+        for c0 in range(s0, s1, chunk_size):
+            c1 = min(c0 + chunk_size, s1)
+            terms = chunk_terms(q[b, c0:c1], k[b, c0:c1], v[b, c0:c1], g[b, c0:c1],
+                                beta[b, c0:c1], scale)
+            O, S = chunk_step(S, terms)
+            o[b, c0:c1] = O.transpose(1, 0, 2)
+            if return_terms:
+                all_terms.append((n, c0, terms))
+        final[n] = S
+    if return_terms:
+        return o, final, all_terms
+    return o, final
+
+
+# --------------------------------------------------------------------------
+# Affine state summaries ([Tokamax] 9.1.8)
+# --------------------------------------------------------------------------
+def chunk_affine_summary(terms):
+    """S_next = Phi S + Psi with Phi = Diag(gamma) - kg^T W, Psi = kg^T U."""
+    kgT = terms["kg"].transpose(0, 2, 1)
+    Kdim = kgT.shape[1]
+    Phi = terms["gamma"][:, :, None] * np.eye(Kdim)[None] - kgT @ terms["W"]
+    Psi = kgT @ terms["U"]
+    return Phi, Psi
+
+
+def compose_affine(first, second):
+    """Summary of `first` followed by `second`: (Phi_b Phi_a, Phi_b Psi_a + Psi_b)."""
+    Pa, Sa = first
+    Pb, Sb = second
+    return Pb @ Pa, Pb @ Sa + Sb
+
+
+# --------------------------------------------------------------------------
+# KDA layer around the core ([K3] "From the hidden states to causal Q, K, and
+# V", "FP32 core and log-space decay", "Returning to the model dimension";
+# [Tokamax] 9.1.3 lower-bound sigmoid gate)
+# --------------------------------------------------------------------------
+def depthwise_causal_conv(x, w):
+    """Depthwise causal 1-D convolution along T with left zero padding.
+
+    x: [B, T, C]; w: [C, k]. out[t, c] = sum_m w[c, m] x[t + m - (k-1), c]:
+    a Conv1d with groups = channels applied after padding k-1 zeros on the
+    left, so position t only sees positions <= t ([K3] "From the hidden
+    states to causal Q, K, and V").
+    """
+    x = _f64(x)
+    w = _f64(w)
+    B, T, C = x.shape
+    kw = w.shape[1]
+    xp = np.concatenate([np.zeros((B, kw - 1, C)), x], axis=1)
+    out = np.zeros_like(x)
+    for m in range(kw):
+        out += w[:, m][None, None, :] * xp[:, m:m + T, :]
+    return out
+
+
+def rms_norm(x, weight, eps):
+    """x / sqrt(mean(x^2) + eps) * weight over the last axis."""
+    x = _f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(weight)
+
+
+def kda_layer_ref(x, w, num_heads, head_dim, chunk_size=64, gate_lower_bound=-5.0,
+                  norm_eps=1e-6, l2_eps=1e-6):
+    """KDA layer forward with the low-rank output gate, float64.
+
+    x: [B, T, M]. `w` maps names to arrays (Linear weights are [out, in]):
+      Wqkv [3*H*D, M]; conv_q, conv_k, conv_v [H*D, 4]; Wb [H, M];
+      Wad [r, M]; Wau [H*D, r]; A_log [H]; dt_bias [H*D];
+      Wgd [D, M]; Wgu [H*D, D]; norm_w [D]; Wo [M, H*D].
+    Steps ([K3]):
+      QKV projection -> per-stream causal depthwise conv -> SiLU ->
+      q, k L2-normalised over D -> beta = sigmoid(x Wb^T) ->
+      log decay g = a * sigmoid(exp(A_log_h) * (x Wad^T Wau^T + dt_bias)),
+      a = gate_lower_bound ([Tokamax] 9.1.3 lower-bound variant) ->
+      chunkwise core with scale D^-1/2 and zero state ->
+      per-head RMSNorm -> * sigmoid(x Wgd^T Wgu^T) -> Wo.
+    Returns (x_new [B, T, M], dict of intermediates).
+    """
+    x = _f64(x)
+    B, T, M = x.shape
+    H, D = num_heads, head_dim
+    HD = H * D
+    qkv = x @ _f64(w["Wqkv"]).T
+    qp, kp, vp = qkv[..., :HD], qkv[..., HD:2 * HD], qkv[..., 2 * HD:]
+    q = silu(depthwise_causal_conv(qp, w["conv_q"])).reshape(B, T, H, D)
+    k = silu(depthwise_causal_conv(kp, w["conv_k"])).reshape(B, T, H, D)
+    v = silu(depthwise_causal_conv(vp, w["conv_v"])).reshape(B, T, H, D)
+    q, k = l2norm(q, l2_eps), l2norm(k, l2_eps)
+    beta = sigmoid(x @ _f64(w["Wb"]).T)
+    a = (x @ _f64(w["Wad"]).T) @ _f64(w["Wau"]).T
+    lam = np.exp(_f64(w["A_log"]))                       # [H]
+    pre = (a + _f64(w["dt_bias"])).reshape(B, T, H, D) * lam[None, None, :, None]
+    g = gate_lower_bound * sigmoid(pre)
+    o, _ = kda_chunkwise(q, k, v, g, beta, D ** -0.5, chunk_size)
+    on = rms_norm(o, w["norm_w"], norm_eps)
+    gate = sigmoid((x @ _f64(w["Wgd"]).T) @ _f64(w["Wgu"]).T).reshape(B, T, H, D)
+    y = (on * gate).reshape(B, T, HD)
+    x_new = y @ _f64(w["Wo"]).T
+    return x_new, {"q": q, "k": k, "v": v, "g": g, "beta": beta, "o": o}
