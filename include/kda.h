@@ -1,0 +1,142 @@
+/*
+ * kda.h - C ABI of the MI355X (gfx950) chunkwise Kimi Delta Attention forward.
+ *
+ * The operation (all three sources agree on it):
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp g_t) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ * per (sequence, head), with a K x V fp32 state S and a per-channel natural-log
+ * decay g <= 0. Defined as Paper Eq. 1 in the Tokamax "chunk_kda_fwd design
+ * doc" (openxla.org), section 9.1.2, and as steps (0)-(5) in "KDA Doesn't Care
+ * About the Future" (drisspg.github.io), section "Chunkwise KDA in Broad
+ * Strokes". The library evaluates it chunkwise (chunk size 64): Tokamax design
+ * doc sections 4.1 (stage 1+2: gate cumsum, relation matrices, unit
+ * lower-triangular solve, W/U factors) and 4.3 (stage 3+4: ordered state
+ * recurrence and output), Paper Eq. 6-9 (section 9.1.5-9.1.6).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers on the current HIP device; the caller
+ *    owns every buffer, the library keeps no pointer after the call returns
+ *    and allocates nothing.
+ *  - Work is enqueued on `stream` and the call returns without synchronising,
+ *    so calls can be captured in a HIP graph.
+ *  - Shapes, dtypes, sizes and alignment are checked on the host before any
+ *    launch; a failed check returns a non-zero kda_status and launches
+ *    nothing. kda_last_error() then gives a message (thread-local).
+ *  - Value preconditions are NOT checked on the fast path: g in [-5, 0]
+ *    (the lower bound of the pages; it keeps the rebased operands inside the
+ *    fp32 range), beta in [0, 1], cu_seqlens non-decreasing from 0 to T.
+ *    Values outside give undefined numbers but never an out-of-bounds access.
+ *
+ * Layouts (row-major, contiguous, token-major like the layer projections):
+ *   q, k, g : [B, T, H, K]     v, o : [B, T, H, V]     beta : [B, T, H]
+ *   initial_state, final_state : [N, H, K, V] fp32, N = B (fixed length) or
+ *   num_seqs (variable length).
+ * Variable length (Tokamax design doc section 3.5 and 9.1.7): B must be 1,
+ * the sequences are packed along T and cu_seqlens[0..num_seqs] (int32,
+ * device) gives their boundaries. Every sequence is cut into chunks from its
+ * own start, so no chunk spans two sequences; a short last chunk is padded
+ * virtually with q = k = v = beta = 0, g = 0 (zero writes, identity decay).
+ */
+#ifndef KDA_MI355X_H
+#define KDA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARG = 1,   /* bad shape, dtype, pointer, alignment or size */
+  KDA_ERR_UNSUPPORTED = 2,   /* valid request the GPU path does not implement */
+  KDA_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+  KDA_ERR_HIP = 4            /* a HIP runtime call failed (launch error) */
+} kda_status;
+
+typedef struct {
+  int64_t B, T, H;       /* batch, tokens per row (total packed tokens if varlen), heads */
+  int32_t K, V;          /* head dims; the GPU path supports K == V in {64, 128} */
+  int32_t qkv_dtype;     /* kda_dtype of q, k, v and of the output o */
+  int32_t g_dtype;       /* kda_dtype of g */
+  int32_t beta_dtype;    /* kda_dtype of beta */
+  float scale;           /* output scale, usually K^-1/2 */
+  int32_t chunk_size;    /* must be 64 */
+  int32_t use_qk_l2norm; /* 1: q, k <- x / max(||x||_2, l2norm_eps) per token and head
+                            ("KDAChunkwise" docs, section "FP32 core and log-space decay") */
+  float l2norm_eps;      /* eps of the L2 normalisation (1e-6 by convention) */
+  int32_t num_seqs;      /* 0: fixed length (T % 64 == 0, cu_seqlens NULL);
+                            > 0: variable length with that many sequences (B == 1) */
+} kda_fwd_params;
+
+/* Bytes of device workspace kda_chunk_fwd needs for these parameters.
+ * Returns KDA_ERR_* if the parameters are invalid. Pure host computation. */
+kda_status kda_chunk_fwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes);
+
+/* Full forward: stage 1+2 then stage 3+4 on `stream`.
+ *   q, k, v, g, beta : inputs as laid out above (16-byte aligned, beta 4-byte)
+ *   initial_state    : [N, H, K, V] fp32 or NULL (zeros)
+ *   cu_seqlens       : [num_seqs + 1] int32 or NULL (fixed length)
+ *   o                : output, dtype qkv_dtype, same layout as v
+ *   final_state      : [N, H, K, V] fp32 or NULL (not written)
+ *   workspace        : device buffer of at least kda_chunk_fwd_workspace_bytes
+ * A zero-length sequence writes final_state = initial_state (or zeros). */
+kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, void* o, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 1+2 alone (Tokamax design doc section 4.1): chunk-local gate cumsum,
+ * rebased Aqk / L relation tiles, (I + L)^{-1}, W, U, gated keys and queries,
+ * written into the workspace (layout: kda_workspace_info). With cu_seqlens
+ * it first builds the chunk map from cu_seqlens. Same argument rules as
+ * kda_chunk_fwd. */
+kda_status kda_chunk_fwd_stage12(const kda_fwd_params* p, const void* q, const void* k,
+                                 const void* v, const void* g, const void* beta,
+                                 const int32_t* cu_seqlens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+
+/* Stage 3+4 alone (Tokamax design doc section 4.3): reads a workspace filled
+ * by kda_chunk_fwd_stage12 with the same parameters and writes o and
+ * final_state. */
+kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Where stage 1+2 puts its outputs inside the workspace (for inspection).
+ * All offsets are in bytes. For head h and physical chunk p the record starts
+ * at records_offset + (h * chunk_slots + p) * record_bytes and holds, in the
+ * stored element type (bf16 for bf16 q/k/v, else fp32):
+ *   W, QG (qg), KG (kg^T), AQ (Aqk) as 16-row x 32-wide MFMA fragments and U
+ *   in accumulator-tile order, then gamma (fp32, K values). The fragment
+ *   orders are documented in kimi_delta_attention_03_amd/csrc/kda_layout.h. */
+typedef struct {
+  size_t total_bytes, records_offset, record_bytes, chunk_slots;
+  size_t off_w, off_qg, off_kg, off_aq, off_u, off_gamma;
+  int32_t elem_bytes;
+  size_t off_chunk_table;  /* varlen: int32 pairs (first token, valid length) per chunk slot */
+  size_t off_seq_table;    /* varlen: int32 pairs (first chunk slot, chunk count) per sequence */
+  size_t off_order;        /* varlen: sequences ordered longest first */
+} kda_workspace_info;
+
+kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* info);
+
+/* Human-readable name of a status code (static string). */
+const char* kda_status_string(kda_status s);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the built library. */
+int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_MI355X_H */

@@ -1,0 +1,147 @@
+"""MI355X (gfx950) chunkwise Kimi Delta Attention forward.
+
+Python binding of the C ABI in include/kda.h. This module only checks and
+marshals arguments; every step of the forward runs in the HIP kernels of
+libkda_mi355x.so. torch provides device memory and the current HIP stream.
+
+    o, final_state = chunk_fwd(q, k, v, g, beta, scale=None, initial_state=None,
+                               cu_seqlens=None, output_final_state=True,
+                               use_qk_l2norm=False)
+
+Layouts: q, k, g [B, T, H, K]; v [B, T, H, V]; beta [B, T, H]; states
+[N, H, K, V] fp32 (N = B, or the number of sequences with cu_seqlens, B = 1).
+g is the natural-log decay (<= 0, >= -5).
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
+
+__all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _lib.KDA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return _lib.KDA_DTYPE_F32
+    raise KdaValueError(1, f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def make_params(B, T, H, K, V, qkv_dtype, g_dtype, beta_dtype, scale, chunk_size=64,
+                use_qk_l2norm=False, l2norm_eps=1e-6, num_seqs=0) -> KdaFwdParams:
+    p = KdaFwdParams()
+    p.B, p.T, p.H, p.K, p.V = int(B), int(T), int(H), int(K), int(V)
+    p.qkv_dtype, p.g_dtype, p.beta_dtype = int(qkv_dtype), int(g_dtype), int(beta_dtype)
+    p.scale = float(scale)
+    p.chunk_size = int(chunk_size)
+    p.use_qk_l2norm = 1 if use_qk_l2norm else 0
+    p.l2norm_eps = float(l2norm_eps)
+    p.num_seqs = int(num_seqs)
+    return p
+
+
+def workspace_layout(p: KdaFwdParams) -> KdaWorkspaceInfo:
+    info = KdaWorkspaceInfo()
+    _lib.check(_lib.load().kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)))
+    return info
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class KdaForward:
+    """A bound forward call: checked inputs, preallocated outputs and workspace.
+
+    Calling the object runs both stages on the current stream; stage12() and
+    stage34() run them one at a time (same workspace), e.g. to time each.
+    """
+
+    def __init__(self, q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None,
+                 cu_seqlens=None, output_final_state=True, use_qk_l2norm=False, l2norm_eps=1e-6,
+                 out=None, workspace=None):
+        torch = _torch()
+        lib = _lib.load()
+        if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape:
+            raise KdaValueError(1, "q, k, g must be [B, T, H, K] with equal shapes")
+        B, T, H, K = q.shape
+        if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+            raise KdaValueError(1, "v must be [B, T, H, V]")
+        V = v.shape[3]
+        if tuple(beta.shape) != (B, T, H):
+            raise KdaValueError(1, "beta must be [B, T, H]")
+        if k.dtype != q.dtype or v.dtype != q.dtype:
+            raise KdaValueError(1, "q, k, v must share a dtype")
+        tensors = [q, k, v, g, beta]
+        for t in tensors:
+            if not t.is_cuda:
+                raise KdaValueError(1, "inputs must be on the GPU")
+            if not t.is_contiguous():
+                raise KdaValueError(1, "inputs must be contiguous")
+        num_seqs = 0
+        if cu_seqlens is not None:
+            if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+                raise KdaValueError(1, "cu_seqlens must be a 1-D int32 GPU tensor")
+            num_seqs = cu_seqlens.numel() - 1
+            if num_seqs < 1:
+                raise KdaValueError(1, "cu_seqlens needs at least 2 entries")
+        N = num_seqs if num_seqs else B
+        if initial_state is not None:
+            if (tuple(initial_state.shape) != (N, H, K, V) or initial_state.dtype != torch.float32
+                    or not initial_state.is_cuda or not initial_state.is_contiguous()):
+                raise KdaValueError(1, f"initial_state must be contiguous fp32 [{N}, {H}, {K}, {V}] on the GPU")
+        if scale is None:
+            scale = K ** -0.5
+        self.params = make_params(B, T, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale,
+                                  chunk_size, use_qk_l2norm, l2norm_eps, num_seqs)
+        nbytes = ctypes.c_size_t(0)
+        _lib.check(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(self.params), ctypes.byref(nbytes)))
+        dev = q.device
+        if workspace is None or workspace.numel() < nbytes.value:
+            workspace = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        self.o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=dev)
+        self.final_state = (torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+                            if output_final_state else None)
+        self.inputs = (q, k, v, g, beta)
+        self.initial_state = initial_state
+        self.cu_seqlens = cu_seqlens
+        self._lib = lib
+
+    def _stream(self):
+        return ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)
+
+    def stage12(self):
+        q, k, v, g, beta = self.inputs
+        _lib.check(self._lib.kda_chunk_fwd_stage12(
+            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.cu_seqlens),
+            _ptr(self.workspace), self.workspace.numel(), self._stream()))
+
+    def stage34(self):
+        _lib.check(self._lib.kda_chunk_fwd_stage34(
+            ctypes.byref(self.params), _ptr(self.initial_state), _ptr(self.cu_seqlens), _ptr(self.o),
+            _ptr(self.final_state), _ptr(self.workspace), self.workspace.numel(), self._stream()))
+
+    def __call__(self):
+        q, k, v, g, beta = self.inputs
+        _lib.check(self._lib.kda_chunk_fwd(
+            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.initial_state),
+            _ptr(self.cu_seqlens), _ptr(self.o), _ptr(self.final_state), _ptr(self.workspace),
+            self.workspace.numel(), self._stream()))
+        return self.o, self.final_state
+
+
+def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, cu_seqlens=None,
+              output_final_state=True, use_qk_l2norm=False, l2norm_eps=1e-6):
+    """Chunkwise KDA forward on the GPU. Returns (o, final_state or None)."""
+    return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
+                      output_final_state, use_qk_l2norm, l2norm_eps)()

@@ -1,0 +1,222 @@
+// Host side of the C ABI declared in include/kda.h: argument validation,
+// workspace sizing and kernel dispatch. Nothing here allocates or
+// synchronises; every launch goes to the caller's stream.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_kernels.h"
+#include "kda_layout.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+kda_status fail(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+kda_status check_params(const kda_fwd_params* p) {
+  g_msg[0] = 0;
+  if (!p) return fail(KDA_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 0 || p->T < 0 || p->H <= 0) return fail(KDA_ERR_INVALID_ARG, "need B >= 0, T >= 0, H > 0");
+  if (p->K <= 0 || p->V <= 0) return fail(KDA_ERR_INVALID_ARG, "need K > 0 and V > 0");
+  if (p->K > 256) return fail(KDA_ERR_INVALID_ARG, "K must be <= 256 (got %d)", p->K);
+  if (!(p->K == p->V && (p->K == 64 || p->K == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "GPU path supports K == V in {64, 128} (got K=%d V=%d)", p->K, p->V);
+  for (int32_t d : {p->qkv_dtype, p->g_dtype, p->beta_dtype})
+    if (d != KDA_DTYPE_F32 && d != KDA_DTYPE_BF16) return fail(KDA_ERR_INVALID_ARG, "unknown dtype %d", d);
+  if (p->chunk_size != 64) return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 64 (got %d)", p->chunk_size);
+  if (p->use_qk_l2norm && !(p->l2norm_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "l2norm_eps must be > 0");
+  if (p->num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 0");
+  if (p->num_seqs > 0) {
+    if (p->B != 1) return fail(KDA_ERR_INVALID_ARG, "variable-length input needs B == 1 (got %lld)", (long long)p->B);
+  } else if (p->T % 64 != 0) {
+    return fail(KDA_ERR_INVALID_ARG, "fixed-length T must be a multiple of 64 (got %lld); pass cu_seqlens for ragged input",
+                (long long)p->T);
+  }
+  // 32-bit indexing limits of the kernels' tables
+  const int64_t tokens = p->B * p->T;
+  if (tokens > (int64_t)INT32_MAX / 2 || p->H > 65536 || tokens * p->H * p->K > ((int64_t)1 << 40))
+    return fail(KDA_ERR_UNSUPPORTED, "problem too large");
+  if (p->num_seqs > (1 << 24)) return fail(KDA_ERR_UNSUPPORTED, "too many sequences");
+  return KDA_OK;
+}
+
+kda::Layout layout_of(const kda_fwd_params* p) {
+  const int elem = p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+  return kda::make_layout(p->K, p->V, elem, p->B, p->T, p->H, p->num_seqs);
+}
+
+kda_status check_common(const kda_fwd_params* p, const int32_t* cu, void* ws, size_t ws_bytes, kda::Layout* L) {
+  kda_status s = check_params(p);
+  if (s != KDA_OK) return s;
+  if (p->num_seqs > 0 && !cu) return fail(KDA_ERR_INVALID_ARG, "num_seqs > 0 needs cu_seqlens");
+  if (p->num_seqs == 0 && cu) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens given but num_seqs == 0");
+  if (cu && !aligned(cu, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+  *L = layout_of(p);
+  if (!ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes < L->total_bytes)
+    return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, L->total_bytes);
+  return KDA_OK;
+}
+
+bool empty_problem(const kda_fwd_params* p) { return p->B == 0 || (p->num_seqs == 0 && p->T == 0); }
+
+kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream) {
+  if (p->T > 0 && p->B > 0) {
+    if (!q || !k || !v || !g || !beta) return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
+    for (const void* t : {q, k, v, g})
+      if (!aligned(t, 16)) return fail(KDA_ERR_INVALID_ARG, "q, k, v and g must be 16-byte aligned");
+    if (!aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARG, "beta must be 4-byte aligned");
+  }
+  char* w = static_cast<char*>(ws);
+  const int varlen = p->num_seqs > 0;
+  if (varlen) {
+    hipError_t e = kda::launch_varlen_map(cu, p->num_seqs, p->T, w, L.ncp, L.off_chunk_tab, L.off_seq_tab,
+                                          L.off_order, stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
+  }
+  if (empty_problem(p) || p->T == 0) return KDA_OK;
+  kda::Stage12Args a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.g_f32 = p->g_dtype == KDA_DTYPE_F32;
+  a.beta_f32 = p->beta_dtype == KDA_DTYPE_F32;
+  a.H = (int)p->H;
+  a.scale = p->scale;
+  a.l2norm = p->use_qk_l2norm != 0;
+  a.l2eps = p->l2norm_eps;
+  a.varlen = varlen;
+  a.ws = w;
+  a.meta_bytes = L.meta_bytes; a.rec_bytes = L.rec_bytes; a.ncp = L.ncp;
+  a.off_chunk_tab = L.off_chunk_tab;
+  a.off_w = L.off_w; a.off_qg = L.off_qg; a.off_kg = L.off_kg; a.off_aq = L.off_aq; a.off_u = L.off_u;
+  a.off_gam = L.off_gam;
+  const size_t nblocks = L.ncp * (size_t)p->H;
+  if (nblocks > (size_t)INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = kda::launch_stage12(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, (int)nblocks, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "stage 1+2 launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float* fin, void* ws,
+                      const kda::Layout& L, hipStream_t stream) {
+  const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
+  if (nseq == 0) return KDA_OK;
+  if (p->T > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  if (o && !aligned(o, 16)) return fail(KDA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+  if ((init && !aligned(init, 16)) || (fin && !aligned(fin, 16)))
+    return fail(KDA_ERR_INVALID_ARG, "states must be 16-byte aligned");
+  kda::Stage34Args a{};
+  a.init = init;
+  a.final_state = fin;
+  a.o = o;
+  a.H = (int)p->H;
+  const int64_t nunits = nseq * p->H;
+  if (nunits > INT32_MAX / 16) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  a.nunits = (int)nunits;
+  a.nt = p->num_seqs > 0 ? 0 : (int)(p->T / 64);
+  a.varlen = p->num_seqs > 0;
+  a.ws = static_cast<const char*>(ws);
+  a.meta_bytes = L.meta_bytes; a.rec_bytes = L.rec_bytes; a.ncp = L.ncp;
+  a.off_chunk_tab = L.off_chunk_tab; a.off_seq_tab = L.off_seq_tab; a.off_order = L.off_order;
+  a.off_w = L.off_w; a.off_qg = L.off_qg; a.off_kg = L.off_kg; a.off_aq = L.off_aq; a.off_u = L.off_u;
+  a.off_gam = L.off_gam;
+  hipError_t e = kda::launch_stage34(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "stage 3+4 launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_chunk_fwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes) {
+  kda_status s = check_params(p);
+  if (s != KDA_OK) return s;
+  if (!bytes) return fail(KDA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = layout_of(p).total_bytes;
+  return KDA_OK;
+}
+
+kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* info) {
+  kda_status s = check_params(p);
+  if (s != KDA_OK) return s;
+  if (!info) return fail(KDA_ERR_INVALID_ARG, "info is NULL");
+  const kda::Layout L = layout_of(p);
+  info->total_bytes = L.total_bytes;
+  info->records_offset = L.meta_bytes;
+  info->record_bytes = L.rec_bytes;
+  info->chunk_slots = L.ncp;
+  info->off_w = L.off_w;
+  info->off_qg = L.off_qg;
+  info->off_kg = L.off_kg;
+  info->off_aq = L.off_aq;
+  info->off_u = L.off_u;
+  info->off_gamma = L.off_gam;
+  info->elem_bytes = L.elem;
+  info->off_chunk_table = L.off_chunk_tab;
+  info->off_seq_table = L.off_seq_tab;
+  info->off_order = L.off_order;
+  return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const int32_t* cu_seqlens, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  kda::Layout L;
+  kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  return do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream);
+}
+
+kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_state, const int32_t* cu_seqlens,
+                                 void* o, float* final_state, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  kda::Layout L;
+  kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+}
+
+kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens, void* o,
+                         float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda::Layout L;
+  kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  if (p->T > 0 && p->B > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream);
+  if (s != KDA_OK) return s;
+  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_ERR_UNKNOWN";
+}
+
+const char* kda_last_error(void) { return g_msg; }
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Launch interface between the host dispatcher (kda_api.cpp) and the gfx950
+// kernels. Internal to the library.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda_layout.h"
+
+namespace kda {
+
+struct Stage12Args {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  int g_f32;        // 1: g is fp32, 0: bf16
+  int beta_f32;     // 1: beta is fp32, 0: bf16
+  int H;
+  float scale;
+  int l2norm;
+  float l2eps;
+  int varlen;       // 1: chunk table in the workspace metadata
+  char* ws;         // workspace base
+  size_t meta_bytes, rec_bytes, ncp;
+  size_t off_chunk_tab;
+  size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;
+};
+
+struct Stage34Args {
+  const float* init;   // [N, H, K, V] or null
+  float* final_state;  // [N, H, K, V] or null
+  void* o;
+  int H;
+  int nunits;          // N * H
+  int nt;              // fixed length: chunks per batch row
+  int varlen;
+  const char* ws;
+  size_t meta_bytes, rec_bytes, ncp;
+  size_t off_chunk_tab, off_seq_tab, off_order;
+  size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;
+};
+
+// bf16 == 1 selects the bf16 instantiation (bf16 q/k/v, bf16 intermediates).
+hipError_t launch_stage12(const Stage12Args& a, int K, int bf16, int nblocks, hipStream_t s);
+hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s);
+hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, size_t ncp,
+                             size_t off_chunk_tab, size_t off_seq_tab, size_t off_order,
+                             hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,83 @@
+// Internal layout of the KDA forward workspace, shared by the host dispatcher
+// and the gfx950 kernels.
+//
+// The stage-1+2 kernel writes, for every (head h, physical chunk p), one
+// fixed-size record that the stage-3+4 kernel streams in chunk order. The
+// record holds the chunk's operands already arranged as MFMA fragments so
+// that stage 3+4 loads each fragment with one coalesced 16-byte (bf16) or
+// 32-byte (fp32) access per lane:
+//
+//   W   [rt 0..3][kb 0..K/32-1][lane 0..63][8]   W = A (D_beta K+), rows = chunk position
+//   QG  [rt 0..3][kb 0..K/32-1][lane][8]         qg = scale * q * 2^G
+//   KG  [rt 0..K/16-1][kb 0..1][lane][8]         kg^T, rows = key channel, k = chunk position
+//   AQ  [rt 0..3][kb 0..1][lane][8]              Aqk (scale folded in, causal mask applied)
+//   U   [vb 0..V/16-1][rt 0..3][lane][4]         U = A (D_beta V) in accumulator layout
+//   GAM [K] float                                 gamma = 2^{G_last} (chunk-end decay)
+//
+// Fragment element t of lane l (g = l / 16, i = l % 16) holds row i of a
+// 16-row tile and the reduction index phys(g, t) of a 32-wide block:
+//   phys(g, t) = 4g + t          for t < 4
+//              = 16 + 4g + t - 4 for t >= 4
+// which is where two stacked 16x16 accumulator tiles keep their rows. This
+// lets accumulator tiles feed the next product's B operand without any lane
+// shuffle (see kda_device.h).
+//
+// The metadata region at the start of the workspace serves variable-length
+// input (cu_seqlens): per physical chunk its first token and valid length,
+// per sequence its first chunk and chunk count, and a longest-first order of
+// the sequences.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunk = 64;      // chunk size C of the GPU path
+constexpr int kThreads = 256;   // 4 waves of 64 lanes per workgroup
+
+struct Layout {
+  int K, V, elem;               // elem = bytes of the stored element (2 bf16, 4 fp32)
+  size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;  // byte offsets in a record
+  size_t rec_bytes;
+  size_t ncp;                   // physical chunk slots per head
+  int nseq;                     // sequences (varlen) or batch rows (fixed)
+  size_t meta_bytes;            // metadata region at the workspace start
+  size_t off_chunk_tab, off_seq_tab, off_order;  // byte offsets inside metadata
+  size_t total_bytes;
+};
+
+static inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// K, V: head dims; elem: 2 or 4; B, T: batch and (packed) length; H: heads;
+// nseq: 0 for fixed length, else number of packed sequences.
+static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, int64_t H,
+                                 int nseq) {
+  Layout L{};
+  L.K = K;
+  L.V = V;
+  L.elem = elem;
+  const size_t C = kChunk;
+  size_t e = (size_t)elem;
+  L.off_w = 0;
+  L.off_qg = L.off_w + C * K * e;
+  L.off_kg = L.off_qg + C * K * e;
+  L.off_aq = L.off_kg + C * K * e;
+  L.off_u = L.off_aq + C * C * e;
+  L.off_gam = L.off_u + C * V * e;
+  L.rec_bytes = round_up(L.off_gam + (size_t)K * 4, 256);
+  if (nseq > 0) {
+    L.ncp = (size_t)((T + kChunk - 1) / kChunk) + (size_t)nseq;
+    L.nseq = nseq;
+  } else {
+    L.ncp = (size_t)B * (size_t)(T / kChunk);
+    L.nseq = (int)B;
+  }
+  L.off_chunk_tab = 64;
+  L.off_seq_tab = L.off_chunk_tab + L.ncp * 8;
+  L.off_order = L.off_seq_tab + (size_t)L.nseq * 8;
+  L.meta_bytes = round_up(L.off_order + (size_t)L.nseq * 4, 256);
+  L.total_bytes = L.meta_bytes + L.rec_bytes * L.ncp * (size_t)H;
+  return L;
+}
+
+}  // namespace kda
