@@ -1,0 +1,190 @@
+"""Benchmark of the chunkwise KDA forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+
+A step is one full forward pass (stage 1+2 then stage 3+4, through the C
+ABI) over the headline workload: B=1, H=32, T=32768, K=V=128, bf16 inputs,
+fp32 state, random initial state. Inputs are synthetic (seeded) and already
+resident in HBM when timing starts. W untimed warmup steps, then exactly K
+timed steps bracketed by device synchronisation; HIP events on the stream the
+kernels run on give the step time and, in separate loops, each kernel's
+average duration for the roofline entry.
+
+Prints ONE JSON line. Throughput `value` is tokens/s (B*T per step).
+Rooflines use MI355X's published peaks (HBM3E 8 TB/s, dense bf16 MFMA
+2.5 PFLOP/s) and the algorithmic traffic of each kernel:
+  stage 1+2: reads q,k,v,g (4 x 256 B) + beta (2 B), writes its workspace
+             record (1160 B)                     -> 2186 B per token-head
+  stage 3+4: reads the record (1160 B), writes o (256 B) -> 1416 B per token-head
+  algorithmic FLOPs: 6CKV + C(C+1)(3K+2V) + C^3/3 per chunk-head (C = 64).
+The CPU baseline times the float64 oracle on a bounded sample of the same
+workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import resource
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # bytes/s
+PEAK_BF16 = 2.5e15         # dense bf16 MFMA FLOP/s
+PEAK_FP32 = 157.3e12       # dense fp32 MFMA FLOP/s
+METRIC = "KDA chunk-fwd tokens/s at H=32,K=V=128,T=32k bf16; % MFMA peak"
+
+
+def alg_flops_per_chunk_head(C, K, V):
+    return 6 * C * K * V + C * (C + 1) * (3 * K + 2 * V) + C ** 3 / 3
+
+
+def alg_bytes_per_token_head(K, V, elem, gelem, belem):
+    s12 = (2 * K) * elem + V * elem + K * gelem + belem          # q, k, v, g, beta
+    rec = (3 * K + 64 + V) * elem + 4 * K / 64                  # W, qg, kg, Aqk, U, gamma
+    s34 = rec + V * elem                                          # record in, o out
+    return s12 + rec, s34
+
+
+def time_loop(fn, reps, torch):
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cpu_baseline(x, target_s=15.0):
+    """Time the float64 chunkwise oracle on a bounded sample of the workload."""
+    import oracle.kda_oracle as orc
+    H = x.q.shape[2]
+    heads = [0, 1]
+    T = x.q.shape[1]
+    tok = 1024
+    # grow the sample until it takes a measurable time, then run the bounded one
+    while True:
+        t0 = time.perf_counter()
+        c0 = time.process_time()
+        orc.kda_chunkwise(x.q[:, :tok], x.k[:, :tok], x.v[:, :tok], x.g[:, :tok], x.beta[:, :tok],
+                          x.scale, 64, None if x.initial_state is None else x.initial_state,
+                          heads=heads)
+        wall = time.perf_counter() - t0
+        cpu = time.process_time() - c0
+        if wall * 2 >= target_s or tok * 2 > T:
+            break
+        tok = min(T, tok * max(2, int(target_s / max(wall, 1e-3) / 2)))
+        tok = max(64, tok // 64 * 64)
+    token_heads = tok * len(heads)
+    tps = token_heads / wall / H       # tokens/s of the full-H workload
+    return {
+        "value": tps, "unit": "tokens/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "sample": f"float64 chunkwise oracle on heads {heads} of {H}, first {tok} of {T} tokens "
+                  f"({token_heads} token-heads, {wall:.1f} s wall, {cpu:.1f} s CPU); tokens/s scaled "
+                  f"to all {H} heads; host has {len(os.sched_getaffinity(0))} usable cores",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the KDA forward here is a single-GPU kernel path); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kimi_delta_attention_03_amd as kda
+    from kimi_delta_attention_03_amd.synthetic import WORKLOADS, workload
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    x = workload(args.workload)
+    t_gen = time.perf_counter() - t_gen
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    to = lambda a, d: torch.from_numpy(a).to(d).to(dev)
+    q, k, v, g, beta = (to(a, dt) for a in (x.q, x.k, x.v, x.g, x.beta))
+    init = None if x.initial_state is None else to(x.initial_state, torch.float32)
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens.astype(np.int32)).to(dev)
+    B, T, H, K = x.q.shape
+    V = x.v.shape[3]
+    fwd = kda.KdaForward(q, k, v, g, beta, scale=x.scale, initial_state=init, cu_seqlens=cu)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    ms_step = time_loop(fwd, args.steps, torch)
+
+    # per-kernel durations on the launch stream
+    ms12 = time_loop(fwd.stage12, args.kernel_reps, torch)
+    ms34 = time_loop(fwd.stage34, args.kernel_reps, torch)
+
+    tokens = B * T
+    token_heads = tokens * H
+    elem = 2 if x.dtype == "bf16" else 4
+    b12, b34 = alg_bytes_per_token_head(K, V, elem, elem, elem)
+    if cu is not None:
+        nchunk_heads = int(sum(-(-int(L) // 64) for L in np.diff(x.cu_seqlens))) * H
+    else:
+        nchunk_heads = B * (T // 64) * H
+    flops = alg_flops_per_chunk_head(64, K, V) * nchunk_heads
+    bytes_total = (b12 + b34) * token_heads
+    peak_mma = PEAK_BF16 if x.dtype == "bf16" else PEAK_FP32
+    s_step = ms_step / 1e3
+    dom = "stage12" if ms12 >= ms34 else "stage34"
+    dom_bytes = (b12 if dom == "stage12" else b34) * token_heads
+    dom_ms = ms12 if dom == "stage12" else ms34
+    achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+
+    cfg = WORKLOADS[args.workload]
+    result = {
+        "metric": METRIC,
+        "value": tokens / s_step,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.dtype,
+        "data": "synthetic (seeded numpy generators; no dataset)",
+        "config": {"workload": cfg["name"], "B": B, "T": T, "H": H, "K": K, "V": V, "chunk": 64,
+                   "state": "fp32", "initial_state": init is not None, "varlen": cu is not None},
+        "tflops": flops / s_step / 1e12,
+        "mfma_frac": flops / s_step / peak_mma,
+        "hbm_alg_GBps": bytes_total / s_step / 1e9,
+        "hbm_alg_frac": bytes_total / s_step / PEAK_HBM,
+        "kernels_ms": {"stage12": ms12, "stage34": ms34},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
+                     "unit": "GB/s", "frac": achieved * 1e9 / PEAK_HBM, "traffic": None,
+                     "alg_bytes_per_launch": dom_bytes},
+        "record": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                   "device": torch.cuda.get_device_name(0),
+                   "cus": torch.cuda.get_device_properties(0).multi_processor_count,
+                   "sync": "torch.cuda.synchronize + HIP events on the launch stream",
+                   "timed": "kernel launches only (inputs resident, workspace preallocated)",
+                   "input_gen_s": round(t_gen, 1)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

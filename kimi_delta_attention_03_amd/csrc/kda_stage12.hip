@@ -37,20 +37,19 @@ __device__ __forceinline__ float ld_scalar(const void* p, size_t idx, int is_f32
                 : (float)reinterpret_cast<const bf16*>(p)[idx];
 }
 
-// 16-byte chunk of a row of T, zero when the row is padding
-struct Raw16 { uint4 u; };
-
 template <typename T>
-__device__ __forceinline__ float sumsq16(const uint4& u) {
+__device__ __forceinline__ float sumsq16(uint4 u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   float s = 0.f;
-  if constexpr (sizeof(T) == 2) {
-    const bf16* e = reinterpret_cast<const bf16*>(&u);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) { float x = (float)e[t]; s += x * x; }
-  } else {
-    const float* e = reinterpret_cast<const float*>(&u);
-#pragma unroll
-    for (int t = 0; t < 4; ++t) s += e[t] * e[t];
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(T) == 2) {  // two bf16 per word: the high half is the bf16 bit pattern
+      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+      s += lo * lo + hi * hi;
+    } else {
+      const float x = __uint_as_float(w[i]);
+      s += x * x;
+    }
   }
   return s;
 }
@@ -140,20 +139,28 @@ __global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
     sA[seg * K + c] = run;  // segment totals (sA is free until the relations)
   }
 
-  uint4 kraw[NCH], vraw[NCH];
+  // k and v tiles, 16 bytes per thread and chunk; kept as vector values (not
+  // arrays) so they stay in registers until they are written to LDS
+  typedef uint32_t rawv __attribute__((ext_vector_type(4 * NCH)));
+  rawv kraw, vraw;
 #pragma unroll
   for (int m = 0; m < NCH; ++m) {
     const int ci = tid + m * kThreads;
     const int row = ci / CPR, col = (ci % CPR) * EPC;
-    uint4 z = {0u, 0u, 0u, 0u};
-    kraw[m] = row < len ? *reinterpret_cast<const uint4*>(kg_ + rowK(row) + col) : z;
-    vraw[m] = row < len ? *reinterpret_cast<const uint4*>(vg_ + rowV(row) + col) : z;
+    uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+    if (row < len) {
+      kk = *reinterpret_cast<const uint4*>(kg_ + rowK(row) + col);
+      vv = *reinterpret_cast<const uint4*>(vg_ + rowV(row) + col);
+    }
+    kraw[4 * m] = kk.x; kraw[4 * m + 1] = kk.y; kraw[4 * m + 2] = kk.z; kraw[4 * m + 3] = kk.w;
+    vraw[4 * m] = vv.x; vraw[4 * m + 1] = vv.y; vraw[4 * m + 2] = vv.z; vraw[4 * m + 3] = vv.w;
   }
+  auto part = [](const rawv& r, int m) { return uint4{r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]}; };
 #pragma unroll
   for (int m = 0; m < NCH; ++m) {
     const int ci = tid + m * kThreads;
     const int row = ci / CPR, col = (ci % CPR) * EPC;
-    *reinterpret_cast<uint4*>(sK + row * KS + col) = kraw[m];
+    *reinterpret_cast<uint4*>(sK + row * KS + col) = part(kraw, m);
   }
   if (a.l2norm) {
     // rows are owned by CPR consecutive lanes: reduce the squares across them
@@ -161,9 +168,9 @@ __global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
     for (int m = 0; m < NCH; ++m) {
       const int ci = tid + m * kThreads;
       const int row = ci / CPR, col = (ci % CPR) * EPC;
-      float sk = sumsq16<T>(kraw[m]);
-      uint4 z = {0u, 0u, 0u, 0u};
-      uint4 qr = row < len ? *reinterpret_cast<const uint4*>(qg_ + rowK(row) + col) : z;
+      float sk = sumsq16<T>(part(kraw, m));
+      uint4 qr = {0u, 0u, 0u, 0u};
+      if (row < len) qr = *reinterpret_cast<const uint4*>(qg_ + rowK(row) + col);
       float sq = sumsq16<T>(qr);
 #pragma unroll
       for (int o = 1; o < CPR; o <<= 1) {
@@ -375,9 +382,12 @@ __global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
         cvt8(x, BKf[cc][kb]);
       }
     }
+    // rt runs over compile-time values (a register array indexed by a runtime
+    // value becomes a compare/select chain); the wave-uniform guard picks the
+    // row tiles of this wave
 #pragma unroll
-    for (int m = 0; m < NKB; ++m) {
-      const int rt = rt0 + m * RSTEP;
+    for (int rt = 0; rt < 4; ++rt) {
+      if ((rt - rt0) % RSTEP != 0) continue;
       floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -396,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
   for (int m = 0; m < NCH; ++m) {
     const int ci = tid + m * kThreads;
     const int row = ci / CPR, col = (ci % CPR) * EPC;
-    *reinterpret_cast<uint4*>(sV + row * KS + col) = vraw[m];
+    *reinterpret_cast<uint4*>(sV + row * KS + col) = part(vraw, m);
   }
   lds_sync();
   {
