@@ -133,6 +133,7 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   a.ws = static_cast<const char*>(ws);
   a.meta_bytes = L.meta_bytes; a.rec_bytes = L.rec_bytes; a.ncp = L.ncp;
   a.off_chunk_tab = L.off_chunk_tab; a.off_seq_tab = L.off_seq_tab; a.off_order = L.off_order;
+  a.off_sink = L.off_sink;
   a.off_w = L.off_w; a.off_qg = L.off_qg; a.off_kg = L.off_kg; a.off_aq = L.off_aq; a.off_u = L.off_u;
   a.off_gam = L.off_gam;
   hipError_t e = kda::launch_stage34(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, stream);

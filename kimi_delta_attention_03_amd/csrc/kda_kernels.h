@@ -37,7 +37,7 @@ struct Stage34Args {
   int varlen;
   const char* ws;
   size_t meta_bytes, rec_bytes, ncp;
-  size_t off_chunk_tab, off_seq_tab, off_order;
+  size_t off_chunk_tab, off_seq_tab, off_order, off_sink;
   size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;
 };
 

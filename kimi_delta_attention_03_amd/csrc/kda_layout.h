@@ -25,7 +25,8 @@
 // The metadata region at the start of the workspace serves variable-length
 // input (cu_seqlens): per physical chunk its first token and valid length,
 // per sequence its first chunk and chunk count, and a longest-first order of
-// the sequences.
+// the sequences, and a small sink that absorbs the output stores of padding
+// rows (so that the stores need no branch).
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -43,6 +44,7 @@ struct Layout {
   int nseq;                     // sequences (varlen) or batch rows (fixed)
   size_t meta_bytes;            // metadata region at the workspace start
   size_t off_chunk_tab, off_seq_tab, off_order;  // byte offsets inside metadata
+  size_t off_sink;              // 256-byte target of stores that must be dropped
   size_t total_bytes;
 };
 
@@ -75,7 +77,8 @@ static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, i
   L.off_chunk_tab = 64;
   L.off_seq_tab = L.off_chunk_tab + L.ncp * 8;
   L.off_order = L.off_seq_tab + (size_t)L.nseq * 8;
-  L.meta_bytes = round_up(L.off_order + (size_t)L.nseq * 4, 256);
+  L.off_sink = round_up(L.off_order + (size_t)L.nseq * 4, 256);
+  L.meta_bytes = L.off_sink + 256;
   L.total_bytes = L.meta_bytes + L.rec_bytes * L.ncp * (size_t)H;
   return L;
 }

@@ -7,11 +7,17 @@
 //
 // The V columns of S evolve independently (every product above is linear in
 // S's columns), so one workgroup owns a 16-column block of S for one
-// (sequence, head) and walks that sequence's chunks in order. The K x 16
-// fp32 state block lives in MFMA accumulators spread over the 4 waves; each
-// chunk exchanges only the state block and V_new (as MFMA B fragments)
-// through LDS. The chunk operands are read as ready-made MFMA fragments from
-// the stage-1+2 record, one chunk ahead of use.
+// (sequence, head) and walks that sequence's chunks in order.
+//
+// The workgroup has 8 waves in two roles:
+//   row waves 0..3   - wave r computes V_new and O for chunk rows 16 r .. 16 r + 15
+//   state waves 4..7 - hold the K x 16 fp32 state block in MFMA accumulators
+//                      (K / 64 tiles of 16 rows each) and apply the update.
+// Per chunk the row waves publish V_new and the state waves publish the new
+// state (both as MFMA B-operand halves) through LDS; both roles pass the
+// same two barriers per chunk. The chunk operands are read as ready-made MFMA
+// fragments from the stage-1+2 record through a ring of NB register buffers,
+// NB - 1 chunks ahead of use.
 //
 // Workgroup ids are mapped so that the V/16 workgroups of one (sequence,
 // head) get ids congruent modulo 8: with round-robin dispatch over the 8
@@ -23,61 +29,100 @@
 namespace kda {
 namespace {
 
+constexpr int kThreads34 = 512;
+
 __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// operands of one chunk for a row wave
 template <typename T, int K>
-struct ChunkFrags {
+struct RowFrags {
   static constexpr int NKB = K / 32;
+  typename Vec<T>::x8 w[NKB];   // W rows of this wave's 16-row block
+  typename Vec<T>::x8 qg[NKB];  // qg rows of this wave's block
+  typename Vec<T>::x8 aq[2];    // Aqk rows of this wave's block
+  typename Vec<T>::x4 u;        // U, accumulator layout
+  int2 ct;                      // (first token, valid length) of the chunk
+};
+
+// operands of one chunk for a state wave
+template <typename T, int K>
+struct StateFrags {
   static constexpr int TPW = K / 64;
-  typename Vec<T>::x8 w[NKB];      // W rows of this wave's 16-row block
-  typename Vec<T>::x8 qg[NKB];     // qg rows of this wave's block
-  typename Vec<T>::x8 aq[2];       // Aqk rows of this wave's block
-  typename Vec<T>::x8 kg[TPW][2];  // kg^T rows for this wave's state tiles
-  typename Vec<T>::x4 u;           // U, accumulator layout
+  typename Vec<T>::x8 kg[TPW][2];  // kg^T rows of this wave's state tiles
   floatx4 gam[TPW];                // gamma for this lane's state rows
 };
 
+// Fragment loads go through a buffer resource covering this (sequence, head)'s
+// records: one uniform descriptor, the chunk offset in a scalar register and a
+// single per-lane offset register shared by every load. With 64-bit per-lane
+// addresses instead, the register allocator reuses address registers that are
+// still the destination of in-flight loads and the prefetch ring stalls.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void bload(bf16x8& d, __amdgpu_buffer_rsrc_t r, int lane_off, int soff) {
+  d = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, soff, 0));
+}
+__device__ __forceinline__ void bload(floatx8& d, __amdgpu_buffer_rsrc_t r, int lane_off, int soff) {
+  const floatx4 a = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, 2 * lane_off, soff, 0));
+  const floatx4 b = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, 2 * lane_off + 16, soff, 0));
+  d = stackf(a, b);
+}
+__device__ __forceinline__ void bload4(bf16x4& d, __amdgpu_buffer_rsrc_t r, int lane_off, int soff) {
+  d = __builtin_bit_cast(bf16x4, __builtin_amdgcn_raw_buffer_load_b64(r, lane_off / 2, soff, 0));
+}
+__device__ __forceinline__ void bload4(floatx4& d, __amdgpu_buffer_rsrc_t r, int lane_off, int soff) {
+  d = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, soff, 0));
+}
+
+// lane_off = 16 * lane; frag8 fragments are 64 * 8 elements, accumulator-layout
+// fragments 64 * 4 elements
 template <typename T, int K>
-__device__ __forceinline__ void load_frags(ChunkFrags<T, K>& f, const char* rec, const Stage34Args& a,
-                                           int w, int lane, int vb, int gq) {
+__device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff, const int2* ct,
+                                         const Stage34Args& a, int r, int lane_off, int vb) {
   constexpr int NKB = K / 32;
-  constexpr int TPW = K / 64;
-  typedef typename Vec<T>::x8 F8;
-  typedef typename Vec<T>::x4 F4;
-  const F8* W = reinterpret_cast<const F8*>(rec + a.off_w);
-  const F8* QG = reinterpret_cast<const F8*>(rec + a.off_qg);
-  const F8* AQ = reinterpret_cast<const F8*>(rec + a.off_aq);
-  const F8* KG = reinterpret_cast<const F8*>(rec + a.off_kg);
-  const F4* U = reinterpret_cast<const F4*>(rec + a.off_u);
-  const float* G = reinterpret_cast<const float*>(rec + a.off_gam);
+  constexpr int F8B = 512 * (int)sizeof(T);  // bytes of one frag8 fragment
+  constexpr int F4B = 256 * (int)sizeof(T);  // bytes of one accumulator fragment
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
-    f.w[kb] = W[(w * NKB + kb) * 64 + lane];
-    f.qg[kb] = QG[(w * NKB + kb) * 64 + lane];
+    bload(f.w[kb], rs, lane_off, soff + (int)a.off_w + (r * NKB + kb) * F8B);
+    bload(f.qg[kb], rs, lane_off, soff + (int)a.off_qg + (r * NKB + kb) * F8B);
   }
-  f.aq[0] = AQ[(w * 2 + 0) * 64 + lane];
-  if (w >= 2) f.aq[1] = AQ[(w * 2 + 1) * 64 + lane];
-#pragma unroll
-  for (int m = 0; m < TPW; ++m) {
-    const int rt = w * TPW + m;
-    f.kg[m][0] = KG[(rt * 2 + 0) * 64 + lane];
-    f.kg[m][1] = KG[(rt * 2 + 1) * 64 + lane];
-    f.gam[m] = *reinterpret_cast<const floatx4*>(G + 16 * rt + 4 * gq);
-  }
-  f.u = U[(vb * 4 + w) * 64 + lane];
+  // both Aqk halves are loaded for every wave (the second is unused for rows < 32):
+  // no branch around a load keeps the compiler's memory-counter waits exact
+  bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + (r * 2 + 0) * F8B);
+  bload(f.aq[1], rs, lane_off, soff + (int)a.off_aq + (r * 2 + 1) * F8B);
+  bload4(f.u, rs, lane_off, soff + (int)a.off_u + (vb * 4 + r) * F4B);
+  f.ct = *ct;  // read in both modes (the table exists in every workspace); used for varlen only
 }
 
 template <typename T, int K>
-__global__ __launch_bounds__(kThreads) void stage34_kernel(Stage34Args a) {
+__device__ __forceinline__ void load_state(StateFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff,
+                                           const Stage34Args& a, int s, int lane_off, int gam_off) {
+  constexpr int TPW = K / 64;
+  constexpr int F8B = 512 * (int)sizeof(T);
+#pragma unroll
+  for (int m = 0; m < TPW; ++m) {
+    const int rt = s * TPW + m;
+    bload(f.kg[m][0], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 0) * F8B);
+    bload(f.kg[m][1], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 1) * F8B);
+    f.gam[m] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rs, gam_off, soff + (int)a.off_gam + 64 * rt, 0));
+  }
+}
+
+template <typename T, int K, int NB>
+__global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   constexpr int C = kChunk;
   constexpr int V = K;
   constexpr int NKB = K / 32;
   constexpr int NVB = V / 16;
-  constexpr int TPW = K / 64;      // 16-row state tiles per wave
+  constexpr int TPW = K / 64;      // 16-row state tiles per state wave
   constexpr int NST = K / 16;      // state tiles
   typedef typename Vec<T>::x4 F4;
+  typedef typename Vec<T>::x8 F8;
 
   __shared__ F4 sS[NST][64];       // state block as B-operand halves
   __shared__ F4 sVn[4][64];        // V_new block as B-operand halves
@@ -90,7 +135,7 @@ __global__ __launch_bounds__(kThreads) void stage34_kernel(Stage34Args a) {
   const int gq = lane >> 4;
   const int xi = lane & 15;
 
-  // XCD-aware id mapping: ids u*? with equal id % 8 share an XCD
+  // XCD-aware id mapping: ids with equal id % 8 run on the same XCD
   const int bid = blockIdx.x;
   const int xcd = bid & 7;
   const int slot = bid >> 3;
@@ -115,90 +160,120 @@ __global__ __launch_bounds__(kThreads) void stage34_kernel(Stage34Args a) {
   }
   const char* rec0 = a.ws + a.meta_bytes + ((size_t)h * a.ncp + p0) * a.rec_bytes;
   const size_t state_base = ((size_t)seq * H + h) * K * V + 16 * vb + xi;
+  const int last = nch - 1;
+  // buffer resource over this (sequence, head)'s records (offsets stay < 2^31)
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, 0x7ffffff0, 0x00020000);
+  const int lane_off = 16 * lane;
 
-  // state tiles of this wave: rows 16 * (w * TPW + m) + 4 gq + r, column 16 vb + xi
-  floatx4 S[TPW];
-#pragma unroll
-  for (int m = 0; m < TPW; ++m) {
-    const int rt = w * TPW + m;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      S[m][r] = a.init ? a.init[state_base + (size_t)(16 * rt + 4 * gq + r) * V] : 0.f;
-    F4 y;
-    cvt4(S[m], y);
-    sS[rt][lane] = y;
-  }
-  lds_sync();
-
-  T* out = reinterpret_cast<T*>(a.o);
-  ChunkFrags<T, K> F[2];
-  if (nch > 0) load_frags<T, K>(F[0], rec0, a, w, lane, vb, gq);
-
-  auto step = [&](ChunkFrags<T, K>& f, int c) {
-    int64_t tok0;
-    int len;
-    if (a.varlen) {
-      const int2 ct = ctab[p0 + c];
-      tok0 = ct.x;
-      len = ct.y;
-    } else {
-      tok0 = (int64_t)(p0 + c) * C;
-      len = C;
-    }
-    // V_new and the inter-chunk read for rows 16 w .. 16 w + 15
-    floatx4 accV = zero4(), accO = zero4();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const typename Vec<T>::x8 Sb = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
-      accV = mma32(accV, f.w[kb], Sb);
-      accO = mma32(accO, f.qg[kb], Sb);
-    }
-    const floatx4 vn = widen4(f.u) - accV;
-    F4 vnT;
-    cvt4(vn, vnT);
-    sVn[w][lane] = vnT;
-    lds_sync();
-    const typename Vec<T>::x8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
-    const typename Vec<T>::x8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
-    // intra-chunk contribution, causal: row block w only reads V_new blocks <= w
-    accO = mma32(accO, f.aq[0], Vb0);
-    if (w >= 2) accO = mma32(accO, f.aq[1], Vb1);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * w + 4 * gq + r;
-      if (row < len) {
-        T y;
-        if constexpr (sizeof(T) == 2) y = (T)accO[r]; else y = accO[r];
-        out[((size_t)(tok0 + row) * H + h) * V + 16 * vb + xi] = y;
-      }
-    }
-    // state update for this wave's tiles
+  if (w >= 4) {
+    // ------------------------------------------------------------ state waves
+    const int s = w - 4;
+    floatx4 S[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
-      S[m] = S[m] * f.gam[m];
-      S[m] = mma32(S[m], f.kg[m][0], Vb0);
-      S[m] = mma32(S[m], f.kg[m][1], Vb1);
+      const int rt = s * TPW + m;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        S[m][r] = a.init ? a.init[state_base + (size_t)(16 * rt + 4 * gq + r) * V] : 0.f;
       F4 y;
       cvt4(S[m], y);
-      sS[w * TPW + m][lane] = y;
+      sS[rt][lane] = y;
     }
-    lds_sync();
-  };
-
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) load_frags<T, K>(F[1], rec0 + (size_t)(c + 1) * a.rec_bytes, a, w, lane, vb, gq);
-    step(F[0], c);
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) load_frags<T, K>(F[0], rec0 + (size_t)(c + 2) * a.rec_bytes, a, w, lane, vb, gq);
-    step(F[1], c + 1);
-  }
-
-  if (a.final_state) {
+    if (nch > 0) {
+      StateFrags<T, K> F[NB];
+      // prefetches are unconditional (chunk index clamped to the last chunk): with
+      // no branch around the loads the memory-counter waits stay exact
+      auto issue = [&](StateFrags<T, K>& f, int c) {
+        const int cc = c < last ? c : last;
+        load_state<T, K>(f, rs, cc * (int)a.rec_bytes, a, s, lane_off, 16 * gq);
+      };
 #pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const int rt = w * TPW + m;
+      for (int i = 0; i < NB - 1; ++i) issue(F[i], i);
+      lds_sync();  // initial state published
+      for (int c0 = 0; c0 < nch; c0 += NB) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) a.final_state[state_base + (size_t)(16 * rt + 4 * gq + r) * V] = S[m][r];
+        for (int j = 0; j < NB; ++j) {
+          const int c = c0 + j;
+          if (c >= nch) break;
+          issue(F[(j + NB - 1) % NB], c + NB - 1);
+          StateFrags<T, K>& f = F[j];
+          lds_sync();  // V_new of chunk c published
+          const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
+          const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
+#pragma unroll
+          for (int m = 0; m < TPW; ++m) {
+            S[m] = S[m] * f.gam[m];
+            S[m] = mma32(S[m], f.kg[m][0], Vb0);
+            S[m] = mma32(S[m], f.kg[m][1], Vb1);
+            F4 y;
+            cvt4(S[m], y);
+            sS[s * TPW + m][lane] = y;
+          }
+          lds_sync();  // state after chunk c published
+        }
+      }
+    }
+    if (a.final_state) {
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const int rt = s * TPW + m;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) a.final_state[state_base + (size_t)(16 * rt + 4 * gq + r) * V] = S[m][r];
+      }
+    }
+  } else {
+    // -------------------------------------------------------------- row waves
+    if (nch <= 0) return;
+    const int r0 = w;  // chunk rows 16 r0 .. 16 r0 + 15
+    T* out = reinterpret_cast<T*>(a.o);
+    T* sink = reinterpret_cast<T*>(const_cast<char*>(a.ws) + a.off_sink);
+    RowFrags<T, K> F[NB];
+    auto issue = [&](RowFrags<T, K>& f, int c) {
+      const int cc = c < last ? c : last;
+      load_row<T, K>(f, rs, cc * (int)a.rec_bytes, ctab + p0 + cc, a, r0, lane_off, vb);
+    };
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i) issue(F[i], i);
+    lds_sync();  // initial state published
+    for (int c0 = 0; c0 < nch; c0 += NB) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const int c = c0 + j;
+        if (c >= nch) break;
+        issue(F[(j + NB - 1) % NB], c + NB - 1);
+        RowFrags<T, K>& f = F[j];
+        const int64_t tok0 = a.varlen ? (int64_t)f.ct.x : (int64_t)(p0 + c) * C;
+        const int len = a.varlen ? f.ct.y : C;
+        floatx4 accV = zero4(), accO = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const F8 Sb = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
+          accV = mma32(accV, f.w[kb], Sb);
+          accO = mma32(accO, f.qg[kb], Sb);
+        }
+        const floatx4 vn = widen4(f.u) - accV;
+        F4 vnT;
+        cvt4(vn, vnT);
+        sVn[r0][lane] = vnT;
+        lds_sync();  // V_new of chunk c published
+        const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
+        const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
+        // intra-chunk part, causal: row block r0 reads V_new blocks <= r0
+        accO = mma32(accO, f.aq[0], Vb0);
+        if (r0 >= 2) accO = mma32(accO, f.aq[1], Vb1);
+        // rows past the end of a short chunk store into the sink: no branch
+        // around the stores keeps the memory-counter waits identical on all paths
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int row = 16 * r0 + 4 * gq + rr;
+          T y;
+          if constexpr (sizeof(T) == 2) y = (T)accO[rr]; else y = accO[rr];
+          T* dst = row < len ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + xi : sink;
+          *dst = y;
+        }
+        lds_sync();  // state after chunk c published
+      }
     }
   }
 }
@@ -209,13 +284,13 @@ hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s) 
   if (a.nunits <= 0) return hipSuccess;
   const int nvb = K / 16;
   const int units8 = (a.nunits + 7) / 8;
-  dim3 grid(units8 * 8 * nvb), block(kThreads);
+  dim3 grid(units8 * 8 * nvb), block(kThreads34);
   if (bf16) {
-    if (K == 128) hipLaunchKernelGGL((stage34_kernel<kda::bf16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage34_kernel<kda::bf16, 64>), grid, block, 0, s, a);
+    if (K == 128) hipLaunchKernelGGL((stage34_kernel<kda::bf16, 128, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage34_kernel<kda::bf16, 64, 4>), grid, block, 0, s, a);
   } else {
-    if (K == 128) hipLaunchKernelGGL((stage34_kernel<float, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage34_kernel<float, 64>), grid, block, 0, s, a);
+    if (K == 128) hipLaunchKernelGGL((stage34_kernel<float, 128, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage34_kernel<float, 64, 4>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -60,7 +60,12 @@ def test_workspace_size_formula(lib):
         assert st == 0
         rec = (3 * 64 * K + 64 * 64 + 64 * K) * elem + 4 * K
         rec = (rec + 255) // 256 * 256
-        assert n == 256 + rec * (3 * 256 // 64) * 5
+        info = _lib.KdaWorkspaceInfo()
+        assert lib.kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
+        # metadata: header, chunk table, sequence table, order, then a 256-byte sink
+        meta = ((64 + 8 * 12 + 8 * 3 + 4 * 3 + 255) // 256) * 256 + 256
+        assert info.records_offset == meta and info.record_bytes == rec
+        assert n == meta + rec * (3 * 256 // 64) * 5
     # varlen: ceil(T/64) + N chunk slots per head
     p = P(T=1000, num_seqs=7)
     st, n = ws_bytes(lib, p)
