@@ -51,6 +51,32 @@ def alg_bytes_per_token_head(K, V, elem, gelem, belem):
     return s12 + rec, s34
 
 
+KERNEL_SOURCES = {
+    "stage12": ["kda_stage12.hip", "kda_device.h", "kda_layout.h", "kda_kernels.h"],
+    "stage34": ["kda_stage34.hip", "kda_device.h", "kda_layout.h", "kda_kernels.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    m = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        m.update(open(os.path.join(ROOT, "kimi_delta_attention_03_amd", "csrc", f), "rb").read())
+    return m.hexdigest()[:16]
+
+
+def measured_traffic(workload_name, kernel):
+    """Calibrated HBM bytes per launch from the committed rocprofv3 counter runs,
+    or None when they were taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", f"traffic_kda_fwd_{workload_name}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get("kernels", {}).get(kernel)
+    if not rec or rec.get("source_sha256_16") != kernel_source_hash(kernel):
+        return None
+    return rec["traffic_bytes"]
+
+
 def time_loop(fn, reps, torch):
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -100,6 +126,8 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the KDA forward here is a single-GPU kernel path); "
@@ -107,6 +135,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        ms = time_loop(lambda: dst.copy_(src), 5, torch)
+        print(json.dumps({"copy_bytes": n, "ms": ms, "GBps_read_plus_write": 2 * n / ms / 1e6}), flush=True)
+        return
     import kimi_delta_attention_03_amd as kda
     from kimi_delta_attention_03_amd.synthetic import WORKLOADS, workload
 
@@ -172,7 +209,8 @@ def main():
         "hbm_alg_frac": bytes_total / s_step / PEAK_HBM,
         "kernels_ms": {"stage12": ms12, "stage34": ms34},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
-                     "unit": "GB/s", "frac": achieved * 1e9 / PEAK_HBM, "traffic": None,
+                     "unit": "GB/s", "frac": achieved * 1e9 / PEAK_HBM,
+                     "traffic": measured_traffic(cfg["name"], dom),
                      "alg_bytes_per_launch": dom_bytes},
         "record": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                    "device": torch.cuda.get_device_name(0),
