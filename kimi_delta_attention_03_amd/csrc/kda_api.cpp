@@ -48,7 +48,7 @@ kda_status check_params(const kda_fwd_params* p) {
   }
   // 32-bit indexing limits of the kernels' tables
   const int64_t tokens = p->B * p->T;
-  if (tokens > (int64_t)INT32_MAX / 2 || p->H > 65536 || tokens * p->H * p->K > ((int64_t)1 << 40))
+  if (tokens > (int64_t)INT32_MAX / 2 || p->H > 16384 || tokens * p->H * p->K > ((int64_t)1 << 40))
     return fail(KDA_ERR_UNSUPPORTED, "problem too large");
   if (p->num_seqs > (1 << 24)) return fail(KDA_ERR_UNSUPPORTED, "too many sequences");
   return KDA_OK;

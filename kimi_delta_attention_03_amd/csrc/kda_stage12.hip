@@ -1,6 +1,8 @@
-// Stage 1+2 of the chunkwise KDA forward on gfx950: one workgroup (4 waves)
-// per (chunk, head). Everything a chunk needs stays in LDS; the outputs are
-// written once, as MFMA fragments, into the chunk's workspace record.
+// Stage 1+2 of the chunkwise KDA forward on gfx950. Workgroups (4 waves) are
+// persistent: each loops over (chunk, head) items, keeps everything an item
+// needs in LDS and writes the outputs once, as MFMA fragments, into the item's
+// workspace record. The raw inputs of the next item are loaded into registers
+// while the current one is in its solve and W/U phases.
 //
 // What it computes for a chunk of C = 64 tokens (Tokamax "chunk_kda_fwd
 // design doc", sections 4.1.2-4.1.4 and 9.1.3-9.1.5, Paper Eq. 6-7):
@@ -19,6 +21,10 @@
 // g >= -5 bound, section "What's the catch?"), so nothing overflows, and r
 // never depends on a later token: every output row is a function of tokens
 // up to that row only (section "Decisions Decisions").
+//
+// Inputs are read with buffer loads whose descriptor covers exactly the valid
+// rows of the chunk: rows past the end of a short (variable-length) chunk read
+// as zeros, so no load sits behind a branch.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -27,27 +33,46 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // block-wide LDS synchronisation without waiting for global memory traffic
 __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ float ld_scalar(const void* p, size_t idx, int is_f32) {
-  return is_f32 ? reinterpret_cast<const float*>(p)[idx]
-                : (float)reinterpret_cast<const bf16*>(p)[idx];
-}
+// 4 consecutive elements of T as a raw register value
+template <typename T> struct Raw4;
+template <> struct Raw4<bf16> { typedef u32x2 type; };
+template <> struct Raw4<float> { typedef u32x4 type; };
 
 template <typename T>
-__device__ __forceinline__ float sumsq16(uint4 u) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ typename Raw4<T>::type bload4(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (sizeof(T) == 2) return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  else return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+
+__device__ __forceinline__ floatx4 bf16pair4(uint32_t a, uint32_t b) {
+  return floatx4{__uint_as_float(a << 16), __uint_as_float(a & 0xffff0000u),
+                 __uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)};
+}
+template <typename T>
+__device__ __forceinline__ floatx4 unpack4(const typename Raw4<T>::type& x) {
+  if constexpr (sizeof(T) == 2) return bf16pair4(x[0], x[1]);
+  else return floatx4{__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]), __uint_as_float(x[3])};
+}
+
+// squares of the elements in a 16-byte chunk of T
+template <typename T>
+__device__ __forceinline__ float sumsq16(const u32x4& u) {
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if constexpr (sizeof(T) == 2) {  // two bf16 per word: the high half is the bf16 bit pattern
-      const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+      const float lo = __uint_as_float(u[i] << 16), hi = __uint_as_float(u[i] & 0xffff0000u);
       s += lo * lo + hi * hi;
     } else {
-      const float x = __uint_as_float(w[i]);
+      const float x = __uint_as_float(u[i]);
       s += x * x;
     }
   }
@@ -70,27 +95,45 @@ __device__ __forceinline__ void store_frag8(char* base, size_t frag_elem_index, 
   *reinterpret_cast<typename Vec<T>::x8*>(reinterpret_cast<T*>(base) + frag_elem_index) = y;
 }
 
-template <typename T, int K>
-__global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
+// descriptor over rows [0, len) of a [tokens, H, rowbytes] tensor, starting at
+// (token tok0, head h)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int64_t tok0, int h, int H,
+                                                            int rowbytes, int len) {
+  const char* base = reinterpret_cast<const char*>(p) + ((size_t)tok0 * H + h) * (size_t)rowbytes;
+  const int n = len > 0 ? (len - 1) * H * rowbytes + rowbytes : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, 0x00020000);
+}
+
+template <typename T, int K, bool GF32>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
+void stage12_kernel(Stage12Args a) {
   constexpr int C = kChunk;
   constexpr int V = K;
+  constexpr int E = (int)sizeof(T);
   constexpr int NKB = K / 32;          // 32-wide channel blocks
   constexpr int GS = K + 4;            // sG row stride (floats)
-  constexpr int KS = (sizeof(T) == 2) ? K + 8 : K + 4;  // sK / sV row stride (elements)
+  constexpr int KS = (E == 2) ? K + 8 : K + 4;  // sK / sV row stride (elements)
   constexpr int AS = C + 4;            // sA row stride (floats)
-  constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int EPC = 16 / E;          // elements per 16-byte chunk
   constexpr int CPR = K / EPC;         // 16-byte chunks per row
   constexpr int NCH = C * CPR / kThreads;  // chunks per thread for a C x K tile
-  constexpr int TPC = kThreads / K;    // threads per channel in the cumsum
-  constexpr int RPS = C / TPC;         // rows per cumsum segment
+  constexpr int kRowStep = kThreads / CPR; // rows between a thread's chunks
+  constexpr int CPT = K / 16;          // gate channels per thread in the cumsum
+  constexpr int SEG = 16;              // row segments of the cumsum
+  constexpr int RPS = C / SEG;         // rows per segment
+  constexpr int GB = CPT * (GF32 ? 4 : 2);       // gate bytes per thread and row
+  constexpr int GL = GB / 16 > 0 ? GB / 16 : 1;  // 16-byte gate loads per row (8-byte if GB == 8)
+  constexpr bool kPrefetch = (E == 2);  // fp32 lacks the registers: load at item start
   static_assert(NCH * kThreads == C * CPR, "tile split");
+  static_assert(kThreads % CPR == 0, "rows per step");
 
   __shared__ __attribute__((aligned(16))) float sG[C * GS];   // G, later V (as T)
   __shared__ __attribute__((aligned(16))) T sK[C * KS];
   __shared__ __attribute__((aligned(16))) float sA[C * AS];   // scratch, L, then A
-  __shared__ float sB[C], sQn[C], sKn[C];
+  __shared__ float sB[C], sKn[C];
   T* sV = reinterpret_cast<T*>(sG);
   static_assert(sizeof(T) * C * KS <= sizeof(float) * C * GS, "sV fits in sG");
+  static_assert(SEG * K <= C * AS, "cumsum totals fit in sA");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -100,358 +143,446 @@ __global__ __launch_bounds__(kThreads, 1) void stage12_kernel(Stage12Args a) {
   const int gq = lane >> 4;
   const int xi = lane & 15;
   const int H = a.H;
-  const int p = blockIdx.x / H;
-  const int h = blockIdx.x - p * H;
+  const int nitems = (a.varlen ? *reinterpret_cast<const int*>(a.ws) : (int)a.ncp) * H;
+  if ((int)blockIdx.x >= nitems) return;
 
-  int64_t tok0;
-  int len;
-  if (a.varlen) {
-    const int2 ct = reinterpret_cast<const int2*>(a.ws + a.off_chunk_tab)[p];
-    tok0 = ct.x;
-    len = ct.y;
-    if (len <= 0) return;  // unused chunk slot
-  } else {
-    tok0 = (int64_t)p * C;
-    len = C;
-  }
-  char* rec = a.ws + a.meta_bytes + ((size_t)h * a.ncp + p) * a.rec_bytes;
-  const T* qg_ = reinterpret_cast<const T*>(a.q);
-  const T* kg_ = reinterpret_cast<const T*>(a.k);
-  const T* vg_ = reinterpret_cast<const T*>(a.v);
-  auto rowK = [&](int i) -> size_t { return ((size_t)(tok0 + i) * H + h) * K; };
-  auto rowV = [&](int i) -> size_t { return ((size_t)(tok0 + i) * H + h) * V; };
-
-  // ---------------- phase 1: beta, gate cumsum, k -> LDS, norms, v prefetch
-  if (tid < C) sB[tid] = tid < len ? ld_scalar(a.beta, (size_t)(tok0 + tid) * H + h, a.beta_f32) : 0.f;
-
-  float loc[RPS];
-  {
-    const int c = tid % K;
-    const int seg = tid / K;
-    float run = 0.f;
-#pragma unroll
-    for (int r = 0; r < RPS; ++r) {
-      const int i = seg * RPS + r;
-      const float gv = i < len ? ld_scalar(a.g, rowK(i) + c, a.g_f32) : 0.f;
-      run += gv;
-      loc[r] = run;
-    }
-    sA[seg * K + c] = run;  // segment totals (sA is free until the relations)
-  }
-
-  // k and v tiles, 16 bytes per thread and chunk; kept as vector values (not
-  // arrays) so they stay in registers until they are written to LDS
-  typedef uint32_t rawv __attribute__((ext_vector_type(4 * NCH)));
-  rawv kraw, vraw;
-#pragma unroll
-  for (int m = 0; m < NCH; ++m) {
-    const int ci = tid + m * kThreads;
-    const int row = ci / CPR, col = (ci % CPR) * EPC;
-    uint4 kk = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-    if (row < len) {
-      kk = *reinterpret_cast<const uint4*>(kg_ + rowK(row) + col);
-      vv = *reinterpret_cast<const uint4*>(vg_ + rowV(row) + col);
-    }
-    kraw[4 * m] = kk.x; kraw[4 * m + 1] = kk.y; kraw[4 * m + 2] = kk.z; kraw[4 * m + 3] = kk.w;
-    vraw[4 * m] = vv.x; vraw[4 * m + 1] = vv.y; vraw[4 * m + 2] = vv.z; vraw[4 * m + 3] = vv.w;
-  }
-  auto part = [](const rawv& r, int m) { return uint4{r[4 * m], r[4 * m + 1], r[4 * m + 2], r[4 * m + 3]}; };
-#pragma unroll
-  for (int m = 0; m < NCH; ++m) {
-    const int ci = tid + m * kThreads;
-    const int row = ci / CPR, col = (ci % CPR) * EPC;
-    *reinterpret_cast<uint4*>(sK + row * KS + col) = part(kraw, m);
-  }
-  if (a.l2norm) {
-    // rows are owned by CPR consecutive lanes: reduce the squares across them
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) {
-      const int ci = tid + m * kThreads;
-      const int row = ci / CPR, col = (ci % CPR) * EPC;
-      float sk = sumsq16<T>(part(kraw, m));
-      uint4 qr = {0u, 0u, 0u, 0u};
-      if (row < len) qr = *reinterpret_cast<const uint4*>(qg_ + rowK(row) + col);
-      float sq = sumsq16<T>(qr);
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) {
-        sk += __shfl_xor(sk, o, 64);
-        sq += __shfl_xor(sq, o, 64);
-      }
-      if (col == 0) {
-        sKn[row] = 1.f / fmaxf(sqrtf(sk), a.l2eps);
-        sQn[row] = 1.f / fmaxf(sqrtf(sq), a.l2eps);
-      }
-    }
-  } else if (tid < C) {
-    sKn[tid] = 1.f;
-    sQn[tid] = 1.f;
-  }
-  lds_sync();
-  {
-    const int c = tid % K;
-    const int seg = tid / K;
-    float carry = 0.f;
-    for (int s = 0; s < seg; ++s) carry += sA[s * K + c];
-#pragma unroll
-    for (int r = 0; r < RPS; ++r) sG[(seg * RPS + r) * GS + c] = (carry + loc[r]) * kLog2e;
-  }
-  lds_sync();
-
-  // ---------------- phase 2: relation tiles for query block w (this wave)
-  // Aqk^T and L^T tiles (keys j x queries i) = Khat_j . (Qhat_i | Khat'_i):
-  //   Qhat_i = q_i 2^(G_i - r), Khat'_i = k_i 2^(G_i - r), Khat_j = k_j 2^(r - G_j),
-  //   r = G of row 16 w.
+  // per-thread constant byte offsets inside one (chunk, head) row block
+  const int RBK = K * E, RBV = V * E, RBG = K * (GF32 ? 4 : 2), RBB = a.beta_f32 ? 4 : 2;
+  const int kv_row = tid / CPR, kv_col = (tid % CPR) * EPC;
+  const int off_k0 = kv_row * H * RBK + kv_col * E;
+  const int off_v0 = kv_row * H * RBV + kv_col * E;
+  const int kstep = kRowStep * H * RBK, vstep = kRowStep * H * RBV;
+  const int cg = tid % 16, seg = tid / 16;
+  const int off_g0 = seg * RPS * H * RBG + cg * CPT * (GF32 ? 4 : 2);
   const int irow = 16 * w + xi;
-  {
-    const float qn = sQn[irow];
-    const float kni = sKn[irow];
-    floatx4 accQ[4], accL[4];
+  const int off_q0 = irow * H * RBK + 4 * gq * E;
+  const int off_b = (tid & 63) * H * RBB;
+
+  struct Item { int p, h, len; int64_t tok0; };
+  const int2* ctab = reinterpret_cast<const int2*>(a.ws + a.off_chunk_tab);
+  auto item_of = [&](int it) {
+    Item r;
+    r.p = it / H;
+    r.h = it - r.p * H;
+    if (a.varlen) {
+      const int2 ct = ctab[r.p];
+      r.tok0 = ct.x;
+      r.len = ct.y;
+    } else {
+      r.tok0 = (int64_t)r.p * C;
+      r.len = C;
+    }
+    return r;
+  };
+
+  // raw inputs of one item, as loaded
+  struct RawIn {
+    u32x4 k[NCH], v[NCH];
+    u32x4 g[RPS][GL];
+    typename Raw4<T>::type q[NKB][2];
+    uint32_t b;
+  };
+  auto issue_qkgb = [&](RawIn& r, const Item& it) {
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k, it.tok0, it.h, H, RBK, it.len);
+    const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q, it.tok0, it.h, H, RBK, it.len);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(a.g, it.tok0, it.h, H, RBG, it.len);
+    const __amdgpu_buffer_rsrc_t rb = rows_rsrc(a.beta, it.tok0, it.h, H, RBB, it.len);
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) { accQ[bj] = zero4(); accL[bj] = zero4(); }
-    const T* qrow = qg_ + rowK(irow < len ? irow : 0);
+    for (int m = 0; m < NCH; ++m) r.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_k0 + m * kstep, 0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int c0 = 32 * kb + 4 * gq;
-      const floatx8 Gi = stackf(ldsf4(sG + irow * GS + c0), ldsf4(sG + irow * GS + c0 + 16));
-      const floatx8 Gr = stackf(ldsf4(sG + (16 * w) * GS + c0), ldsf4(sG + (16 * w) * GS + c0 + 16));
-      floatx8 qv = stackf(load4_f32(qrow + c0), load4_f32(qrow + c0 + 16));
-      if (irow >= len) qv = floatx8{0, 0, 0, 0, 0, 0, 0, 0};
-      const floatx8 kv = lds_row8<T, KS>(sK, irow, c0);
-      floatx8 qh, kh, qgv;
+      r.q[kb][0] = bload4<T>(rq, off_q0 + 32 * kb * E);
+      r.q[kb][1] = bload4<T>(rq, off_q0 + (32 * kb + 16) * E);
+    }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float e = exp2_fast(Gi[t] - Gr[t]);
-        qh[t] = qv[t] * qn * e;
-        kh[t] = kv[t] * kni * e;
-        qgv[t] = a.scale * qv[t] * qn * exp2_fast(Gi[t]);
-      }
-      store_frag8<T>(rec + a.off_qg, ((size_t)(w * NKB + kb) * 64 + lane) * 8, qgv);
-      typename Vec<T>::x8 qhT, khT;
-      cvt8(qh, qhT);
-      cvt8(kh, khT);
+    for (int rr = 0; rr < RPS; ++rr) {
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        if (bj <= w) {
-          const int j = 16 * bj + xi;
-          const floatx8 Gj = stackf(ldsf4(sG + j * GS + c0), ldsf4(sG + j * GS + c0 + 16));
-          const floatx8 kj = lds_row8<T, KS>(sK, j, c0);
-          const float knj = sKn[j];
-          floatx8 kk;
-#pragma unroll
-          for (int t = 0; t < 8; ++t) kk[t] = kj[t] * knj * exp2_fast(Gr[t] - Gj[t]);
-          typename Vec<T>::x8 kkT;
-          cvt8(kk, kkT);
-          accQ[bj] = mma32(accQ[bj], kkT, qhT);
-          accL[bj] = mma32(accL[bj], kkT, khT);
+      for (int l = 0; l < GL; ++l) {
+        if constexpr (GB >= 16) {
+          r.g[rr][l] = __builtin_amdgcn_raw_buffer_load_b128(rg, off_g0 + rr * H * RBG + 16 * l, 0, 0);
+        } else {
+          const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(rg, off_g0 + rr * H * RBG, 0, 0);
+          r.g[rr][l] = u32x4{x[0], x[1], 0u, 0u};
         }
       }
     }
-    // epilogue: lane (gq, xi) holds, per tile bj, row irow and columns 16 bj + 4 gq + r
-    const float bi = sB[irow];
-    floatx4 aq[4];
+    r.b = a.beta_f32 ? __builtin_amdgcn_raw_buffer_load_b32(rb, off_b, 0, 0)
+                     : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off_b, 0, 0);
+  };
+  auto issue_v = [&](RawIn& r, const Item& it) {
+    const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v, it.tok0, it.h, H, RBV, it.len);
 #pragma unroll
-    for (int bj = 0; bj < 4; ++bj) {
-      floatx4 lv;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const bool diag = (bj == w);
-        const int jc = 4 * gq + r;
-        aq[bj][r] = (bj < w || (diag && jc <= xi)) ? a.scale * accQ[bj][r] : 0.f;
-        lv[r] = (bj < w || (diag && jc < xi)) ? bi * accL[bj][r] : 0.f;
-      }
-      if (bj <= w) *reinterpret_cast<floatx4*>(sA + irow * AS + 16 * bj + 4 * gq) = lv;
-    }
-    if (w == 0 || w == 2)  // blocks (0,1) and (2,3) are read as zeros later
-      *reinterpret_cast<floatx4*>(sA + irow * AS + 16 * (w + 1) + 4 * gq) = zero4();
-    // Aqk fragments of query block w: kb' = 0 from tiles (0, 1), kb' = 1 from (2, 3)
-    store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 0) * 64 + lane) * 8, stackf(aq[0], aq[1]));
-    if (w >= 2)
-      store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 1) * 64 + lane) * 8, stackf(aq[2], aq[3]));
+    for (int m = 0; m < NCH; ++m) r.v[m] = __builtin_amdgcn_raw_buffer_load_b128(rv, off_v0 + m * vstep, 0, 0);
+  };
+
+  RawIn R;
+  if constexpr (kPrefetch) {
+    const Item it0 = item_of(blockIdx.x);
+    issue_qkgb(R, it0);
+    issue_v(R, it0);
   }
 
-  // ---------------- phase 3: gated keys kg^T and gamma (only G, k needed)
-  {
-    constexpr int TPW = K / 64;  // 16-channel row tiles per wave
+  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
+    const Item it = item_of(item);
+    const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : nitems - 1;
+    const Item nx = item_of(nxt);
+    if constexpr (!kPrefetch) {
+      issue_qkgb(R, it);
+      issue_v(R, it);
+    }
+    const int p = it.p, h = it.h;
+    char* rec = a.ws + a.meta_bytes + ((size_t)h * a.ncp + p) * a.rec_bytes;
+
+    // ---------------- phase 1: beta, k -> LDS, k norms, gate cumsum
+    if (tid < C) {
+      const uint32_t bw = R.b;
+      sB[tid] = a.beta_f32 ? __uint_as_float(bw) : __uint_as_float(bw << 16);
+    }
 #pragma unroll
-    for (int m = 0; m < TPW; ++m) {
-      const int rt = w * TPW + m;
-      const int ch = 16 * rt + xi;
-      const float Glast = sG[(C - 1) * GS + ch];
+    for (int m = 0; m < NCH; ++m)
+      *reinterpret_cast<u32x4*>(sK + (kv_row + m * kRowStep) * KS + kv_col) = R.k[m];
+    if (a.l2norm) {
+      // rows are owned by CPR consecutive lanes: reduce the squares across them
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        floatx8 x;
+      for (int m = 0; m < NCH; ++m) {
+        float sk = sumsq16<T>(R.k[m]);
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) sk += __shfl_xor(sk, o, 64);
+        if (kv_col == 0) sKn[kv_row + m * kRowStep] = 1.f / fmaxf(sqrtf(sk), a.l2eps);
+      }
+    } else if (tid < C) {
+      sKn[tid] = 1.f;
+    }
+    // inclusive cumsum over rows: thread (cg, seg) sums its CPT channels over the
+    // RPS rows of segment seg into sG, then adds the totals of all earlier
+    // segments (in segment order) and converts to log2 units
+    {
+      float run[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) run[c] = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < RPS; ++rr) {
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) {
+          float gv;
+          if constexpr (GF32) gv = __uint_as_float(R.g[rr][c / 4][c % 4]);
+          else gv = (c & 1) ? __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] & 0xffff0000u)
+                            : __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] << 16);
+          run[c] += gv;
+        }
+#pragma unroll
+        for (int c = 0; c < CPT; c += 4)
+          *reinterpret_cast<floatx4*>(sG + (seg * RPS + rr) * GS + cg * CPT + c) =
+              floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
+      }
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4)
+        *reinterpret_cast<floatx4*>(sA + seg * K + cg * CPT + c) = floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
+    }
+    lds_sync();
+    {
+#pragma unroll
+      for (int c = 0; c < CPT; c += 4) {
+        floatx4 carry = zero4();
+#pragma unroll
+        for (int s = 0; s < SEG - 1; ++s) {
+          const floatx4 t4 = ldsf4(sA + s * K + cg * CPT + c);
+          if (s < seg) carry += t4;
+        }
+#pragma unroll
+        for (int rr = 0; rr < RPS; ++rr) {
+          float* gp = sG + (seg * RPS + rr) * GS + cg * CPT + c;
+          *reinterpret_cast<floatx4*>(gp) = (carry + ldsf4(gp)) * kLog2e;
+        }
+      }
+    }
+    lds_sync();
+
+    // ---------------- phase 2: relation tiles for query block w (this wave)
+    // Aqk^T and L^T tiles (keys j x queries i) = Khat_j . (Qhat_i | Khat'_i):
+    //   Qhat_i = q_i 2^(G_i - r), Khat'_i = k_i 2^(G_i - r), Khat_j = k_j 2^(r - G_j),
+    //   r = G of row 16 w.
+    {
+      const float kni = sKn[irow];
+      // q of row irow: this lane holds channels 32 kb + 4 gq + {0..3, 16..19}; the
+      // row's L2 norm sums the squares over the 4 lane groups of the row
+      float qn = 1.f;
+      if (a.l2norm) {
+        float qss = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const floatx8 x = stackf(unpack4<T>(R.q[kb][0]), unpack4<T>(R.q[kb][1]));
+#pragma unroll
+          for (int t = 0; t < 8; ++t) qss += x[t] * x[t];
+        }
+        qss += __shfl_xor(qss, 16, 64);
+        qss += __shfl_xor(qss, 32, 64);
+        qn = 1.f / fmaxf(sqrtf(qss), a.l2eps);
+      }
+      floatx4 accQ[4], accL[4];
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) { accQ[bj] = zero4(); accL[bj] = zero4(); }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const int c0 = 32 * kb + 4 * gq;
+        const floatx8 Gi = stackf(ldsf4(sG + irow * GS + c0), ldsf4(sG + irow * GS + c0 + 16));
+        const floatx8 Gr = stackf(ldsf4(sG + (16 * w) * GS + c0), ldsf4(sG + (16 * w) * GS + c0 + 16));
+        const floatx8 qv = stackf(unpack4<T>(R.q[kb][0]), unpack4<T>(R.q[kb][1]));
+        const floatx8 kv = lds_row8<T, KS>(sK, irow, c0);
+        floatx8 qh, kh, qgv;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
-          x[t] = to_f32(sK[j * KS + ch]) * sKn[j] * exp2_fast(Glast - sG[j * GS + ch]);
+          const float e = exp2_fast(Gi[t] - Gr[t]);
+          qh[t] = qv[t] * qn * e;
+          kh[t] = kv[t] * kni * e;
+          qgv[t] = a.scale * qv[t] * qn * exp2_fast(Gi[t]);
         }
-        store_frag8<T>(rec + a.off_kg, ((size_t)(rt * 2 + kb) * 64 + lane) * 8, x);
-      }
-    }
-    if (tid < K) reinterpret_cast<float*>(rec + a.off_gam)[tid] = exp2_fast(sG[(C - 1) * GS + tid]);
-  }
-  lds_sync();
-
-  // ---------------- phase 4: A = (I + L)^-1 in fp32
-  // 4a: diagonal 16x16 blocks by forward substitution, wave w -> block w,
-  //     lane column xi (lanes of the other groups compute the same values)
-  {
-    float x[16];
+        store_frag8<T>(rec + a.off_qg, ((size_t)(w * NKB + kb) * 64 + lane) * 8, qgv);
+        typename Vec<T>::x8 qhT, khT;
+        cvt8(qh, qhT);
+        cvt8(kh, khT);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == xi) ? 1.f : 0.f;
-    const float* Lb = sA + (16 * w) * AS + 16 * w;
+        for (int bj = 0; bj < 4; ++bj) {
+          if (bj <= w) {
+            const int j = 16 * bj + xi;
+            const floatx8 Gj = stackf(ldsf4(sG + j * GS + c0), ldsf4(sG + j * GS + c0 + 16));
+            const floatx8 kj = lds_row8<T, KS>(sK, j, c0);
+            const float knj = sKn[j];
+            floatx8 kk;
 #pragma unroll
-    for (int j = 0; j < 15; ++j) {
-#pragma unroll
-      for (int i = j + 1; i < 16; ++i) x[i] -= Lb[i * AS + j] * x[j];
-    }
-    if (gq == 0) {
-      float* Db = sA + (16 * w) * AS + 16 * w;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Db[i * AS + xi] = x[i];
-    }
-  }
-  lds_sync();
-  // 4b: block column w below the diagonal:
-  //     A_{ib,w} = -D_ib * sum_{kb=w}^{ib-1} L_{ib,kb} A_{kb,w}
-  floatx4 Ab[4];
-  {
-    floatx4 Dw;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) Dw[s] = sA[(16 * w + 4 * gq + s) * AS + 16 * w + xi];
-#pragma unroll
-    for (int ib = 1; ib < 4; ++ib) {
-      Ab[ib] = zero4();
-      if (ib > w) {
-        floatx4 P = zero4();
-#pragma unroll
-        for (int kb = 0; kb < 3; ++kb) {
-          if (kb >= w && kb < ib) {
-            const floatx4 La = ldsf4(sA + (16 * ib + xi) * AS + 16 * kb + 4 * gq);
-            const floatx4 Bk = (kb == w) ? Dw : Ab[kb];
-            P = mma16_f32(P, La, Bk);
+            for (int t = 0; t < 8; ++t) kk[t] = kj[t] * knj * exp2_fast(Gr[t] - Gj[t]);
+            typename Vec<T>::x8 kkT;
+            cvt8(kk, kkT);
+            accQ[bj] = mma32(accQ[bj], kkT, qhT);
+            accL[bj] = mma32(accL[bj], kkT, khT);
           }
         }
-        const floatx4 Da = ldsf4(sA + (16 * ib + xi) * AS + 16 * ib + 4 * gq);
-        const floatx4 R = mma16_f32(zero4(), Da, P);
-        Ab[ib] = -R;
       }
-    }
-  }
-  lds_sync();
+      // epilogue: lane (gq, xi) holds, per tile bj, row irow and columns 16 bj + 4 gq + r
+      const float bi = sB[irow];
+      floatx4 aq[4];
 #pragma unroll
-  for (int ib = 1; ib < 4; ++ib) {
-    if (ib > w) {
+      for (int bj = 0; bj < 4; ++bj) {
+        floatx4 lv;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sA[(16 * ib + 4 * gq + r) * AS + 16 * w + xi] = Ab[ib][r];
-    }
-  }
-  lds_sync();
-
-  // ---------------- phase 5a: W^T tiles = (beta k 2^G)^T A^T
-  // A fragments (rt, kb) for the causal pairs: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
-  typename Vec<T>::x8 Af[4][2];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (kb <= rt / 2) {
-        const int c0 = 32 * kb + 4 * gq;
-        const floatx8 x = stackf(ldsf4(sA + (16 * rt + xi) * AS + c0),
-                                 ldsf4(sA + (16 * rt + xi) * AS + c0 + 16));
-        cvt8(x, Af[rt][kb]);
-      }
-    }
-  }
-  {
-    const int kbp = w % NKB;             // W fragment column block of this wave
-    constexpr int RSTEP = 4 / NKB;       // rt stride between this wave's row tiles
-    const int rt0 = w / NKB;
-    typename Vec<T>::x8 BKf[2][2];       // [ct 2kbp / 2kbp+1][kb]
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const int ch = 16 * (2 * kbp + cc) + xi;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        floatx8 x;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
-          x[t] = sB[j] * to_f32(sK[j * KS + ch]) * sKn[j] * exp2_fast(sG[j * GS + ch]);
+        for (int r = 0; r < 4; ++r) {
+          const bool diag = (bj == w);
+          const int jc = 4 * gq + r;
+          aq[bj][r] = (bj < w || (diag && jc <= xi)) ? a.scale * accQ[bj][r] : 0.f;
+          lv[r] = (bj < w || (diag && jc < xi)) ? bi * accL[bj][r] : 0.f;
         }
-        cvt8(x, BKf[cc][kb]);
+        if (bj <= w) *reinterpret_cast<floatx4*>(sA + irow * AS + 16 * bj + 4 * gq) = lv;
+      }
+      if (w == 0 || w == 2)  // blocks (0,1) and (2,3) are read as zeros later
+        *reinterpret_cast<floatx4*>(sA + irow * AS + 16 * (w + 1) + 4 * gq) = zero4();
+      // Aqk fragments of query block w: kb' = 0 from tiles (0, 1), kb' = 1 from (2, 3)
+      store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 0) * 64 + lane) * 8, stackf(aq[0], aq[1]));
+      if (w >= 2)
+        store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 1) * 64 + lane) * 8, stackf(aq[2], aq[3]));
+    }
+
+    // ---------------- phase 3: gated keys kg^T and gamma (only G, k needed)
+    {
+      constexpr int TPW = K / 64;  // 16-channel row tiles per wave
+#pragma unroll
+      for (int m = 0; m < TPW; ++m) {
+        const int rt = w * TPW + m;
+        const int ch = 16 * rt + xi;
+        const float Glast = sG[(C - 1) * GS + ch];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          floatx8 x;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
+            x[t] = to_f32(sK[j * KS + ch]) * sKn[j] * exp2_fast(Glast - sG[j * GS + ch]);
+          }
+          store_frag8<T>(rec + a.off_kg, ((size_t)(rt * 2 + kb) * 64 + lane) * 8, x);
+        }
+      }
+      if (tid < K) reinterpret_cast<float*>(rec + a.off_gam)[tid] = exp2_fast(sG[(C - 1) * GS + tid]);
+    }
+    // q, k, g and beta of this item are consumed: start loading the next item's
+    if constexpr (kPrefetch) issue_qkgb(R, nx);
+    lds_sync();
+
+    // ---------------- phase 4: A = (I + L)^-1 in fp32
+    // 4a: diagonal 16x16 blocks by forward substitution, wave w -> block w,
+    //     lane column xi (lanes of the other groups compute the same values)
+    {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = (i == xi) ? 1.f : 0.f;
+      const float* Lb = sA + (16 * w) * AS + 16 * w;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) {
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= Lb[i * AS + j] * x[j];
+      }
+      if (gq == 0) {
+        float* Db = sA + (16 * w) * AS + 16 * w;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Db[i * AS + xi] = x[i];
       }
     }
-    // rt runs over compile-time values (a register array indexed by a runtime
-    // value becomes a compare/select chain); the wave-uniform guard picks the
-    // row tiles of this wave
+    lds_sync();
+    // 4b: block column w below the diagonal:
+    //     A_{ib,w} = -D_ib * sum_{kb=w}^{ib-1} L_{ib,kb} A_{kb,w}
+    floatx4 Ab[4];
+    {
+      floatx4 Dw;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Dw[s] = sA[(16 * w + 4 * gq + s) * AS + 16 * w + xi];
+#pragma unroll
+      for (int ib = 1; ib < 4; ++ib) {
+        Ab[ib] = zero4();
+        if (ib > w) {
+          floatx4 P = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 3; ++kb) {
+            if (kb >= w && kb < ib) {
+              const floatx4 La = ldsf4(sA + (16 * ib + xi) * AS + 16 * kb + 4 * gq);
+              const floatx4 Bk = (kb == w) ? Dw : Ab[kb];
+              P = mma16_f32(P, La, Bk);
+            }
+          }
+          const floatx4 Da = ldsf4(sA + (16 * ib + xi) * AS + 16 * ib + 4 * gq);
+          const floatx4 R = mma16_f32(zero4(), Da, P);
+          Ab[ib] = -R;
+        }
+      }
+    }
+    lds_sync();
+#pragma unroll
+    for (int ib = 1; ib < 4; ++ib) {
+      if (ib > w) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sA[(16 * ib + 4 * gq + r) * AS + 16 * w + xi] = Ab[ib][r];
+      }
+    }
+    lds_sync();
+
+    // ---------------- phase 5a: W^T tiles = (beta k 2^G)^T A^T
+    // A fragments (rt, kb) for the causal pairs: (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+    typename Vec<T>::x8 Af[4][2];
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      if ((rt - rt0) % RSTEP != 0) continue;
-      floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         if (kb <= rt / 2) {
-          acc0 = mma32(acc0, BKf[0][kb], Af[rt][kb]);
-          acc1 = mma32(acc1, BKf[1][kb], Af[rt][kb]);
+          const int c0 = 32 * kb + 4 * gq;
+          const floatx8 x = stackf(ldsf4(sA + (16 * rt + xi) * AS + c0),
+                                   ldsf4(sA + (16 * rt + xi) * AS + c0 + 16));
+          cvt8(x, Af[rt][kb]);
         }
       }
-      store_frag8<T>(rec + a.off_w, ((size_t)(rt * NKB + kbp) * 64 + lane) * 8, stackf(acc0, acc1));
     }
-  }
-  lds_sync();  // G and k are dead: reuse sG for v
-
-  // ---------------- phase 5b/5c: U tiles = A (beta v), accumulator layout
+    {
+      const int kbp = w % NKB;             // W fragment column block of this wave
+      constexpr int RSTEP = 4 / NKB;       // rt stride between this wave's row tiles
+      const int rt0 = w / NKB;
+      typename Vec<T>::x8 BKf[2][2];       // [ct 2kbp / 2kbp+1][kb]
 #pragma unroll
-  for (int m = 0; m < NCH; ++m) {
-    const int ci = tid + m * kThreads;
-    const int row = ci / CPR, col = (ci % CPR) * EPC;
-    *reinterpret_cast<uint4*>(sV + row * KS + col) = part(vraw, m);
-  }
-  lds_sync();
-  {
-    constexpr int NVB = V / 16;
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ch = 16 * (2 * kbp + cc) + xi;
 #pragma unroll
-    for (int vb = w; vb < NVB; vb += 4) {
-      typename Vec<T>::x8 BV[2];
+        for (int kb = 0; kb < 2; ++kb) {
+          floatx8 x;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        floatx8 x;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
-          x[t] = sB[j] * to_f32(sV[j * KS + 16 * vb + xi]);
+          for (int t = 0; t < 8; ++t) {
+            const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
+            x[t] = sB[j] * to_f32(sK[j * KS + ch]) * sKn[j] * exp2_fast(sG[j * GS + ch]);
+          }
+          cvt8(x, BKf[cc][kb]);
         }
-        cvt8(x, BV[kb]);
       }
+      // rt runs over compile-time values (a register array indexed by a runtime
+      // value becomes a compare/select chain); the wave-uniform guard picks the
+      // row tiles of this wave
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        floatx4 acc = zero4();
+        if ((rt - rt0) % RSTEP != 0) continue;
+        floatx4 acc0 = zero4(), acc1 = zero4();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          if (kb <= rt / 2) acc = mma32(acc, Af[rt][kb], BV[kb]);
-        typename Vec<T>::x4 y;
-        cvt4(acc, y);
-        *reinterpret_cast<typename Vec<T>::x4*>(reinterpret_cast<T*>(rec + a.off_u) +
-                                                ((size_t)(vb * 4 + rt) * 64 + lane) * 4) = y;
+        for (int kb = 0; kb < 2; ++kb) {
+          if (kb <= rt / 2) {
+            acc0 = mma32(acc0, BKf[0][kb], Af[rt][kb]);
+            acc1 = mma32(acc1, BKf[1][kb], Af[rt][kb]);
+          }
+        }
+        store_frag8<T>(rec + a.off_w, ((size_t)(rt * NKB + kbp) * 64 + lane) * 8, stackf(acc0, acc1));
       }
     }
+    lds_sync();  // G and k are dead: reuse sG for v
+
+    // ---------------- phase 5b/5c: U tiles = A (beta v), accumulator layout
+#pragma unroll
+    for (int m = 0; m < NCH; ++m)
+      *reinterpret_cast<u32x4*>(sV + (kv_row + m * kRowStep) * KS + kv_col) = R.v[m];
+    if constexpr (kPrefetch) issue_v(R, nx);
+    lds_sync();
+    {
+      constexpr int NVB = V / 16;
+#pragma unroll
+      for (int vb = w; vb < NVB; vb += 4) {
+        typename Vec<T>::x8 BV[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          floatx8 x;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) {
+            const int j = 32 * kb + (t < 4 ? 4 * gq + t : 16 + 4 * gq + t - 4);
+            x[t] = sB[j] * to_f32(sV[j * KS + 16 * vb + xi]);
+          }
+          cvt8(x, BV[kb]);
+        }
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          floatx4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            if (kb <= rt / 2) acc = mma32(acc, Af[rt][kb], BV[kb]);
+          typename Vec<T>::x4 y;
+          cvt4(acc, y);
+          *reinterpret_cast<typename Vec<T>::x4*>(reinterpret_cast<T*>(rec + a.off_u) +
+                                                  ((size_t)(vb * 4 + rt) * 64 + lane) * 4) = y;
+        }
+      }
+    }
+
+    lds_sync();  // LDS is reused by the next item
   }
 }
 
 }  // namespace
 
+template <typename T, int K, bool GF32>
+static hipError_t launch12(const Stage12Args& a, int nitems, hipStream_t s) {
+  static int occ = -1;  // resident workgroups per CU (same for every MI355X)
+  if (occ < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stage12_kernel<T, K, GF32>, kThreads, 0) != hipSuccess ||
+        n < 1)
+      n = 1;
+    occ = n;
+  }
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus < 1)
+    cus = 256;
+  const int grid = nitems < occ * cus ? nitems : occ * cus;
+  hipLaunchKernelGGL((stage12_kernel<T, K, GF32>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_stage12(const Stage12Args& a, int K, int bf16, int nblocks, hipStream_t s) {
   if (nblocks <= 0) return hipSuccess;
-  dim3 grid(nblocks), block(kThreads);
   if (bf16) {
-    if (K == 128) hipLaunchKernelGGL((stage12_kernel<kda::bf16, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage12_kernel<kda::bf16, 64>), grid, block, 0, s, a);
-  } else {
-    if (K == 128) hipLaunchKernelGGL((stage12_kernel<float, 128>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage12_kernel<float, 64>), grid, block, 0, s, a);
+    if (K == 128) return a.g_f32 ? launch12<kda::bf16, 128, true>(a, nblocks, s) : launch12<kda::bf16, 128, false>(a, nblocks, s);
+    return a.g_f32 ? launch12<kda::bf16, 64, true>(a, nblocks, s) : launch12<kda::bf16, 64, false>(a, nblocks, s);
   }
-  return hipGetLastError();
+  if (K == 128) return a.g_f32 ? launch12<float, 128, true>(a, nblocks, s) : launch12<float, 128, false>(a, nblocks, s);
+  return a.g_f32 ? launch12<float, 64, true>(a, nblocks, s) : launch12<float, 64, false>(a, nblocks, s);
 }
 
 }  // namespace kda

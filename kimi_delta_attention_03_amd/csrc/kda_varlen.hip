@@ -6,6 +6,7 @@
 //   chunk table [slot]  = (first token, valid length), length 0 for unused slots
 //   sequence table [n]  = (first chunk slot, chunk count)
 //   order [rank]        = sequence ids, longest first (ties by id)
+//   header word 0       = number of chunk slots in use
 // cu_seqlens is read defensively: each boundary is clamped into [0, T] and
 // made non-decreasing, so malformed input cannot address memory outside the
 // inputs or the workspace.
@@ -93,6 +94,8 @@ __global__ __launch_bounds__(kMapThreads) void varlen_map_kernel(const int32_t* 
     __syncthreads();
   }
   for (size_t slot = (size_t)chunk_carry + t; slot < ncp; slot += kMapThreads) ctab[slot] = make_int2(0, 0);
+  // header word 0: chunk slots in use (<= ncp by construction; clamped for safety)
+  if (t == 0) reinterpret_cast<int*>(ws)[0] = min(chunk_carry, (int)ncp);
   if (nseq <= kSortMax) {
     __syncthreads();
     for (int n = t; n < nseq; n += kMapThreads) {
