@@ -188,17 +188,19 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
         const int cc = c < last ? c : last;
         load_state<T, K>(f, rs, cc * (int)a.rec_bytes, a, s, lane_off, 16 * gq);
       };
+      // the prologue loads stay in chunk order (no scheduling across the barriers):
+      // the memory-counter wait at the top of each ring pass is computed from
+      // the worst case over the loop entry and the back edge
 #pragma unroll
-      for (int i = 0; i < NB - 1; ++i) issue(F[i], i);
+      for (int i = 0; i < NB - 1; ++i) {
+        issue(F[i], i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       lds_sync();  // initial state published
-      for (int c0 = 0; c0 < nch; c0 += NB) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-          const int c = c0 + j;
-          if (c >= nch) break;
-          issue(F[(j + NB - 1) % NB], c + NB - 1);
-          StateFrags<T, K>& f = F[j];
-          lds_sync();  // V_new of chunk c published
+      auto step = [&](StateFrags<T, K>& f, StateFrags<T, K>& next, int c) {
+        issue(next, c + NB - 1);
+        if (c < nch) {  // uniform: both roles skip the same steps, barriers included
+          lds_sync();   // V_new of chunk c published
           const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
           const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
 #pragma unroll
@@ -212,6 +214,14 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
           }
           lds_sync();  // state after chunk c published
         }
+      };
+      // whole ring passes with a single exit: steps past the last chunk only
+      // issue their (clamped) loads. An exit inside a pass, or a separate tail,
+      // would make the memory-counter waits at the top of a pass cover the ring.
+      const int npass = (nch + NB - 1) / NB;
+      for (int p = 0; p < npass; ++p) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
       }
     }
     if (a.final_state) {
@@ -233,24 +243,28 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
       const int cc = c < last ? c : last;
       load_row<T, K>(f, rs, cc * (int)a.rec_bytes, ctab + p0 + cc, a, r0, lane_off, vb);
     };
+    // prologue loads in chunk order (see the state waves)
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i) issue(F[i], i);
+    for (int i = 0; i < NB - 1; ++i) {
+      issue(F[i], i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     lds_sync();  // initial state published
-    for (int c0 = 0; c0 < nch; c0 += NB) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) {
-        const int c = c0 + j;
-        if (c >= nch) break;
-        issue(F[(j + NB - 1) % NB], c + NB - 1);
-        RowFrags<T, K>& f = F[j];
-        const int64_t tok0 = a.varlen ? (int64_t)f.ct.x : (int64_t)(p0 + c) * C;
-        const int len = a.varlen ? f.ct.y : C;
-        floatx4 accV = zero4(), accO = zero4();
+    auto step = [&](RowFrags<T, K>& f, RowFrags<T, K>& next, int c) {
+      issue(next, c + NB - 1);
+      const int64_t tok0 = a.varlen ? (int64_t)f.ct.x : (int64_t)(p0 + c) * C;
+      const int len = c < nch ? (a.varlen ? f.ct.y : C) : 0;
+      // accO is built transposed (operands swapped): lane (g, i) then holds chunk
+      // row 16 r0 + i at the four consecutive columns 16 vb + 4 g .. + 3, which
+      // leaves as one vector store per lane
+      floatx4 accO = zero4();
+      if (c < nch) {  // uniform, as in the state waves
+        floatx4 accV = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
           const F8 Sb = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
           accV = mma32(accV, f.w[kb], Sb);
-          accO = mma32(accO, f.qg[kb], Sb);
+          accO = mma32(accO, Sb, f.qg[kb]);
         }
         const floatx4 vn = widen4(f.u) - accV;
         F4 vnT;
@@ -260,20 +274,23 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
         const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
         const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
         // intra-chunk part, causal: row block r0 reads V_new blocks <= r0
-        accO = mma32(accO, f.aq[0], Vb0);
-        if (r0 >= 2) accO = mma32(accO, f.aq[1], Vb1);
-        // rows past the end of a short chunk store into the sink: no branch
-        // around the stores keeps the memory-counter waits identical on all paths
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int row = 16 * r0 + 4 * gq + rr;
-          T y;
-          if constexpr (sizeof(T) == 2) y = (T)accO[rr]; else y = accO[rr];
-          T* dst = row < len ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + xi : sink;
-          *dst = y;
-        }
+        accO = mma32(accO, Vb0, f.aq[0]);
+        if (r0 >= 2) accO = mma32(accO, Vb1, f.aq[1]);
         lds_sync();  // state after chunk c published
       }
+      // rows past the end of a short chunk, and every row of a step past the
+      // last chunk, store into the sink: the store is never under a branch
+      const int row = 16 * r0 + xi;
+      F4 y;
+      cvt4(accO, y);
+      T* dst = row < len ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
+      *reinterpret_cast<F4*>(dst) = y;
+    };
+    // whole ring passes with a single exit (see the state waves)
+    const int npass = (nch + NB - 1) / NB;
+    for (int p = 0; p < npass; ++p) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
     }
   }
 }
