@@ -14,8 +14,8 @@ Prints ONE JSON line. Throughput `value` is tokens/s (B*T per step).
 Rooflines use MI355X's published peaks (HBM3E 8 TB/s, dense bf16 MFMA
 2.5 PFLOP/s) and the algorithmic traffic of each kernel:
   stage 1+2: reads q,k,v,g (4 x 256 B) + beta (2 B), writes its workspace
-             record (1160 B)                     -> 2186 B per token-head
-  stage 3+4: reads the record (1160 B), writes o (256 B) -> 1416 B per token-head
+             record (1128 B)                     -> 2154 B per token-head
+  stage 3+4: reads the record (1128 B), writes o (256 B) -> 1384 B per token-head
   algorithmic FLOPs: 6CKV + C(C+1)(3K+2V) + C^3/3 per chunk-head (C = 64).
 The CPU baseline times the float64 oracle on a bounded sample of the same
 workload on this host.
@@ -46,7 +46,7 @@ def alg_flops_per_chunk_head(C, K, V):
 
 def alg_bytes_per_token_head(K, V, elem, gelem, belem):
     s12 = (2 * K) * elem + V * elem + K * gelem + belem          # q, k, v, g, beta
-    rec = (3 * K + 64 + V) * elem + 4 * K / 64                  # W, qg, kg, Aqk, U, gamma
+    rec = (3 * K + 48 + V) * elem + 4 * K / 64                  # W, qg, kg, Aqk (6 of 8 blocks), U, gamma
     s34 = rec + V * elem                                          # record in, o out
     return s12 + rec, s34
 

@@ -111,11 +111,12 @@ kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_s
 
 /* Where stage 1+2 puts its outputs inside the workspace (for inspection).
  * All offsets are in bytes. For head h and physical chunk p the record starts
- * at records_offset + (h * chunk_slots + p) * record_bytes and holds, in the
- * stored element type (bf16 for bf16 q/k/v, else fp32):
- *   W, QG (qg), KG (kg^T), AQ (Aqk) as 16-row x 32-wide MFMA fragments and U
- *   in accumulator-tile order, then gamma (fp32, K values). The fragment
- *   orders are documented in kimi_delta_attention_03_amd/csrc/kda_layout.h. */
+ * at records_offset + (p * H + h) * record_bytes (chunk-major) and holds, in
+ * the stored element type (bf16 for bf16 q/k/v, else fp32):
+ *   W, QG (qg), KG (kg^T), AQ (Aqk, the 6 causally non-zero fragments) as
+ *   16-row x 32-wide MFMA fragments and U in accumulator-tile order, then
+ *   gamma (fp32, K values). The fragment orders are documented in
+ *   kimi_delta_attention_03_amd/csrc/kda_layout.h. */
 typedef struct {
   size_t total_bytes, records_offset, record_bytes, chunk_slots;
   size_t off_w, off_qg, off_kg, off_aq, off_u, off_gamma;

@@ -2,7 +2,11 @@
 // and the gfx950 kernels.
 //
 // The stage-1+2 kernel writes, for every (head h, physical chunk p), one
-// fixed-size record that the stage-3+4 kernel streams in chunk order. The
+// fixed-size record that the stage-3+4 kernel streams in chunk order.
+// Records are stored chunk-major, record (p, h) at index p * H + h: the
+// stage-3+4 workgroups of all heads walk the chunks in step, so at any time
+// they read one contiguous region, spread over all HBM channels (a head-major
+// order puts the heads a large power-of-two stride apart). The
 // record holds the chunk's operands already arranged as MFMA fragments so
 // that stage 3+4 loads each fragment with one coalesced 16-byte (bf16) or
 // 32-byte (fp32) access per lane:
@@ -10,7 +14,10 @@
 //   W   [rt 0..3][kb 0..K/32-1][lane 0..63][8]   W = A (D_beta K+), rows = chunk position
 //   QG  [rt 0..3][kb 0..K/32-1][lane][8]         qg = scale * q * 2^G
 //   KG  [rt 0..K/16-1][kb 0..1][lane][8]         kg^T, rows = key channel, k = chunk position
-//   AQ  [rt 0..3][kb 0..1][lane][8]              Aqk (scale folded in, causal mask applied)
+//   AQ  [6][lane][8]                              Aqk (scale folded in, causal mask applied):
+//                                                 fragment (rt, kb) for kb <= rt / 2 at index
+//                                                 aq_frag(rt, kb); (0, 1) and (1, 1) are all
+//                                                 zero and not stored
 //   U   [vb 0..V/16-1][rt 0..3][lane][4]         U = A (D_beta V) in accumulator layout
 //   GAM [K] float                                 gamma = 2^{G_last} (chunk-end decay)
 //
@@ -34,6 +41,10 @@
 namespace kda {
 
 constexpr int kChunk = 64;      // chunk size C of the GPU path
+constexpr int kAqFrags = 6;     // stored Aqk fragments per record
+
+// index of Aqk fragment (row tile rt, 32-wide block kb), kb <= rt / 2
+__host__ __device__ constexpr int aq_frag(int rt, int kb) { return rt < 2 ? rt : 2 * rt - 2 + kb; }
 constexpr int kThreads = 256;   // 4 waves of 64 lanes per workgroup
 
 struct Layout {
@@ -64,7 +75,7 @@ static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, i
   L.off_qg = L.off_w + C * K * e;
   L.off_kg = L.off_qg + C * K * e;
   L.off_aq = L.off_kg + C * K * e;
-  L.off_u = L.off_aq + C * C * e;
+  L.off_u = L.off_aq + (size_t)kAqFrags * 512 * e;
   L.off_gam = L.off_u + C * V * e;
   L.rec_bytes = round_up(L.off_gam + (size_t)K * 4, 256);
   if (nseq > 0) {

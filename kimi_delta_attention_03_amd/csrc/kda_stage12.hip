@@ -231,7 +231,7 @@ void stage12_kernel(Stage12Args a) {
       issue_v(R, it);
     }
     const int p = it.p, h = it.h;
-    char* rec = a.ws + a.meta_bytes + ((size_t)h * a.ncp + p) * a.rec_bytes;
+    char* rec = a.ws + a.meta_bytes + ((size_t)p * H + h) * a.rec_bytes;  // chunk-major
 
     // ---------------- phase 1: beta, k -> LDS, k norms, gate cumsum
     if (tid < C) {
@@ -376,9 +376,9 @@ void stage12_kernel(Stage12Args a) {
       if (w == 0 || w == 2)  // blocks (0,1) and (2,3) are read as zeros later
         *reinterpret_cast<floatx4*>(sA + irow * AS + 16 * (w + 1) + 4 * gq) = zero4();
       // Aqk fragments of query block w: kb' = 0 from tiles (0, 1), kb' = 1 from (2, 3)
-      store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 0) * 64 + lane) * 8, stackf(aq[0], aq[1]));
+      store_frag8<T>(rec + a.off_aq, ((size_t)aq_frag(w, 0) * 64 + lane) * 8, stackf(aq[0], aq[1]));
       if (w >= 2)
-        store_frag8<T>(rec + a.off_aq, ((size_t)(w * 2 + 1) * 64 + lane) * 8, stackf(aq[2], aq[3]));
+        store_frag8<T>(rec + a.off_aq, ((size_t)aq_frag(w, 1) * 64 + lane) * 8, stackf(aq[2], aq[3]));
     }
 
     // ---------------- phase 3: gated keys kg^T and gamma (only G, k needed)

@@ -43,7 +43,6 @@ struct RowFrags {
   typename Vec<T>::x8 qg[NKB];  // qg rows of this wave's block
   typename Vec<T>::x8 aq[2];    // Aqk rows of this wave's block
   typename Vec<T>::x4 u;        // U, accumulator layout
-  int2 ct;                      // (first token, valid length) of the chunk
 };
 
 // operands of one chunk for a state wave
@@ -51,12 +50,11 @@ template <typename T, int K>
 struct StateFrags {
   static constexpr int TPW = K / 64;
   typename Vec<T>::x8 kg[TPW][2];  // kg^T rows of this wave's state tiles
-  floatx4 gam[TPW];                // gamma for this lane's state rows
+  float gam;                       // gamma of channel 16 TPW s + lane % (16 TPW)
 };
 
-// Fragment loads go through a buffer resource covering this (sequence, head)'s
-// records: one uniform descriptor, the chunk offset in a scalar register and a
-// single per-lane offset register shared by every load. With 64-bit per-lane
+// Fragment loads go through a buffer resource covering one record: a uniform
+// descriptor and a single per-lane offset register shared by every load. With 64-bit per-lane
 // addresses instead, the register allocator reuses address registers that are
 // still the destination of in-flight loads and the prefetch ring stalls.
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -78,9 +76,11 @@ __device__ __forceinline__ void bload4(floatx4& d, __amdgpu_buffer_rsrc_t r, int
 }
 
 // lane_off = 16 * lane; frag8 fragments are 64 * 8 elements, accumulator-layout
-// fragments 64 * 4 elements
+// fragments 64 * 4 elements. Every lane-byte loaded here passes the CU's
+// vector-memory path, whose rate bounds a chunk step, so nothing is loaded
+// twice: gamma comes as one float per lane and is spread by lane shuffles.
 template <typename T, int K>
-__device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff, const int2* ct,
+__device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff,
                                          const Stage34Args& a, int r, int lane_off, int vb) {
   constexpr int NKB = K / 32;
   constexpr int F8B = 512 * (int)sizeof(T);  // bytes of one frag8 fragment
@@ -90,12 +90,13 @@ __device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc
     bload(f.w[kb], rs, lane_off, soff + (int)a.off_w + (r * NKB + kb) * F8B);
     bload(f.qg[kb], rs, lane_off, soff + (int)a.off_qg + (r * NKB + kb) * F8B);
   }
-  // both Aqk halves are loaded for every wave (the second is unused for rows < 32):
-  // no branch around a load keeps the compiler's memory-counter waits exact
-  bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + (r * 2 + 0) * F8B);
-  bload(f.aq[1], rs, lane_off, soff + (int)a.off_aq + (r * 2 + 1) * F8B);
+  // every wave issues both Aqk loads (no branch around a load keeps the
+  // compiler's memory-counter waits exact); rows < 32 have no second block and
+  // point that load past the end of the record, where it reads zeros without
+  // touching memory
+  bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + aq_frag(r, 0) * F8B);
+  bload(f.aq[1], rs, lane_off, r >= 2 ? soff + (int)a.off_aq + aq_frag(r, 1) * F8B : (int)a.rec_bytes);
   bload4(f.u, rs, lane_off, soff + (int)a.off_u + (vb * 4 + r) * F4B);
-  f.ct = *ct;  // read in both modes (the table exists in every workspace); used for varlen only
 }
 
 template <typename T, int K>
@@ -108,9 +109,9 @@ __device__ __forceinline__ void load_state(StateFrags<T, K>& f, __amdgpu_buffer_
     const int rt = s * TPW + m;
     bload(f.kg[m][0], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 0) * F8B);
     bload(f.kg[m][1], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 1) * F8B);
-    f.gam[m] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rs, gam_off, soff + (int)a.off_gam + 64 * rt, 0));
   }
+  f.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                        rs, gam_off, soff + (int)a.off_gam + 64 * TPW * s, 0));
 }
 
 template <typename T, int K, int NB>
@@ -146,24 +147,33 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   int seq = u / H;
   const int h = u - seq * H;
 
+  // chunk c of this sequence starts at token tfirst + 64 c; every chunk but the
+  // last is full, the last holds lastlen tokens
   size_t p0;
   int nch;
-  const int2* ctab = reinterpret_cast<const int2*>(a.ws + a.off_chunk_tab);
+  int64_t tfirst;
+  int lastlen = kChunk;
   if (a.varlen) {
+    const int2* ctab = reinterpret_cast<const int2*>(a.ws + a.off_chunk_tab);
     seq = reinterpret_cast<const int*>(a.ws + a.off_order)[seq];
     const int2 st = reinterpret_cast<const int2*>(a.ws + a.off_seq_tab)[seq];
     p0 = (size_t)st.x;
     nch = st.y;
+    tfirst = nch > 0 ? (int64_t)ctab[p0].x : 0;
+    if (nch > 0) lastlen = ctab[p0 + nch - 1].y;
   } else {
     p0 = (size_t)seq * a.nt;
     nch = a.nt;
+    tfirst = (int64_t)p0 * kChunk;
   }
-  const char* rec0 = a.ws + a.meta_bytes + ((size_t)h * a.ncp + p0) * a.rec_bytes;
-  const size_t state_base = ((size_t)seq * H + h) * K * V + 16 * vb + xi;
   const int last = nch - 1;
-  // buffer resource over this (sequence, head)'s records (offsets stay < 2^31)
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(rec0), (short)0, 0x7ffffff0, 0x00020000);
+  const size_t state_base = ((size_t)seq * H + h) * K * V + 16 * vb + xi;
+  // buffer resource over exactly one record (chunk cc of this sequence, head h;
+  // records are chunk-major): offsets past the record read zeros
+  auto rec_rsrc = [&](int cc) {
+    const char* base = a.ws + a.meta_bytes + (((size_t)p0 + cc) * H + h) * a.rec_bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)a.rec_bytes, 0x00020000);
+  };
   const int lane_off = 16 * lane;
 
   if (w >= 4) {
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
       // no branch around the loads the memory-counter waits stay exact
       auto issue = [&](StateFrags<T, K>& f, int c) {
         const int cc = c < last ? c : last;
-        load_state<T, K>(f, rs, cc * (int)a.rec_bytes, a, s, lane_off, 16 * gq);
+        load_state<T, K>(f, rec_rsrc(cc), 0, a, s, lane_off, 4 * (lane % (16 * TPW)));
       };
       // the prologue loads stay in chunk order (no scheduling across the barriers):
       // the memory-counter wait at the top of each ring pass is computed from
@@ -205,7 +215,10 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
           const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
 #pragma unroll
           for (int m = 0; m < TPW; ++m) {
-            S[m] = S[m] * f.gam[m];
+            floatx4 gm;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gm[r] = __shfl(f.gam, 16 * m + 4 * gq + r, 64);
+            S[m] = S[m] * gm;
             S[m] = mma32(S[m], f.kg[m][0], Vb0);
             S[m] = mma32(S[m], f.kg[m][1], Vb1);
             F4 y;
@@ -241,7 +254,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
     RowFrags<T, K> F[NB];
     auto issue = [&](RowFrags<T, K>& f, int c) {
       const int cc = c < last ? c : last;
-      load_row<T, K>(f, rs, cc * (int)a.rec_bytes, ctab + p0 + cc, a, r0, lane_off, vb);
+      load_row<T, K>(f, rec_rsrc(cc), 0, a, r0, lane_off, vb);
     };
     // prologue loads in chunk order (see the state waves)
 #pragma unroll
@@ -251,26 +264,33 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
     }
     lds_sync();  // initial state published
     auto step = [&](RowFrags<T, K>& f, RowFrags<T, K>& next, int c) {
-      issue(next, c + NB - 1);
-      const int64_t tok0 = a.varlen ? (int64_t)f.ct.x : (int64_t)(p0 + c) * C;
-      const int len = c < nch ? (a.varlen ? f.ct.y : C) : 0;
-      // accO is built transposed (operands swapped): lane (g, i) then holds chunk
-      // row 16 r0 + i at the four consecutive columns 16 vb + 4 g .. + 3, which
-      // leaves as one vector store per lane
-      floatx4 accO = zero4();
+      const int64_t tok0 = tfirst + (int64_t)c * C;
+      const int len = c < nch - 1 ? C : (c == nch - 1 ? lastlen : 0);
+      // critical part first: V_new = U - W S feeds the state waves
+      F8 Sb[NKB];
       if (c < nch) {  // uniform, as in the state waves
         floatx4 accV = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const F8 Sb = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
-          accV = mma32(accV, f.w[kb], Sb);
-          accO = mma32(accO, Sb, f.qg[kb]);
+          Sb[kb] = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
+          accV = mma32(accV, f.w[kb], Sb[kb]);
         }
         const floatx4 vn = widen4(f.u) - accV;
         F4 vnT;
         cvt4(vn, vnT);
         sVn[r0][lane] = vnT;
         lds_sync();  // V_new of chunk c published
+      }
+      // the next loads are issued while the state waves apply the update; a
+      // full vector-memory queue then stalls this wave, not the chain
+      issue(next, c + NB - 1);
+      // accO is built transposed (operands swapped): lane (g, i) then holds chunk
+      // row 16 r0 + i at the four consecutive columns 16 vb + 4 g .. + 3, which
+      // leaves as one vector store per lane
+      floatx4 accO = zero4();
+      if (c < nch) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) accO = mma32(accO, Sb[kb], f.qg[kb]);
         const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
         const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
         // intra-chunk part, causal: row block r0 reads V_new blocks <= r0

@@ -75,10 +75,23 @@ def decode_acc(arr, n_vb, n_rt=4):
     return out
 
 
-def decode_record(ws_bytes, info, h, p, K, V, bf16):
-    """Decode the stage-1+2 record of (head h, chunk slot p) into dense matrices."""
+def decode_aq(arr):
+    """The 6 stored Aqk fragments -> dense [64, 64]; fragment (rt, kb) sits at
+    index rt for rt < 2 (kb = 0 only) and 2 rt - 2 + kb otherwise."""
+    a = np.asarray(arr, np.float64).reshape(6, 64, 8)
+    out = np.zeros((64, 64))
+    for rt in range(4):
+        for kb in range(2 if rt >= 2 else 1):
+            idx = rt if rt < 2 else 2 * rt - 2 + kb
+            out[16 * rt + _FR, 32 * kb + _FC] = a[idx]
+    return out
+
+
+def decode_record(ws_bytes, info, h, p, K, V, bf16, H):
+    """Decode the stage-1+2 record of (head h, chunk slot p) into dense matrices
+    (records are chunk-major: index p * H + h)."""
     import torch
-    base = info.records_offset + (h * info.chunk_slots + p) * info.record_bytes
+    base = info.records_offset + (p * H + h) * info.record_bytes
     rec = ws_bytes[base:base + info.record_bytes]
 
     def elems(off, n):
@@ -93,7 +106,7 @@ def decode_record(ws_bytes, info, h, p, K, V, bf16):
         "W": decode_frag8(elems(info.off_w, C * K), 4, K // 32),
         "qg": decode_frag8(elems(info.off_qg, C * K), 4, K // 32),
         "kgT": decode_frag8(elems(info.off_kg, C * K), K // 16, 2),
-        "Aqk": decode_frag8(elems(info.off_aq, C * C), 4, 2),
+        "Aqk": decode_aq(elems(info.off_aq, 6 * 512)),
         "U": decode_acc(elems(info.off_u, C * V), V // 16),
         "gamma": rec[info.off_gamma:info.off_gamma + 4 * K].copy().view(np.float32).astype(np.float64),
     }

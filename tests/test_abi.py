@@ -53,12 +53,13 @@ def ws_bytes(lib, p):
 
 
 def test_workspace_size_formula(lib):
-    # record = (3 C K + C^2 + C V) elements + 4 K bytes, rounded to 256; C = 64
+    # record = (3 C K + 6 * 512 + C V) elements + 4 K bytes, rounded to 256; C = 64
+    # (6 stored Aqk fragments of 16 x 32)
     for (K, dt, elem) in ((128, 1, 2), (128, 0, 4), (64, 1, 2), (64, 0, 4)):
         p = P(K=K, V=K, qkv_dtype=dt, g_dtype=dt, beta_dtype=dt, B=3, T=256, H=5)
         st, n = ws_bytes(lib, p)
         assert st == 0
-        rec = (3 * 64 * K + 64 * 64 + 64 * K) * elem + 4 * K
+        rec = (3 * 64 * K + 6 * 512 + 64 * K) * elem + 4 * K
         rec = (rec + 255) // 256 * 256
         info = _lib.KdaWorkspaceInfo()
         assert lib.kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
@@ -71,8 +72,8 @@ def test_workspace_size_formula(lib):
     st, n = ws_bytes(lib, p)
     info = _lib.KdaWorkspaceInfo()
     assert lib.kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
-    assert info.chunk_slots == 16 + 7 and info.record_bytes == 74240
-    assert n == info.total_bytes == info.records_offset + 74240 * 23 * 2
+    assert info.chunk_slots == 16 + 7 and info.record_bytes == 72192
+    assert n == info.total_bytes == info.records_offset + 72192 * 23 * 2
 
 
 @pytest.mark.parametrize("kw,status", [

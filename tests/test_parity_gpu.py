@@ -135,7 +135,7 @@ def test_stage12_intermediates_match_oracle():
         for (_, c0, t) in terms:
             p = c0 // 64
             for h in range(2):
-                r = decode_record(ws, info, h, p, K, K, dtype == "bf16")
+                r = decode_record(ws, info, h, p, K, K, dtype == "bf16", 2)
                 errs = {
                     "W": rel_err(r["W"], t["W"][h]), "U": rel_err(r["U"], t["U"][h]),
                     "qg": rel_err(r["qg"], t["qg"][h]), "kg": rel_err(r["kgT"].T, t["kg"][h]),
