@@ -19,7 +19,8 @@ import ctypes
 from . import _lib
 from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
-__all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout"]
+__all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
+           "KdaLayer", "layer_fwd"]
 
 
 def _torch():
@@ -145,3 +146,69 @@ def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, c
     """Chunkwise KDA forward on the GPU. Returns (o, final_state or None)."""
     return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
                       output_final_state, use_qk_l2norm, l2norm_eps)()
+
+
+# bf16 projection weights and fp32 small parameters of the layer (include/kda_layer.h)
+_LAYER_BF16 = ("Wqkv", "Wb", "Wad", "Wau", "Wgd", "Wgu", "Wo")
+_LAYER_F32 = ("conv_q", "conv_k", "conv_v", "A_log", "dt_bias", "norm_w")
+
+
+class KdaLayer:
+    """A bound KDA layer forward (include/kda_layer.h): checked weights,
+    preallocated output and workspace. Calling it with x (bf16 [B, T, M] on the
+    GPU) runs the whole layer on the current stream and returns x_new (bf16)."""
+
+    def __init__(self, weights, B, T, H, D, gate_lower_bound=-5.0, norm_eps=1e-6, l2_eps=1e-6,
+                 keep_core_output=False):
+        torch = _torch()
+        lib = _lib.load()
+        for n in _lib.LAYER_WEIGHT_NAMES:
+            if n not in weights:
+                raise KdaValueError(1, f"missing layer weight {n}")
+            t = weights[n]
+            want = torch.bfloat16 if n in _LAYER_BF16 else torch.float32
+            if not t.is_cuda or t.dtype != want or not t.is_contiguous():
+                raise KdaValueError(1, f"layer weight {n} must be a contiguous {want} GPU tensor")
+        M = weights["Wqkv"].shape[1]
+        p = _lib.KdaLayerParams()
+        p.B, p.T, p.M, p.H, p.D = int(B), int(T), int(M), int(H), int(D)
+        p.gate_rank = int(weights["Wad"].shape[0])
+        p.out_gate_rank = int(weights["Wgd"].shape[0])
+        p.conv_size = int(weights["conv_q"].shape[1])
+        p.gate_lower_bound, p.norm_eps, p.l2_eps = float(gate_lower_bound), float(norm_eps), float(l2_eps)
+        HD = H * D
+        shapes = {"Wqkv": (3 * HD, M), "conv_q": (HD, p.conv_size), "conv_k": (HD, p.conv_size),
+                  "conv_v": (HD, p.conv_size), "Wb": (H, M), "Wad": (p.gate_rank, M), "Wau": (HD, p.gate_rank),
+                  "A_log": (H,), "dt_bias": (HD,), "Wgd": (p.out_gate_rank, M), "Wgu": (HD, p.out_gate_rank),
+                  "norm_w": (D,), "Wo": (M, HD)}
+        for n, shp in shapes.items():
+            if tuple(weights[n].shape) != shp:
+                raise KdaValueError(1, f"layer weight {n} must have shape {shp}, got {tuple(weights[n].shape)}")
+        self.params = p
+        nbytes = ctypes.c_size_t(0)
+        _lib.check(lib.kda_layer_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(nbytes)))
+        dev = weights["Wqkv"].device
+        self.workspace = torch.empty(nbytes.value, dtype=torch.uint8, device=dev)
+        self.x_new = torch.empty((B, T, M), dtype=torch.bfloat16, device=dev)
+        self.core_out = (torch.empty((B, T, H, D), dtype=torch.float32, device=dev) if keep_core_output else None)
+        self.weights = dict(weights)
+        self.cw = _lib.KdaLayerWeights(*[t.data_ptr() for t in (weights[n] for n in _lib.LAYER_WEIGHT_NAMES)])
+        self._lib = lib
+
+    def __call__(self, x):
+        torch = _torch()
+        p = self.params
+        if (not x.is_cuda or x.dtype != torch.bfloat16 or not x.is_contiguous()
+                or tuple(x.shape) != (p.B, p.T, p.M)):
+            raise KdaValueError(1, f"x must be a contiguous bf16 GPU tensor of shape {(p.B, p.T, p.M)}")
+        _lib.check(self._lib.kda_layer_fwd(
+            ctypes.byref(p), ctypes.byref(self.cw), _ptr(x), _ptr(self.x_new), _ptr(self.core_out),
+            _ptr(self.workspace), self.workspace.numel(),
+            ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+        return self.x_new
+
+
+def layer_fwd(x, weights, H, D, **kw):
+    """KDA layer forward on the GPU: x bf16 [B, T, M] -> x_new bf16 [B, T, M]."""
+    B, T, _ = x.shape
+    return KdaLayer(weights, B, T, H, D, **kw)(x)

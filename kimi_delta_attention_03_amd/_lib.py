@@ -1,4 +1,4 @@
-"""ctypes view of the C ABI in include/kda.h (no computation here).
+"""ctypes view of the C ABI in include/kda.h and include/kda_layer.h (no computation here).
 
 The shared library is built in-tree by kimi_delta_attention_03_amd.build. If
 it is missing, loading raises: there is no fallback path.
@@ -44,7 +44,25 @@ class KdaWorkspaceInfo(ctypes.Structure):
     ]
 
 
+class KdaLayerParams(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int64), ("T", ctypes.c_int64),
+        ("M", ctypes.c_int32), ("H", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("gate_rank", ctypes.c_int32), ("out_gate_rank", ctypes.c_int32), ("conv_size", ctypes.c_int32),
+        ("gate_lower_bound", ctypes.c_float), ("norm_eps", ctypes.c_float), ("l2_eps", ctypes.c_float),
+    ]
+
+
+LAYER_WEIGHT_NAMES = ["Wqkv", "conv_q", "conv_k", "conv_v", "Wb", "Wad", "Wau", "A_log", "dt_bias",
+                      "Wgd", "Wgu", "norm_w", "Wo"]
+
+
+class KdaLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_WEIGHT_NAMES]
+
+
 _P = ctypes.POINTER(KdaFwdParams)
+_LP = ctypes.POINTER(KdaLayerParams)
 SIGNATURES = {
     "kda_chunk_fwd_workspace_bytes": (ctypes.c_int, [_P, ctypes.POINTER(ctypes.c_size_t)]),
     "kda_chunk_fwd": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
@@ -54,6 +72,8 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_abi_version": (ctypes.c_int32, []),
+    "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
+    "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 
 _lib = None

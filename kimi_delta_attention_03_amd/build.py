@@ -21,7 +21,9 @@ BUILD = os.path.join(HERE, "_build")
 LIB_NAME = "libkda_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["kda_api.cpp", "kda_stage12.hip", "kda_stage34.hip", "kda_varlen.hip"]
+SOURCES = ["kda_api.cpp", "kda_stage12.hip", "kda_stage34.hip", "kda_varlen.hip", "kda_layer.hip"]
+# the layer's plain projections run on rocBLAS
+LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 
 ARCH = "gfx950"
 FLAGS = [
@@ -60,7 +62,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(jobs) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, *LIBS, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

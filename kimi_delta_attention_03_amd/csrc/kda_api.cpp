@@ -143,6 +143,17 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
 
 }  // namespace
 
+namespace kda {
+kda_status fail_msg(kda_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+void clear_msg() { g_msg[0] = 0; }
+}  // namespace kda
+
 extern "C" {
 
 kda_status kda_chunk_fwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes) {

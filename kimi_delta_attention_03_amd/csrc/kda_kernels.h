@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda.h"
 #include "kda_layout.h"
 
 namespace kda {
@@ -47,5 +48,9 @@ hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s);
 hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, size_t ncp,
                              size_t off_chunk_tab, size_t off_seq_tab, size_t off_order,
                              hipStream_t s);
+
+// sets the thread-local message returned by kda_last_error and returns s
+kda_status fail_msg(kda_status s, const char* fmt, ...);
+void clear_msg();
 
 }  // namespace kda

@@ -1,0 +1,408 @@
+// KDA layer forward around the chunkwise core on gfx950 ("KDAChunkwise" docs,
+// sections "From the hidden states to causal Q, K, and V", "FP32 core and
+// log-space decay", "Returning to the model dimension"; lower-bound sigmoid
+// gate of the Tokamax "chunk_kda_fwd design doc", section 9.1.3).
+//
+// Order of work on the caller's stream (BT = B * T tokens, HD = H * D):
+//   1. Wcat = [Wqkv; Wb; Wad; Wgd] (device copies, rows of width M)
+//   2. P    = x Wcat^T                     rocBLAS, bf16 x bf16 -> fp32 [BT, NP]
+//   3. prologue kernel: q, k, v = SiLU(conv4(P_qkv)) (+ L2 norm for q, k),
+//      beta = sigmoid(P_b); the two low-rank slices of P rounded to bf16 (R)
+//   4. g    = R_a Wau^T                    rocBLAS -> fp32 [BT, HD]
+//   5. gate kernel: g <- lb * sigmoid(exp(A_log_h) (g + dt_bias)), in place
+//   6. core: the two-kernel chunkwise forward on fp32 q, k, v, g, beta
+//   7. Gu   = R_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in P's space)
+//   8. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in q's space)
+//   9. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
+// The plain projections are library GEMMs; every other step is a kernel of
+// this file or of the core. The elementwise kernels are HBM-bound: each reads
+// its inputs once with coalesced vector loads and writes its outputs once.
+#include <hip/hip_runtime.h>
+#include <rocblas/rocblas.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <mutex>
+
+#include "kda.h"
+#include "kda_layer.h"
+#include "kda_kernels.h"
+
+namespace kda {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kLayerThreads = 256;
+constexpr int kTile = 64;  // tokens per prologue wave
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+struct PrologueArgs {
+  const float* P;      // [BT, ldp]
+  int64_t ldp;
+  const float* conv[3];
+  float* out[3];       // q, k, v [BT, HD]
+  float* beta;         // [BT, H]
+  uint16_t* R;         // [BT, nr] bf16 bits: the low-rank slices
+  int64_t T;           // tokens per batch row
+  int H, nt;           // heads, 64-token tiles per row
+  int off_b, off_r, nr;
+  float l2eps;
+  int64_t nwaves;      // B * nt * H * 3
+};
+
+// One wave per (batch row, 64-token tile, head, stream q/k/v): a sliding
+// window of the last 3 pre-activations per channel in registers, so P is read
+// once. Lane l holds channels CPL l .. CPL l + CPL - 1 of the head.
+template <int D>
+__global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueArgs a) {
+  constexpr int CPL = D / kWave;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * (kLayerThreads / kWave) + (threadIdx.x >> 6);
+  if (wid >= a.nwaves) return;
+  const int s = (int)(wid % 3);
+  int64_t r = wid / 3;
+  const int h = (int)(r % a.H);
+  r /= a.H;
+  const int tile = (int)(r % a.nt);
+  const int64_t b = r / a.nt;
+  const int HD = a.H * D;
+  const int c0 = h * D + CPL * lane;
+  const int64_t row0 = b * a.T + (int64_t)tile * kTile;  // first token row of the tile
+  const float* src = a.P + s * HD + c0;
+  float wgt[CPL][4];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const float4 w4 = *reinterpret_cast<const float4*>(a.conv[s] + (size_t)(c0 + j) * 4);
+    wgt[j][0] = w4.x; wgt[j][1] = w4.y; wgt[j][2] = w4.z; wgt[j][3] = w4.w;
+  }
+  // window: x[m] = P at token t - 3 + m (zero before the row start)
+  float win[CPL][3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int64_t t = (int64_t)tile * kTile - 3 + m;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) win[j][m] = t >= 0 ? src[(row0 - 3 + m) * a.ldp + j] : 0.f;
+  }
+  float* dst = a.out[s] + c0;
+  for (int tb = 0; tb < kTile; tb += 8) {
+    float xin[8][CPL];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if constexpr (CPL == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src + (row0 + tb + i) * a.ldp);
+        xin[i][0] = v.x; xin[i][1] = v.y;
+      } else {
+        xin[i][0] = src[(row0 + tb + i) * a.ldp];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float y[CPL];
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const float c = wgt[j][0] * win[j][0] + wgt[j][1] * win[j][1] + wgt[j][2] * win[j][2] + wgt[j][3] * xin[i][j];
+        win[j][0] = win[j][1];
+        win[j][1] = win[j][2];
+        win[j][2] = xin[i][j];
+        y[j] = c * sigmoidf_(c);  // SiLU
+        ss += y[j] * y[j];
+      }
+      if (s < 2) {  // wave-uniform: q and k are L2-normalised over the head dim
+        const float inv = 1.f / fmaxf(sqrtf(wave_sum(ss)), a.l2eps);
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) y[j] *= inv;
+      }
+      float* o = dst + (row0 + tb + i) * HD;
+      if constexpr (CPL == 2) *reinterpret_cast<float2*>(o) = make_float2(y[0], y[1]);
+      else o[0] = y[0];
+    }
+  }
+  if (s == 0) {
+    // beta of the tile's 64 tokens for this head, one token per lane
+    const int64_t row = row0 + lane;
+    a.beta[row * a.H + h] = sigmoidf_(a.P[row * a.ldp + a.off_b + h]);
+  }
+  if (s == 1 && h == 0) {
+    // low-rank slices of the tile, rounded to bf16 (round to nearest even)
+    for (int i = 0; i < kTile; ++i) {
+      const int64_t row = row0 + i;
+      for (int c = lane; c < a.nr; c += kWave) {
+        const __bf16 v = (__bf16)a.P[row * a.ldp + a.off_r + c];
+        a.R[row * a.nr + c] = __builtin_bit_cast(uint16_t, v);
+      }
+    }
+  }
+}
+
+// g <- lb * sigmoid(exp(A_log_h) * (g + dt_bias)), four channels per thread
+__global__ __launch_bounds__(kLayerThreads) void layer_gate_kernel(float* g, const float* A_log,
+                                                                   const float* dt_bias, int64_t n4, int HD, int D,
+                                                                   float lb) {
+  for (int64_t i = (int64_t)blockIdx.x * kLayerThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kLayerThreads) {
+    const int c = (int)((i * 4) % HD);
+    float4 v = reinterpret_cast<float4*>(g)[i];
+    const float4 bias = *reinterpret_cast<const float4*>(dt_bias + c);
+    const float lam = expf(A_log[c / D]);  // the 4 channels share one head (D % 4 == 0)
+    v.x = lb * sigmoidf_(lam * (v.x + bias.x));
+    v.y = lb * sigmoidf_(lam * (v.y + bias.y));
+    v.z = lb * sigmoidf_(lam * (v.z + bias.z));
+    v.w = lb * sigmoidf_(lam * (v.w + bias.w));
+    reinterpret_cast<float4*>(g)[i] = v;
+  }
+}
+
+// y = o / sqrt(mean_D(o^2) + eps) * norm_w * sigmoid(gate), one wave per (token, head)
+template <int D>
+__global__ __launch_bounds__(kLayerThreads) void layer_norm_gate_kernel(const float* o, const float* gate,
+                                                                        const float* norm_w, uint16_t* y,
+                                                                        int64_t nwaves, float eps) {
+  constexpr int CPL = D / kWave;
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * (kLayerThreads / kWave) + (threadIdx.x >> 6);
+  if (wid >= nwaves) return;
+  const size_t base = (size_t)wid * D + CPL * lane;  // o, gate and y share the [BT, H, D] order
+  float x[CPL], gt[CPL];
+  if constexpr (CPL == 2) {
+    const float2 a = *reinterpret_cast<const float2*>(o + base);
+    const float2 b = *reinterpret_cast<const float2*>(gate + base);
+    x[0] = a.x; x[1] = a.y; gt[0] = b.x; gt[1] = b.y;
+  } else {
+    x[0] = o[base];
+    gt[0] = gate[base];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) ss += x[j] * x[j];
+  const float inv = 1.f / sqrtf(wave_sum(ss) / D + eps);
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const float v = x[j] * inv * norm_w[CPL * lane + j] * sigmoidf_(gt[j]);
+    y[base + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct LayerLayout {
+  int64_t BT;
+  int HD, NP, NR;
+  size_t off_wcat, off_P, off_R, off_q, off_k, off_v, off_g, off_beta, off_o, off_core, total;
+  size_t core_bytes;
+};
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+kda_fwd_params core_params(const kda_layer_params* p) {
+  kda_fwd_params c{};
+  c.B = p->B; c.T = p->T; c.H = p->H; c.K = p->D; c.V = p->D;
+  c.qkv_dtype = KDA_DTYPE_F32; c.g_dtype = KDA_DTYPE_F32; c.beta_dtype = KDA_DTYPE_F32;
+  c.scale = 1.f / sqrtf((float)p->D);
+  c.chunk_size = 64;
+  c.use_qk_l2norm = 0;
+  c.l2norm_eps = 1e-6f;
+  c.num_seqs = 0;
+  return c;
+}
+
+kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
+  clear_msg();
+  if (!p) return fail_msg(KDA_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 1 || p->T < 1 || p->M < 1 || p->H < 1) return fail_msg(KDA_ERR_INVALID_ARG, "need B, T, M, H >= 1");
+  if (p->T % 64) return fail_msg(KDA_ERR_INVALID_ARG, "T must be a multiple of 64 (got %lld)", (long long)p->T);
+  if (!(p->D == 64 || p->D == 128)) return fail_msg(KDA_ERR_UNSUPPORTED, "D must be 64 or 128 (got %d)", p->D);
+  if (p->conv_size != 4) return fail_msg(KDA_ERR_UNSUPPORTED, "conv_size must be 4 (got %d)", p->conv_size);
+  if (p->M % 8 || p->gate_rank < 8 || p->gate_rank % 8 || p->out_gate_rank < 8 || p->out_gate_rank % 8)
+    return fail_msg(KDA_ERR_INVALID_ARG, "M and both gate ranks must be positive multiples of 8");
+  if (!(p->norm_eps > 0.f) || !(p->l2_eps > 0.f)) return fail_msg(KDA_ERR_INVALID_ARG, "eps values must be > 0");
+  if (!(p->gate_lower_bound < 0.f) || p->gate_lower_bound < -5.f)
+    return fail_msg(KDA_ERR_INVALID_ARG, "gate_lower_bound must be in [-5, 0) (the core's decay range)");
+  L->BT = p->B * p->T;
+  L->HD = p->H * p->D;
+  L->NP = 3 * L->HD + p->H + p->gate_rank + p->out_gate_rank;
+  L->NR = p->gate_rank + p->out_gate_rank;
+  if (L->BT > INT32_MAX / 2 || (int64_t)L->NP * p->M > INT32_MAX || (int64_t)L->HD > 65536)
+    return fail_msg(KDA_ERR_UNSUPPORTED, "layer too large for 32-bit GEMM sizes");
+  kda_fwd_params c = core_params(p);
+  size_t cb = 0;
+  kda_status s = kda_chunk_fwd_workspace_bytes(&c, &cb);
+  if (s != KDA_OK) return s;
+  L->core_bytes = cb;
+  const size_t BT = (size_t)L->BT, HD = (size_t)L->HD;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { const size_t o = off; off = up256(off + bytes); return o; };
+  L->off_wcat = take((size_t)L->NP * p->M * 2);
+  L->off_P = take(BT * L->NP * 4);        // later the output-gate projection [BT, HD] fp32
+  L->off_R = take(BT * L->NR * 2);
+  L->off_q = take(BT * HD * 4);           // later y (bf16)
+  L->off_k = take(BT * HD * 4);
+  L->off_v = take(BT * HD * 4);
+  L->off_g = take(BT * HD * 4);
+  L->off_beta = take(BT * p->H * 4);
+  L->off_o = take(BT * HD * 4);
+  L->off_core = take(cb);
+  L->total = off;
+  return KDA_OK;
+}
+
+std::mutex g_handle_mu;
+rocblas_handle g_handles[64] = {};
+
+kda_status handle_for_device(rocblas_handle* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail_msg(KDA_ERR_HIP, "no current HIP device");
+  std::lock_guard<std::mutex> lk(g_handle_mu);
+  if (!g_handles[dev]) {
+    rocblas_handle h = nullptr;
+    if (rocblas_create_handle(&h) != rocblas_status_success)
+      return fail_msg(KDA_ERR_HIP, "rocblas_create_handle failed");
+    g_handles[dev] = h;
+  }
+  *out = g_handles[dev];
+  return KDA_OK;
+}
+
+// Y[n_rows, N] = X[n_rows, Kd] W[N, Kd]^T, row-major; X has leading dim ldx
+kda_status gemm_nt(rocblas_handle hb, const void* W, int ldw, const void* X, int ldx, void* Y, int ldy,
+                   rocblas_datatype ytype, int N, int n_rows, int Kd, const char* what) {
+  const float one = 1.f, zero = 0.f;
+  const rocblas_status st =
+      rocblas_gemm_ex(hb, rocblas_operation_transpose, rocblas_operation_none, N, n_rows, Kd, &one, W,
+                      rocblas_datatype_bf16_r, ldw, X, rocblas_datatype_bf16_r, ldx, &zero, Y, ytype, ldy, Y, ytype,
+                      ldy, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
+  if (st != rocblas_status_success)
+    return fail_msg(KDA_ERR_HIP, "rocblas_gemm_ex (%s) failed: %s", what, rocblas_status_to_string(st));
+  return KDA_OK;
+}
+
+}  // namespace
+}  // namespace kda
+
+extern "C" {
+
+kda_status kda_layer_fwd_workspace_bytes(const kda_layer_params* p, size_t* bytes) {
+  kda::LayerLayout L;
+  kda_status s = kda::check_layer(p, &L);
+  if (s != KDA_OK) return s;
+  if (!bytes) return kda::fail_msg(KDA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = L.total;
+  return KDA_OK;
+}
+
+kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, const void* x, void* x_new,
+                         float* core_out, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  using namespace kda;
+  LayerLayout L;
+  kda_status s = check_layer(p, &L);
+  if (s != KDA_OK) return s;
+  if (!w || !x || !x_new) return fail_msg(KDA_ERR_INVALID_ARG, "weights, x and x_new must be non-NULL");
+  const void* ptrs[] = {w->Wqkv, w->conv_q, w->conv_k, w->conv_v, w->Wb, w->Wad, w->Wau,
+                        w->A_log, w->dt_bias, w->Wgd, w->Wgu, w->norm_w, w->Wo};
+  for (const void* q : ptrs)
+    if (!q) return fail_msg(KDA_ERR_INVALID_ARG, "every weight pointer must be non-NULL");
+  for (const void* q : {(const void*)w->conv_q, (const void*)w->conv_k, (const void*)w->conv_v,
+                        (const void*)w->dt_bias})
+    if (reinterpret_cast<uintptr_t>(q) % 16) return fail_msg(KDA_ERR_INVALID_ARG, "conv weights and dt_bias must be 16-byte aligned");
+  if (x == x_new) return fail_msg(KDA_ERR_INVALID_ARG, "x_new must not alias x");
+  if (core_out && reinterpret_cast<uintptr_t>(core_out) % 16)
+    return fail_msg(KDA_ERR_INVALID_ARG, "core_out must be 16-byte aligned");
+  if (!workspace || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return fail_msg(KDA_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
+  if (workspace_bytes < L.total)
+    return fail_msg(KDA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
+  rocblas_handle hb;
+  s = handle_for_device(&hb);
+  if (s != KDA_OK) return s;
+  if (rocblas_set_stream(hb, stream) != rocblas_status_success) return fail_msg(KDA_ERR_HIP, "rocblas_set_stream failed");
+
+  char* ws = static_cast<char*>(workspace);
+  const int M = p->M, H = p->H, D = p->D, HD = L.HD, NP = L.NP, NR = L.NR;
+  const int BT = (int)L.BT;
+  const int r = p->gate_rank, rg = p->out_gate_rank;
+  uint16_t* wcat = reinterpret_cast<uint16_t*>(ws + L.off_wcat);
+  float* P = reinterpret_cast<float*>(ws + L.off_P);
+  uint16_t* R = reinterpret_cast<uint16_t*>(ws + L.off_R);
+  float* q = reinterpret_cast<float*>(ws + L.off_q);
+  float* k = reinterpret_cast<float*>(ws + L.off_k);
+  float* v = reinterpret_cast<float*>(ws + L.off_v);
+  float* g = reinterpret_cast<float*>(ws + L.off_g);
+  float* beta = reinterpret_cast<float*>(ws + L.off_beta);
+  float* o = core_out ? core_out : reinterpret_cast<float*>(ws + L.off_o);
+
+  // 1. concatenated input projections (rows of width M)
+  const size_t rowb = (size_t)M * 2;
+  size_t at = 0;
+  const struct { const void* src; size_t rows; } parts[] = {
+      {w->Wqkv, (size_t)3 * HD}, {w->Wb, (size_t)H}, {w->Wad, (size_t)r}, {w->Wgd, (size_t)rg}};
+  for (const auto& pt : parts) {
+    if (hipMemcpyAsync(reinterpret_cast<char*>(wcat) + at, pt.src, pt.rows * rowb, hipMemcpyDeviceToDevice, stream) !=
+        hipSuccess)
+      return fail_msg(KDA_ERR_HIP, "weight copy failed");
+    at += pt.rows * rowb;
+  }
+  // 2. P = x Wcat^T
+  s = gemm_nt(hb, wcat, M, x, M, P, NP, rocblas_datatype_f32_r, NP, BT, M, "input projections");
+  if (s != KDA_OK) return s;
+  // 3. prologue
+  {
+    PrologueArgs a{};
+    a.P = P; a.ldp = NP;
+    a.conv[0] = w->conv_q; a.conv[1] = w->conv_k; a.conv[2] = w->conv_v;
+    a.out[0] = q; a.out[1] = k; a.out[2] = v;
+    a.beta = beta; a.R = R;
+    a.T = p->T; a.H = H; a.nt = (int)(p->T / kTile);
+    a.off_b = 3 * HD; a.off_r = 3 * HD + H; a.nr = NR;
+    a.l2eps = p->l2_eps;
+    a.nwaves = p->B * a.nt * (int64_t)H * 3;
+    const int wpb = kLayerThreads / kWave;
+    const dim3 grid((unsigned)((a.nwaves + wpb - 1) / wpb));
+    if (D == 128) hipLaunchKernelGGL(layer_prologue_kernel<128>, grid, dim3(kLayerThreads), 0, stream, a);
+    else hipLaunchKernelGGL(layer_prologue_kernel<64>, grid, dim3(kLayerThreads), 0, stream, a);
+    if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "prologue launch failed");
+  }
+  // 4. decay-gate up projection, 5. gate activation
+  s = gemm_nt(hb, w->Wau, r, R, NR, g, HD, rocblas_datatype_f32_r, HD, BT, r, "decay gate");
+  if (s != KDA_OK) return s;
+  {
+    const int64_t n4 = (int64_t)BT * HD / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n4 + kLayerThreads - 1) / kLayerThreads, 8192);
+    hipLaunchKernelGGL(layer_gate_kernel, dim3(blocks), dim3(kLayerThreads), 0, stream, g, w->A_log, w->dt_bias, n4,
+                       HD, D, p->gate_lower_bound);
+    if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "gate launch failed");
+  }
+  // 6. the chunkwise core in fp32
+  {
+    kda_fwd_params c = core_params(p);
+    s = kda_chunk_fwd(&c, q, k, v, g, beta, nullptr, nullptr, o, nullptr, ws + L.off_core, L.core_bytes, stream);
+    if (s != KDA_OK) return s;
+  }
+  // 7. output-gate up projection into P's space, 8. RMSNorm * gate -> y (bf16, in q's space)
+  float* gu = P;
+  s = gemm_nt(hb, w->Wgu, rg, R + r, NR, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
+  if (s != KDA_OK) return s;
+  uint16_t* y = reinterpret_cast<uint16_t*>(q);
+  {
+    const int64_t nw = (int64_t)BT * H;
+    const int wpb = kLayerThreads / kWave;
+    const dim3 grid((unsigned)((nw + wpb - 1) / wpb));
+    if (D == 128)
+      hipLaunchKernelGGL(layer_norm_gate_kernel<128>, grid, dim3(kLayerThreads), 0, stream, o, gu, w->norm_w, y, nw,
+                         p->norm_eps);
+    else
+      hipLaunchKernelGGL(layer_norm_gate_kernel<64>, grid, dim3(kLayerThreads), 0, stream, o, gu, w->norm_w, y, nw,
+                         p->norm_eps);
+    if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "norm launch failed");
+  }
+  // 9. x_new = y Wo^T
+  return gemm_nt(hb, w->Wo, HD, y, HD, x_new, M, rocblas_datatype_bf16_r, M, BT, HD, "output projection");
+}
+
+}  // extern "C"

@@ -1,6 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed; no kernel is launched).
 
-The library must load, export every function include/kda.h declares, size
+The library must load, export every function include/*.h declares, size
 the workspace as documented and reject bad arguments before any launch.
 """
 import ctypes
@@ -15,9 +15,13 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "kda.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if h.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +33,7 @@ def test_exports_every_declared_symbol(lib):
     names = header_functions()
     assert len(names) >= 8
     for n in names:
-        assert hasattr(lib, n), f"{n} declared in kda.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
     assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
 
 
@@ -133,3 +137,55 @@ def test_status_strings(lib):
 def test_binding_fails_loudly_without_library(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "missing.so"))
+
+
+# ---------------------------------------------------------------- layer ABI
+
+def LP(**kw):
+    p = _lib.KdaLayerParams()
+    d = dict(B=2, T=128, M=256, H=2, D=128, gate_rank=32, out_gate_rank=128, conv_size=4,
+             gate_lower_bound=-5.0, norm_eps=1e-6, l2_eps=1e-6)
+    d.update(kw)
+    for k, v in d.items():
+        setattr(p, k, v)
+    return p
+
+
+def test_layer_workspace_formula(lib):
+    p = LP()
+    n = ctypes.c_size_t(0)
+    assert lib.kda_layer_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+    BT, HD, NP, NR = 256, 256, 3 * 256 + 2 + 32 + 128, 32 + 128
+    up = lambda x: (x + 255) // 256 * 256
+    core = make_params(2, 128, 2, 128, 128, 0, 0, 0, 128 ** -0.5)
+    cb = ctypes.c_size_t(0)
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(core), ctypes.byref(cb)) == 0
+    want = (up(NP * 256 * 2) + up(BT * NP * 4) + up(BT * NR * 2) + 5 * up(BT * HD * 4)
+            + up(BT * 2 * 4) + up(cb.value))
+    assert n.value == want
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=100), 1),                 # T % 64
+    (dict(D=96), 2),                  # head dim
+    (dict(conv_size=3), 2),           # conv width
+    (dict(M=100), 1),                 # M % 8
+    (dict(gate_rank=0), 1),
+    (dict(gate_lower_bound=-6.0), 1), # outside the core's decay range
+    (dict(gate_lower_bound=0.0), 1),
+    (dict(norm_eps=0.0), 1),
+    (dict(B=0), 1),
+])
+def test_layer_rejects_bad_params(lib, kw, status):
+    p = LP(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.kda_layer_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.kda_last_error()
+
+
+def test_layer_rejects_null_pointers_before_launch(lib):
+    p = LP()
+    w = _lib.KdaLayerWeights()
+    st = lib.kda_layer_fwd(ctypes.byref(p), ctypes.byref(w), ctypes.c_void_p(256), ctypes.c_void_p(512), None,
+                           ctypes.c_void_p(1 << 20), 1 << 40, None)
+    assert st == 1 and b"weight" in lib.kda_last_error()

@@ -1,0 +1,96 @@
+"""GPU parity of the KDA layer forward (include/kda_layer.h) against the float64
+layer oracle, through the C ABI.
+
+Metric: max|gpu - oracle| / max|oracle| per tensor. The layer output x_new is
+bf16 and the benchmark spec's bound for it is 2e-2; the fp32 core output o (before
+the norm) is held to the same bound, since its inputs come from bf16-operand
+projections and bf16-rounded low-rank gate activations.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle.kda_oracle as orc
+from helpers import host, rel_err, to_dev
+from kimi_delta_attention_03_amd.synthetic import layer_inputs
+
+pytestmark = pytest.mark.gpu
+
+TOL_LAYER = 2e-2
+BF16_W = ("Wqkv", "Wb", "Wad", "Wau", "Wgd", "Wgu", "Wo")
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_weights(w):
+    import torch
+    return {n: to_dev(a, torch.bfloat16 if n in BF16_W else torch.float32) for n, a in w.items()}
+
+
+def run_layer(x, w, H, D, keep_core=True):
+    import kimi_delta_attention_03_amd as kda
+    import torch
+    B, T, _ = x.shape
+    layer = kda.KdaLayer(dev_weights(w), B, T, H, D, keep_core_output=keep_core)
+    y = layer(to_dev(x, torch.bfloat16))
+    torch.cuda.synchronize()
+    return layer, y
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_layer_small_matches_oracle(D):
+    B, T, M, H, r = 2, 192, 256, 3, 32
+    _say(f"layer B={B} T={T} M={M} H={H} D={D} r={r}")
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, rank=r, seed=41 + D)
+    layer, y = run_layer(x, w, H, D)
+    ref, inter = orc.kda_layer_ref(x, w, H, D)
+    eo = rel_err(host(layer.core_out), inter["o"])
+    ey = rel_err(host(y), ref)
+    _say(f"  rel err core o={eo:.2e} x_new={ey:.2e}")
+    assert eo <= TOL_LAYER and ey <= TOL_LAYER
+
+
+def test_layer_deterministic_and_causal():
+    """Bitwise-equal reruns; changing tokens after n leaves x_new[:, :n+1] unchanged."""
+    import torch
+    B, T, M, H, D, r = 1, 256, 128, 2, 128, 16
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, rank=r, seed=77)
+    layer, y1 = run_layer(x, w, H, D, keep_core=False)
+    y1 = y1.clone()
+    y2 = layer(to_dev(x, torch.bfloat16)).clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    n = 100
+    x2 = x.copy()
+    x2[:, n + 1:] = np.float32(0.5) * x2[:, n + 1:] + np.float32(0.25)
+    x2 = torch.from_numpy(x2).to(torch.bfloat16).float().numpy()
+    y3 = layer(to_dev(x2, torch.bfloat16))
+    torch.cuda.synchronize()
+    assert torch.equal(y1[:, :n + 1], y3[:, :n + 1])
+    assert not torch.equal(y1[:, n + 1:], y3[:, n + 1:])
+
+
+def test_layer_workload4_full_size_prefix():
+    """Workload 4 at full size (B=4, T=8192, M=2048, H=16, D=128, rank 128): the
+    whole batch runs on the GPU; the oracle, which is causal, recomputes the
+    first 256 tokens of batch rows 0 and 3 and they must agree."""
+    _say("layer workload 4: generating inputs")
+    x, w = layer_inputs()
+    B, T, M = x.shape
+    H, D = 16, 128
+    _say("layer workload 4: GPU run")
+    layer, y = run_layer(x, w, H, D)
+    yh = host(y)
+    oh = host(layer.core_out)
+    assert np.isfinite(yh).all() and np.isfinite(oh).all()
+    n = 256
+    for b in (0, 3):
+        ref, inter = orc.kda_layer_ref(x[b:b + 1, :n], w, H, D)
+        eo = rel_err(oh[b:b + 1, :n], inter["o"])
+        ey = rel_err(yh[b:b + 1, :n], ref)
+        _say(f"  batch row {b}, first {n} tokens: rel err core o={eo:.2e} x_new={ey:.2e}")
+        assert eo <= TOL_LAYER and ey <= TOL_LAYER
