@@ -9,21 +9,15 @@
 // S's columns), so one workgroup owns a 16-column block of S for one
 // (sequence, head) and walks that sequence's chunks in order.
 //
-// The workgroup has 12 waves in three roles. Only V_new and the state update
-// form the chain that is serial over chunks; the output is taken off it:
-//   V waves 0..3      - wave r computes V_new for chunk rows 16 r .. 16 r + 15
-//   state waves 4..7  - hold the K x 16 fp32 state block in MFMA accumulators
-//                       (K / 64 tiles of 16 rows each) and apply the update
-//   output waves 8..11 - wave 8 + r computes O for rows 16 r .. 16 r + 15 one
-//                       chunk behind, from the previous chunk's S and V_new
-// Every chunk step has two barriers: B1 publishes V_new, B2 the new state,
-// both as MFMA B-operand halves in LDS; S and V_new are double-buffered so
-// the output waves can read chunk c - 1's copies while chunk c is in flight.
-// Each role issues its loads for a chunk NB - 1 steps ahead through a ring of
-// NB register buffers, in the window where its own work is off the chain:
-// state waves before B1 (while V_new is computed), V waves after B1 (while
-// the state is updated), output waves before B1. A full vector-memory queue
-// then stalls a wave that has nothing on the chain.
+// The workgroup has 8 waves in two roles:
+//   row waves 0..3   - wave r computes V_new and O for chunk rows 16 r .. 16 r + 15
+//   state waves 4..7 - hold the K x 16 fp32 state block in MFMA accumulators
+//                      (K / 64 tiles of 16 rows each) and apply the update.
+// Per chunk the row waves publish V_new and the state waves publish the new
+// state (both as MFMA B-operand halves) through LDS; both roles pass the
+// same two barriers per chunk. The chunk operands are read as ready-made MFMA
+// fragments from the stage-1+2 record through a ring of NB register buffers,
+// NB - 1 chunks ahead of use.
 //
 // Workgroup ids are mapped so that the V/16 workgroups of one (sequence,
 // head) get ids congruent modulo 8: with round-robin dispatch over the 8
@@ -35,26 +29,20 @@
 namespace kda {
 namespace {
 
-constexpr int kThreads34 = 768;
+constexpr int kThreads34 = 512;
 
 __device__ __forceinline__ void lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// operands of one chunk for a V wave
+// operands of one chunk for a row wave
 template <typename T, int K>
-struct VFrags {
+struct RowFrags {
   static constexpr int NKB = K / 32;
   typename Vec<T>::x8 w[NKB];   // W rows of this wave's 16-row block
-  typename Vec<T>::x4 u;        // U, accumulator layout
-};
-
-// operands of one chunk for an output wave
-template <typename T, int K>
-struct OFrags {
-  static constexpr int NKB = K / 32;
   typename Vec<T>::x8 qg[NKB];  // qg rows of this wave's block
   typename Vec<T>::x8 aq[2];    // Aqk rows of this wave's block
+  typename Vec<T>::x4 u;        // U, accumulator layout
 };
 
 // operands of one chunk for a state wave
@@ -66,7 +54,12 @@ struct StateFrags {
 };
 
 // Fragment loads go through a buffer resource covering one record: a uniform
-// descriptor and a single per-lane offset register shared by every load.
+// descriptor and a single per-lane offset register shared by every load. With 64-bit per-lane
+// addresses instead, the register allocator reuses address registers that are
+// still the destination of in-flight loads and the prefetch ring stalls.
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ void bload(bf16x8& d, __amdgpu_buffer_rsrc_t r, int lane_off, int soff) {
   d = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, lane_off, soff, 0));
 }
@@ -87,44 +80,38 @@ __device__ __forceinline__ void bload4(floatx4& d, __amdgpu_buffer_rsrc_t r, int
 // vector-memory path, whose rate bounds a chunk step, so nothing is loaded
 // twice: gamma comes as one float per lane and is spread by lane shuffles.
 template <typename T, int K>
-__device__ __forceinline__ void load_v(VFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, const Stage34Args& a, int r,
-                                       int lane_off, int vb) {
+__device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff,
+                                         const Stage34Args& a, int r, int lane_off, int vb) {
   constexpr int NKB = K / 32;
   constexpr int F8B = 512 * (int)sizeof(T);  // bytes of one frag8 fragment
   constexpr int F4B = 256 * (int)sizeof(T);  // bytes of one accumulator fragment
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) bload(f.w[kb], rs, lane_off, (int)a.off_w + (r * NKB + kb) * F8B);
-  bload4(f.u, rs, lane_off, (int)a.off_u + (vb * 4 + r) * F4B);
-}
-
-template <typename T, int K>
-__device__ __forceinline__ void load_o(OFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, const Stage34Args& a, int r,
-                                       int lane_off) {
-  constexpr int NKB = K / 32;
-  constexpr int F8B = 512 * (int)sizeof(T);
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) bload(f.qg[kb], rs, lane_off, (int)a.off_qg + (r * NKB + kb) * F8B);
+  for (int kb = 0; kb < NKB; ++kb) {
+    bload(f.w[kb], rs, lane_off, soff + (int)a.off_w + (r * NKB + kb) * F8B);
+    bload(f.qg[kb], rs, lane_off, soff + (int)a.off_qg + (r * NKB + kb) * F8B);
+  }
   // every wave issues both Aqk loads (no branch around a load keeps the
   // compiler's memory-counter waits exact); rows < 32 have no second block and
   // point that load past the end of the record, where it reads zeros without
   // touching memory
-  bload(f.aq[0], rs, lane_off, (int)a.off_aq + aq_frag(r, 0) * F8B);
-  bload(f.aq[1], rs, lane_off, r >= 2 ? (int)a.off_aq + aq_frag(r, 1) * F8B : (int)a.rec_bytes);
+  bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + aq_frag(r, 0) * F8B);
+  bload(f.aq[1], rs, lane_off, r >= 2 ? soff + (int)a.off_aq + aq_frag(r, 1) * F8B : (int)a.rec_bytes);
+  bload4(f.u, rs, lane_off, soff + (int)a.off_u + (vb * 4 + r) * F4B);
 }
 
 template <typename T, int K>
-__device__ __forceinline__ void load_state(StateFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, const Stage34Args& a,
-                                           int s, int lane_off, int gam_off) {
+__device__ __forceinline__ void load_state(StateFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff,
+                                           const Stage34Args& a, int s, int lane_off, int gam_off) {
   constexpr int TPW = K / 64;
   constexpr int F8B = 512 * (int)sizeof(T);
 #pragma unroll
   for (int m = 0; m < TPW; ++m) {
     const int rt = s * TPW + m;
-    bload(f.kg[m][0], rs, lane_off, (int)a.off_kg + (rt * 2 + 0) * F8B);
-    bload(f.kg[m][1], rs, lane_off, (int)a.off_kg + (rt * 2 + 1) * F8B);
+    bload(f.kg[m][0], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 0) * F8B);
+    bload(f.kg[m][1], rs, lane_off, soff + (int)a.off_kg + (rt * 2 + 1) * F8B);
   }
   f.gam = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                        rs, gam_off, (int)a.off_gam + 64 * TPW * s, 0));
+                                        rs, gam_off, soff + (int)a.off_gam + 64 * TPW * s, 0));
 }
 
 template <typename T, int K, int NB>
@@ -138,16 +125,14 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   typedef typename Vec<T>::x4 F4;
   typedef typename Vec<T>::x8 F8;
 
-  __shared__ F4 sS[2][NST][64];    // state block as B-operand halves, by chunk parity
-  __shared__ F4 sVn[2][4][64];     // V_new block as B-operand halves, by chunk parity
+  __shared__ F4 sS[NST][64];       // state block as B-operand halves
+  __shared__ F4 sVn[4][64];        // V_new block as B-operand halves
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index as a scalar: conditions on it must compile to scalar branches,
   // because an MFMA placed under an EXEC mask still executes for all lanes
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int role = w >> 2;         // 0: V waves, 1: state waves, 2: output waves
-  const int r0 = w & 3;
   const int gq = lane >> 4;
   const int xi = lane & 15;
 
@@ -185,36 +170,15 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   const size_t state_base = ((size_t)seq * H + h) * K * V + 16 * vb + xi;
   // buffer resource over exactly one record (chunk cc of this sequence, head h;
   // records are chunk-major): offsets past the record read zeros
-  auto rec_rsrc = [&](int c) {
-    const int cc = c < last ? c : last;  // prefetches past the end re-read the last chunk
+  auto rec_rsrc = [&](int cc) {
     const char* base = a.ws + a.meta_bytes + (((size_t)p0 + cc) * H + h) * a.rec_bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)a.rec_bytes, 0x00020000);
   };
   const int lane_off = 16 * lane;
 
-  if (nch <= 0) {  // empty sequence: final state = initial state (uniform branch, no barriers)
-    if (role == 1 && a.final_state) {
-#pragma unroll
-      for (int m = 0; m < TPW; ++m) {
-        const int rt = (r0)*TPW + m;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const size_t i = state_base + (size_t)(16 * rt + 4 * gq + r) * V;
-          a.final_state[i] = a.init ? a.init[i] : 0.f;
-        }
-      }
-    }
-    return;
-  }
-  // whole ring passes with a single exit: steps past the last chunk only issue
-  // their (clamped) loads. An exit inside a pass, or a separate tail, would
-  // make the memory-counter waits at the top of a pass cover the ring. Every
-  // role passes 1 + 2 (npass NB + 1) barriers.
-  const int npass = (nch + NB - 1) / NB;
-
-  if (role == 1) {
+  if (w >= 4) {
     // ------------------------------------------------------------ state waves
-    const int s = r0;
+    const int s = w - 4;
     floatx4 S[TPW];
 #pragma unroll
     for (int m = 0; m < TPW; ++m) {
@@ -224,43 +188,55 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
         S[m][r] = a.init ? a.init[state_base + (size_t)(16 * rt + 4 * gq + r) * V] : 0.f;
       F4 y;
       cvt4(S[m], y);
-      sS[0][rt][lane] = y;
+      sS[rt][lane] = y;
     }
-    StateFrags<T, K> F[NB];
-    const int gam_off = 4 * (lane % (16 * TPW));
+    if (nch > 0) {
+      StateFrags<T, K> F[NB];
+      // prefetches are unconditional (chunk index clamped to the last chunk): with
+      // no branch around the loads the memory-counter waits stay exact
+      auto issue = [&](StateFrags<T, K>& f, int c) {
+        const int cc = c < last ? c : last;
+        load_state<T, K>(f, rec_rsrc(cc), 0, a, s, lane_off, 4 * (lane % (16 * TPW)));
+      };
+      // the prologue loads stay in chunk order (no scheduling across the barriers):
+      // the memory-counter wait at the top of each ring pass is computed from
+      // the worst case over the loop entry and the back edge
 #pragma unroll
-    for (int i = 0; i < NB - 1; ++i) {
-      load_state<T, K>(F[i], rec_rsrc(i), a, s, lane_off, gam_off);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_sync();  // initial state published
-    auto step = [&](StateFrags<T, K>& f, StateFrags<T, K>& next, int c) {
-      load_state<T, K>(next, rec_rsrc(c + NB - 1), a, s, lane_off, gam_off);
-      lds_sync();  // B1: V_new of chunk c published
-      if (c < nch) {  // uniform: every role skips the same steps, barriers included
-        const F8 Vb0 = stack8<T>(sVn[c & 1][0][lane], sVn[c & 1][1][lane]);
-        const F8 Vb1 = stack8<T>(sVn[c & 1][2][lane], sVn[c & 1][3][lane]);
-#pragma unroll
-        for (int m = 0; m < TPW; ++m) {
-          floatx4 gm;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) gm[r] = __shfl(f.gam, 16 * m + 4 * gq + r, 64);
-          S[m] = S[m] * gm;
-          S[m] = mma32(S[m], f.kg[m][0], Vb0);
-          S[m] = mma32(S[m], f.kg[m][1], Vb1);
-          F4 y;
-          cvt4(S[m], y);
-          sS[(c + 1) & 1][s * TPW + m][lane] = y;
-        }
+      for (int i = 0; i < NB - 1; ++i) {
+        issue(F[i], i);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      lds_sync();  // B2: state after chunk c published
-    };
-    for (int p = 0; p < npass; ++p) {
+      lds_sync();  // initial state published
+      auto step = [&](StateFrags<T, K>& f, StateFrags<T, K>& next, int c) {
+        issue(next, c + NB - 1);
+        if (c < nch) {  // uniform: both roles skip the same steps, barriers included
+          lds_sync();   // V_new of chunk c published
+          const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
+          const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
 #pragma unroll
-      for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
+          for (int m = 0; m < TPW; ++m) {
+            floatx4 gm;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) gm[r] = __shfl(f.gam, 16 * m + 4 * gq + r, 64);
+            S[m] = S[m] * gm;
+            S[m] = mma32(S[m], f.kg[m][0], Vb0);
+            S[m] = mma32(S[m], f.kg[m][1], Vb1);
+            F4 y;
+            cvt4(S[m], y);
+            sS[s * TPW + m][lane] = y;
+          }
+          lds_sync();  // state after chunk c published
+        }
+      };
+      // whole ring passes with a single exit: steps past the last chunk only
+      // issue their (clamped) loads. An exit inside a pass, or a separate tail,
+      // would make the memory-counter waits at the top of a pass cover the ring.
+      const int npass = (nch + NB - 1) / NB;
+      for (int p = 0; p < npass; ++p) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
+      }
     }
-    lds_sync();  // the output waves' last chunk
-    lds_sync();
     if (a.final_state) {
 #pragma unroll
       for (int m = 0; m < TPW; ++m) {
@@ -269,72 +245,58 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
         for (int r = 0; r < 4; ++r) a.final_state[state_base + (size_t)(16 * rt + 4 * gq + r) * V] = S[m][r];
       }
     }
-  } else if (role == 0) {
-    // ---------------------------------------------------------------- V waves
-    VFrags<T, K> F[NB];
+  } else {
+    // -------------------------------------------------------------- row waves
+    if (nch <= 0) return;
+    const int r0 = w;  // chunk rows 16 r0 .. 16 r0 + 15
+    T* out = reinterpret_cast<T*>(a.o);
+    T* sink = reinterpret_cast<T*>(const_cast<char*>(a.ws) + a.off_sink);
+    RowFrags<T, K> F[NB];
+    auto issue = [&](RowFrags<T, K>& f, int c) {
+      const int cc = c < last ? c : last;
+      load_row<T, K>(f, rec_rsrc(cc), 0, a, r0, lane_off, vb);
+    };
+    // prologue loads in chunk order (see the state waves)
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) {
-      load_v<T, K>(F[i], rec_rsrc(i), a, r0, lane_off, vb);
+      issue(F[i], i);
       __builtin_amdgcn_sched_barrier(0);
     }
     lds_sync();  // initial state published
-    auto step = [&](VFrags<T, K>& f, VFrags<T, K>& next, int c) {
-      if (c < nch) {
+    auto step = [&](RowFrags<T, K>& f, RowFrags<T, K>& next, int c) {
+      const int64_t tok0 = tfirst + (int64_t)c * C;
+      const int len = c < nch - 1 ? C : (c == nch - 1 ? lastlen : 0);
+      // critical part first: V_new = U - W S feeds the state waves
+      F8 Sb[NKB];
+      if (c < nch) {  // uniform, as in the state waves
         floatx4 accV = zero4();
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          accV = mma32(accV, f.w[kb], stack8<T>(sS[c & 1][2 * kb][lane], sS[c & 1][2 * kb + 1][lane]));
+        for (int kb = 0; kb < NKB; ++kb) {
+          Sb[kb] = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
+          accV = mma32(accV, f.w[kb], Sb[kb]);
+        }
         const floatx4 vn = widen4(f.u) - accV;
         F4 vnT;
         cvt4(vn, vnT);
-        sVn[c & 1][r0][lane] = vnT;
+        sVn[r0][lane] = vnT;
+        lds_sync();  // V_new of chunk c published
       }
-      lds_sync();  // B1: V_new of chunk c published
-      load_v<T, K>(next, rec_rsrc(c + NB - 1), a, r0, lane_off, vb);
-      lds_sync();  // B2
-    };
-    for (int p = 0; p < npass; ++p) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
-    }
-    lds_sync();  // the output waves' last chunk
-    lds_sync();
-  } else {
-    // ----------------------------------------------------------- output waves
-    // chunk d is written in the step after its own: its chunk-start state and
-    // V_new stay in the other parity's LDS buffers until the step after that
-    T* out = reinterpret_cast<T*>(a.o);
-    T* sink = reinterpret_cast<T*>(const_cast<char*>(a.ws) + a.off_sink);
-    OFrags<T, K> F[NB];
-#pragma unroll
-    for (int i = 0; i < NB - 1; ++i) {
-      load_o<T, K>(F[i], rec_rsrc(i), a, r0, lane_off);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lds_sync();  // initial state published
-    lds_sync();  // step of chunk 0: nothing to write yet
-    lds_sync();
-    auto step = [&](OFrags<T, K>& f, OFrags<T, K>& next, int d) {
-      // before B1: take S_d (overwritten in this step's second half) and issue loads
-      F8 Sb[NKB];
-      if (d < nch) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) Sb[kb] = stack8<T>(sS[d & 1][2 * kb][lane], sS[d & 1][2 * kb + 1][lane]);
-      }
-      load_o<T, K>(next, rec_rsrc(d + NB - 1), a, r0, lane_off);
-      lds_sync();  // B1
-      const int64_t tok0 = tfirst + (int64_t)d * C;
-      const int len = d < nch - 1 ? C : (d == nch - 1 ? lastlen : 0);
+      // the next loads are issued while the state waves apply the update; a
+      // full vector-memory queue then stalls this wave, not the chain
+      issue(next, c + NB - 1);
       // accO is built transposed (operands swapped): lane (g, i) then holds chunk
       // row 16 r0 + i at the four consecutive columns 16 vb + 4 g .. + 3, which
       // leaves as one vector store per lane
       floatx4 accO = zero4();
-      if (d < nch) {
+      if (c < nch) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) accO = mma32(accO, Sb[kb], f.qg[kb]);
+        const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
+        const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
         // intra-chunk part, causal: row block r0 reads V_new blocks <= r0
-        accO = mma32(accO, stack8<T>(sVn[d & 1][0][lane], sVn[d & 1][1][lane]), f.aq[0]);
-        if (r0 >= 2) accO = mma32(accO, stack8<T>(sVn[d & 1][2][lane], sVn[d & 1][3][lane]), f.aq[1]);
+        accO = mma32(accO, Vb0, f.aq[0]);
+        if (r0 >= 2) accO = mma32(accO, Vb1, f.aq[1]);
+        lds_sync();  // state after chunk c published
       }
       // rows past the end of a short chunk, and every row of a step past the
       // last chunk, store into the sink: the store is never under a branch
@@ -343,8 +305,9 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
       cvt4(accO, y);
       T* dst = row < len ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
       *reinterpret_cast<F4*>(dst) = y;
-      lds_sync();  // B2
     };
+    // whole ring passes with a single exit (see the state waves)
+    const int npass = (nch + NB - 1) / NB;
     for (int p = 0; p < npass; ++p) {
 #pragma unroll
       for (int j = 0; j < NB; ++j) step(F[j], F[(j + NB - 1) % NB], p * NB + j);
