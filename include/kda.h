@@ -128,6 +128,19 @@ typedef struct {
 
 kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* info);
 
+/* One decode step of the token recurrence for B independent sequences
+ * ("KDA Doesn't Care About the Future", section "Chunkwise KDA in Broad
+ * Strokes", steps (0)-(5); Tokamax "chunk_kda_fwd design doc" section 9.1.2,
+ * Paper Eq. 1), with the same state layout as the chunked path:
+ *   S <- (I - beta k k^T) Diag(exp g) S + beta k v^T,   o = scale * S^T q
+ * p->T must be 1 (one token per batch row), p->num_seqs 0; chunk_size is
+ * ignored. q, k, g: [B, 1, H, K]; v, o: [B, 1, H, V]; beta: [B, 1, H];
+ * state: [B, H, K, V] fp32, read and overwritten in place (the state after
+ * the token). use_qk_l2norm normalises q and k as in kda_chunk_fwd. Needs
+ * no workspace; same stream and error conventions as the other calls. */
+kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                           const void* g, const void* beta, float* state, void* o, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status s);
 

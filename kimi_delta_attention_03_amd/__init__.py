@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
 __all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
-           "KdaLayer", "layer_fwd"]
+           "KdaLayer", "layer_fwd", "decode_step"]
 
 
 def _torch():
@@ -146,6 +146,37 @@ def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, c
     """Chunkwise KDA forward on the GPU. Returns (o, final_state or None)."""
     return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
                       output_final_state, use_qk_l2norm, l2norm_eps)()
+
+
+def decode_step(q, k, v, g, beta, state, scale=None, use_qk_l2norm=False, l2norm_eps=1e-6, out=None):
+    """One token per sequence through the KDA recurrence (include/kda.h,
+    kda_decode_step). q, k, g: [B, H, K]; v: [B, H, V]; beta: [B, H];
+    state: fp32 [B, H, K, V], updated in place. Returns o [B, H, V] in q's dtype."""
+    torch = _torch()
+    lib = _lib.load()
+    if q.dim() != 3 or k.shape != q.shape or g.shape != q.shape:
+        raise KdaValueError(1, "q, k, g must be [B, H, K] with equal shapes")
+    B, H, K = q.shape
+    if v.dim() != 3 or tuple(v.shape[:2]) != (B, H):
+        raise KdaValueError(1, "v must be [B, H, V]")
+    V = v.shape[2]
+    if tuple(beta.shape) != (B, H):
+        raise KdaValueError(1, "beta must be [B, H]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise KdaValueError(1, "q, k, v must share a dtype")
+    for t in (q, k, v, g, beta, state):
+        if not t.is_cuda or not t.is_contiguous():
+            raise KdaValueError(1, "inputs and state must be contiguous GPU tensors")
+    if state.dtype != torch.float32 or tuple(state.shape) != (B, H, K, V):
+        raise KdaValueError(1, f"state must be fp32 [{B}, {H}, {K}, {V}]")
+    if scale is None:
+        scale = K ** -0.5
+    p = make_params(B, 1, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale, 64,
+                    use_qk_l2norm, l2norm_eps, 0)
+    o = out if out is not None else torch.empty((B, H, V), dtype=q.dtype, device=q.device)
+    _lib.check(lib.kda_decode_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                   _ptr(o), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    return o
 
 
 # bf16 projection weights and fp32 small parameters of the layer (include/kda_layer.h)

@@ -72,6 +72,7 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_abi_version": (ctypes.c_int32, []),
+    "kda_decode_step": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }

@@ -21,7 +21,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB_NAME = "libkda_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-SOURCES = ["kda_api.cpp", "kda_stage12.hip", "kda_stage34.hip", "kda_varlen.hip", "kda_layer.hip"]
+SOURCES = ["kda_api.cpp", "kda_stage12.hip", "kda_stage34.hip", "kda_varlen.hip", "kda_layer.hip",
+           "kda_decode.hip"]
 # the layer's plain projections run on rocBLAS
 LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
 

@@ -216,6 +216,37 @@ kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, 
   return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
 }
 
+kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, float* state, void* o, hipStream_t stream) {
+  g_msg[0] = 0;
+  if (!p) return fail(KDA_ERR_INVALID_ARG, "params is NULL");
+  if (p->B < 0 || p->H <= 0) return fail(KDA_ERR_INVALID_ARG, "need B >= 0 and H > 0");
+  if (p->T != 1) return fail(KDA_ERR_INVALID_ARG, "a decode step takes T == 1 (got %lld)", (long long)p->T);
+  if (p->num_seqs != 0) return fail(KDA_ERR_INVALID_ARG, "a decode step takes num_seqs == 0 (one token per row)");
+  if (p->K <= 0 || p->V <= 0 || p->K > 256) return fail(KDA_ERR_INVALID_ARG, "need 0 < K <= 256 and V > 0");
+  if (!(p->K == p->V && (p->K == 64 || p->K == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "GPU path supports K == V in {64, 128} (got K=%d V=%d)", p->K, p->V);
+  for (int32_t d : {p->qkv_dtype, p->g_dtype, p->beta_dtype})
+    if (d != KDA_DTYPE_F32 && d != KDA_DTYPE_BF16) return fail(KDA_ERR_INVALID_ARG, "unknown dtype %d", d);
+  if (p->use_qk_l2norm && !(p->l2norm_eps > 0.f)) return fail(KDA_ERR_INVALID_ARG, "l2norm_eps must be > 0");
+  const int64_t units = p->B * p->H;
+  if (units > (int64_t)INT32_MAX / 4) return fail(KDA_ERR_UNSUPPORTED, "problem too large");
+  if (units == 0) return KDA_OK;
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta, state and o must be non-NULL");
+  if (!aligned(state, 16)) return fail(KDA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+  kda::DecodeArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.state = state; a.o = o;
+  a.scale = p->scale;
+  a.l2norm = p->use_qk_l2norm != 0;
+  a.l2eps = p->l2norm_eps;
+  a.nunits = (int)units;
+  hipError_t e = kda::launch_decode(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, p->g_dtype == KDA_DTYPE_F32,
+                                    p->beta_dtype == KDA_DTYPE_F32, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
 const char* kda_status_string(kda_status s) {
   switch (s) {
     case KDA_OK: return "KDA_OK";

@@ -42,12 +42,28 @@ struct Stage34Args {
   size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;
 };
 
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  float* state;        // [N, H, K, V], in place
+  void* o;
+  float scale;
+  int l2norm;
+  float l2eps;
+  int nunits;          // N * H
+};
+
 // bf16 == 1 selects the bf16 instantiation (bf16 q/k/v, bf16 intermediates).
 hipError_t launch_stage12(const Stage12Args& a, int K, int bf16, int nblocks, hipStream_t s);
 hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s);
 hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, size_t ncp,
                              size_t off_chunk_tab, size_t off_seq_tab, size_t off_order,
                              hipStream_t s);
+
+hipError_t launch_decode(const DecodeArgs& a, int K, int bf16_qkv, int g_f32, int b_f32, hipStream_t s);
 
 // sets the thread-local message returned by kda_last_error and returns s
 kda_status fail_msg(kda_status s, const char* fmt, ...);

@@ -189,3 +189,16 @@ def test_layer_rejects_null_pointers_before_launch(lib):
     st = lib.kda_layer_fwd(ctypes.byref(p), ctypes.byref(w), ctypes.c_void_p(256), ctypes.c_void_p(512), None,
                            ctypes.c_void_p(1 << 20), 1 << 40, None)
     assert st == 1 and b"weight" in lib.kda_last_error()
+
+
+def test_decode_rejects_bad_params_before_launch(lib):
+    vp = ctypes.c_void_p(4096)
+    p = make_params(2, 64, 4, 128, 128, 1, 1, 1, 0.1)          # T must be 1
+    assert lib.kda_decode_step(ctypes.byref(p), vp, vp, vp, vp, vp, vp, vp, None) == 1
+    assert b"T == 1" in lib.kda_last_error()
+    p = make_params(2, 1, 4, 96, 96, 1, 1, 1, 0.1)             # unsupported head dim
+    assert lib.kda_decode_step(ctypes.byref(p), vp, vp, vp, vp, vp, vp, vp, None) == 2
+    p = make_params(2, 1, 4, 128, 128, 1, 1, 1, 0.1)
+    assert lib.kda_decode_step(ctypes.byref(p), vp, vp, vp, vp, vp, None, vp, None) == 1
+    p = make_params(0, 1, 4, 128, 128, 1, 1, 1, 0.1)           # empty batch: nothing to do
+    assert lib.kda_decode_step(ctypes.byref(p), None, None, None, None, None, None, None, None) == 0
