@@ -2,7 +2,7 @@
 // persistent: each loops over (chunk, head) items, keeps everything an item
 // needs in LDS and writes the outputs once, as MFMA fragments, into the item's
 // workspace record. The raw inputs of the next item are loaded into registers
-// while the current one is in its solve and W/U phases.
+// as soon as the current item has consumed them.
 //
 // What it computes for a chunk of C = 64 tokens (Tokamax "chunk_kda_fwd
 // design doc", sections 4.1.2-4.1.4 and 9.1.3-9.1.5, Paper Eq. 6-7):
@@ -182,18 +182,22 @@ void stage12_kernel(Stage12Args a) {
     typename Raw4<T>::type q[NKB][2];
     uint32_t b;
   };
-  auto issue_qkgb = [&](RawIn& r, const Item& it) {
-    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k, it.tok0, it.h, H, RBK, it.len);
+  // the raw inputs are loaded in three groups, each as soon as the previous
+  // item has consumed its registers: k, g, beta (phase 1), q (phase 2), v (phase 5)
+  auto issue_q = [&](RawIn& r, const Item& it) {
     const __amdgpu_buffer_rsrc_t rq = rows_rsrc(a.q, it.tok0, it.h, H, RBK, it.len);
-    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(a.g, it.tok0, it.h, H, RBG, it.len);
-    const __amdgpu_buffer_rsrc_t rb = rows_rsrc(a.beta, it.tok0, it.h, H, RBB, it.len);
-#pragma unroll
-    for (int m = 0; m < NCH; ++m) r.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_k0 + m * kstep, 0, 0);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       r.q[kb][0] = bload4<T>(rq, off_q0 + 32 * kb * E);
       r.q[kb][1] = bload4<T>(rq, off_q0 + (32 * kb + 16) * E);
     }
+  };
+  auto issue_kgb = [&](RawIn& r, const Item& it) {
+    const __amdgpu_buffer_rsrc_t rk = rows_rsrc(a.k, it.tok0, it.h, H, RBK, it.len);
+    const __amdgpu_buffer_rsrc_t rg = rows_rsrc(a.g, it.tok0, it.h, H, RBG, it.len);
+    const __amdgpu_buffer_rsrc_t rb = rows_rsrc(a.beta, it.tok0, it.h, H, RBB, it.len);
+#pragma unroll
+    for (int m = 0; m < NCH; ++m) r.k[m] = __builtin_amdgcn_raw_buffer_load_b128(rk, off_k0 + m * kstep, 0, 0);
 #pragma unroll
     for (int rr = 0; rr < RPS; ++rr) {
 #pragma unroll
@@ -218,7 +222,8 @@ void stage12_kernel(Stage12Args a) {
   RawIn R;
   if constexpr (kPrefetch) {
     const Item it0 = item_of(blockIdx.x);
-    issue_qkgb(R, it0);
+    issue_kgb(R, it0);
+    issue_q(R, it0);
     issue_v(R, it0);
   }
 
@@ -227,7 +232,8 @@ void stage12_kernel(Stage12Args a) {
     const int nxt = item + (int)gridDim.x < nitems ? item + (int)gridDim.x : nitems - 1;
     const Item nx = item_of(nxt);
     if constexpr (!kPrefetch) {
-      issue_qkgb(R, it);
+      issue_kgb(R, it);
+      issue_q(R, it);
       issue_v(R, it);
     }
     const int p = it.p, h = it.h;
@@ -279,6 +285,8 @@ void stage12_kernel(Stage12Args a) {
       for (int c = 0; c < CPT; c += 4)
         *reinterpret_cast<floatx4*>(sA + seg * K + cg * CPT + c) = floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
     }
+    // k, g and beta of this item are consumed: start loading the next item's
+    if constexpr (kPrefetch) issue_kgb(R, nx);
     lds_sync();
     {
 #pragma unroll
@@ -381,6 +389,9 @@ void stage12_kernel(Stage12Args a) {
         store_frag8<T>(rec + a.off_aq, ((size_t)aq_frag(w, 1) * 64 + lane) * 8, stackf(aq[2], aq[3]));
     }
 
+    // q of this item is consumed: start loading the next item's
+    if constexpr (kPrefetch) issue_q(R, nx);
+
     // ---------------- phase 3: gated keys kg^T and gamma (only G, k needed)
     {
       constexpr int TPW = K / 64;  // 16-channel row tiles per wave
@@ -402,8 +413,6 @@ void stage12_kernel(Stage12Args a) {
       }
       if (tid < K) reinterpret_cast<float*>(rec + a.off_gam)[tid] = exp2_fast(sG[(C - 1) * GS + tid]);
     }
-    // q, k, g and beta of this item are consumed: start loading the next item's
-    if constexpr (kPrefetch) issue_qkgb(R, nx);
     lds_sync();
 
     // ---------------- phase 4: A = (I + L)^-1 in fp32
