@@ -118,6 +118,35 @@ def cpu_baseline(x, target_s=15.0):
     }
 
 
+def bench_layer(args, torch, kda):
+    """The KDA layer around the core (workload 4): one step = the whole layer
+    forward over a [B, T, M] bf16 input, inputs and weights resident in HBM."""
+    from kimi_delta_attention_03_amd.synthetic import WORKLOADS, layer_inputs
+    cfg = WORKLOADS[4]
+    B, T, M, H, D = cfg["B"], cfg["T"], cfg["M"], cfg["H"], cfg["D"]
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, seed=cfg["seed"])
+    bf = ("Wqkv", "Wb", "Wad", "Wau", "Wgd", "Wgu", "Wo")
+    wd = {n: torch.from_numpy(a).to(torch.bfloat16 if n in bf else torch.float32).to("cuda:0") for n, a in w.items()}
+    xd = torch.from_numpy(x).to(torch.bfloat16).to("cuda:0")
+    layer = kda.KdaLayer(wd, B, T, H, D)
+    for _ in range(args.warmup):
+        layer(xd)
+    ms = time_loop(lambda: layer(xd), args.steps, torch)
+    r, rg, HD = w["Wad"].shape[0], w["Wgd"].shape[0], H * D
+    NP = 3 * HD + H + r + rg
+    BT = B * T
+    gemm = 2.0 * BT * (M * NP + r * HD + rg * HD + HD * M)
+    core = alg_flops_per_chunk_head(64, D, D) * B * (T // 64) * H
+    print(json.dumps({
+        "metric": "KDA layer forward tokens/s (workload 4)", "value": BT / (ms / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "dtype": "bf16 (fp32 core)", "data": "synthetic (seeded numpy generators; random-init weights)",
+        "config": {"workload": cfg["name"], "B": B, "T": T, "M": M, "H": H, "D": D, "gate_rank": int(r),
+                   "out_gate_rank": int(rg)},
+        "gemm_tflops": gemm / (ms / 1e3) / 1e12, "core_gflop": core / 1e9,
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,6 +175,8 @@ def main():
         return
     import kimi_delta_attention_03_amd as kda
     from kimi_delta_attention_03_amd.synthetic import WORKLOADS, workload
+    if args.workload == 4:
+        return bench_layer(args, torch, kda)
 
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
