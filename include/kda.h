@@ -92,6 +92,36 @@ kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, 
                          const int32_t* cu_seqlens, void* o, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Gate activation applied inside stage 1+2 (Tokamax "chunk_kda_fwd design
+ * doc", section 9.1.3). With x = g_raw + dt_bias (per channel) and
+ * lambda = exp(A_log_h):
+ *   KDA_GATE_SOFTPLUS:             g = -lambda * softplus(x)
+ *   KDA_GATE_LOWER_BOUND_SIGMOID:  g = lower_bound * sigmoid(lambda * x)
+ * The lower-bound form keeps g in (lower_bound, 0) by construction; for the
+ * softplus form the g >= -5 precondition of the fast path becomes
+ * lambda * softplus(x) <= 5 (documented, not checked). */
+typedef enum {
+  KDA_GATE_LOG_DECAY = 0,            /* g is already the natural-log decay */
+  KDA_GATE_SOFTPLUS = 1,
+  KDA_GATE_LOWER_BOUND_SIGMOID = 2
+} kda_gate_mode;
+
+typedef struct {
+  int32_t mode;           /* kda_gate_mode */
+  float lower_bound;      /* KDA_GATE_LOWER_BOUND_SIGMOID: in [-5, 0) */
+  const float* A_log;     /* [H] fp32, device; required for modes 1 and 2 */
+  const float* dt_bias;   /* [H, K] fp32, device, or NULL (no bias) */
+} kda_gate_params;
+
+/* kda_chunk_fwd with the gate activation fused into stage 1+2: `g` holds the
+ * raw gate (dtype p->g_dtype, layout [B, T, H, K]). gate may be NULL (same as
+ * mode KDA_GATE_LOG_DECAY). Same workspace, stream and error rules. */
+kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* gate, const void* q,
+                               const void* k, const void* v, const void* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, void* o,
+                               float* final_state, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
 /* Stage 1+2 alone (Tokamax design doc section 4.1): chunk-local gate cumsum,
  * rebased Aqk / L relation tiles, (I + L)^{-1}, W, U, gated keys and queries,
  * written into the workspace (layout: kda_workspace_info). With cu_seqlens

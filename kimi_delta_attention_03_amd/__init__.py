@@ -69,7 +69,7 @@ class KdaForward:
 
     def __init__(self, q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None,
                  cu_seqlens=None, output_final_state=True, use_qk_l2norm=False, l2norm_eps=1e-6,
-                 out=None, workspace=None):
+                 out=None, workspace=None, gate_mode=None, A_log=None, dt_bias=None, gate_lower_bound=-5.0):
         torch = _torch()
         lib = _lib.load()
         if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape:
@@ -114,6 +114,20 @@ class KdaForward:
         self.final_state = (torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
                             if output_final_state else None)
         self.inputs = (q, k, v, g, beta)
+        # optional gate activation inside stage 1+2 (g then holds the raw gate)
+        if gate_mode not in _lib.GATE_MODES:
+            raise KdaValueError(1, f"unknown gate_mode {gate_mode!r}")
+        self.gate = None
+        if _lib.GATE_MODES[gate_mode]:
+            for name, t, shp in (("A_log", A_log, (H,)), ("dt_bias", dt_bias, (H, K))):
+                if t is None and name == "dt_bias":
+                    continue
+                if (t is None or not t.is_cuda or t.dtype != torch.float32 or not t.is_contiguous()
+                        or t.numel() != (H if name == "A_log" else H * K)):
+                    raise KdaValueError(1, f"{name} must be a contiguous fp32 GPU tensor of shape {shp}")
+            self.gate = _lib.KdaGateParams(_lib.GATE_MODES[gate_mode], float(gate_lower_bound),
+                                           A_log.data_ptr(), None if dt_bias is None else dt_bias.data_ptr())
+            self._gate_tensors = (A_log, dt_bias)
         self.initial_state = initial_state
         self.cu_seqlens = cu_seqlens
         self._lib = lib
@@ -134,6 +148,12 @@ class KdaForward:
 
     def __call__(self):
         q, k, v, g, beta = self.inputs
+        if self.gate is not None:
+            _lib.check(self._lib.kda_chunk_fwd_gated(
+                ctypes.byref(self.params), ctypes.byref(self.gate), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                _ptr(self.initial_state), _ptr(self.cu_seqlens), _ptr(self.o), _ptr(self.final_state),
+                _ptr(self.workspace), self.workspace.numel(), self._stream()))
+            return self.o, self.final_state
         _lib.check(self._lib.kda_chunk_fwd(
             ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.initial_state),
             _ptr(self.cu_seqlens), _ptr(self.o), _ptr(self.final_state), _ptr(self.workspace),
@@ -142,10 +162,16 @@ class KdaForward:
 
 
 def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, cu_seqlens=None,
-              output_final_state=True, use_qk_l2norm=False, l2norm_eps=1e-6):
-    """Chunkwise KDA forward on the GPU. Returns (o, final_state or None)."""
+              output_final_state=True, use_qk_l2norm=False, l2norm_eps=1e-6, gate_mode=None, A_log=None,
+              dt_bias=None, gate_lower_bound=-5.0):
+    """Chunkwise KDA forward on the GPU. Returns (o, final_state or None).
+
+    gate_mode None: g is the natural-log decay. "softplus" or
+    "lower_bound_sigmoid": g is the raw gate, activated inside stage 1+2 with
+    A_log [H] and dt_bias [H, K] (fp32, dt_bias optional)."""
     return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
-                      output_final_state, use_qk_l2norm, l2norm_eps)()
+                      output_final_state, use_qk_l2norm, l2norm_eps, gate_mode=gate_mode, A_log=A_log,
+                      dt_bias=dt_bias, gate_lower_bound=gate_lower_bound)()
 
 
 def decode_step(q, k, v, g, beta, state, scale=None, use_qk_l2norm=False, l2norm_eps=1e-6, out=None):

@@ -44,6 +44,14 @@ class KdaWorkspaceInfo(ctypes.Structure):
     ]
 
 
+class KdaGateParams(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+                ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
+
+
+GATE_MODES = {None: 0, "log_decay": 0, "softplus": 1, "lower_bound_sigmoid": 2}
+
+
 class KdaLayerParams(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int64), ("T", ctypes.c_int64),
@@ -72,6 +80,8 @@ SIGNATURES = {
     "kda_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kda_last_error": (ctypes.c_char_p, []),
     "kda_abi_version": (ctypes.c_int32, []),
+    "kda_chunk_fwd_gated": (ctypes.c_int, [_P, ctypes.POINTER(KdaGateParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "kda_decode_step": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

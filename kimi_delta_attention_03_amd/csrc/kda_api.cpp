@@ -75,8 +75,21 @@ kda_status check_common(const kda_fwd_params* p, const int32_t* cu, void* ws, si
 
 bool empty_problem(const kda_fwd_params* p) { return p->B == 0 || (p->num_seqs == 0 && p->T == 0); }
 
+kda_status check_gate(const kda_gate_params* gp) {
+  if (!gp || gp->mode == KDA_GATE_LOG_DECAY) return KDA_OK;
+  if (gp->mode != KDA_GATE_SOFTPLUS && gp->mode != KDA_GATE_LOWER_BOUND_SIGMOID)
+    return fail(KDA_ERR_INVALID_ARG, "unknown gate mode %d", gp->mode);
+  if (!gp->A_log) return fail(KDA_ERR_INVALID_ARG, "gate activation needs A_log");
+  if (!aligned(gp->A_log, 4) || (gp->dt_bias && !aligned(gp->dt_bias, 4)))
+    return fail(KDA_ERR_INVALID_ARG, "A_log and dt_bias must be 4-byte aligned");
+  if (gp->mode == KDA_GATE_LOWER_BOUND_SIGMOID && !(gp->lower_bound >= -5.f && gp->lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARG, "lower_bound must be in [-5, 0) (got %g)", (double)gp->lower_bound);
+  return KDA_OK;
+}
+
 kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
-                      const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream) {
+                      const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream,
+                      const kda_gate_params* gp = nullptr) {
   if (p->T > 0 && p->B > 0) {
     if (!q || !k || !v || !g || !beta) return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
     for (const void* t : {q, k, v, g})
@@ -100,6 +113,12 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
   a.l2norm = p->use_qk_l2norm != 0;
   a.l2eps = p->l2norm_eps;
   a.varlen = varlen;
+  if (gp && gp->mode != KDA_GATE_LOG_DECAY) {
+    a.gate_mode = gp->mode;
+    a.gate_lb = gp->lower_bound;
+    a.A_log = gp->A_log;
+    a.dt_bias = gp->dt_bias;
+  }
   a.ws = w;
   a.meta_bytes = L.meta_bytes; a.rec_bytes = L.rec_bytes; a.ncp = L.ncp;
   a.off_chunk_tab = L.off_chunk_tab;
@@ -245,6 +264,21 @@ kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k
                                     p->beta_dtype == KDA_DTYPE_F32, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
   return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* gate, const void* q, const void* k,
+                               const void* v, const void* g, const void* beta, const float* initial_state,
+                               const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  kda::Layout L;
+  kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  s = check_gate(gate);
+  if (s != KDA_OK) return s;
+  if (p->T > 0 && p->B > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream, gate);
+  if (s != KDA_OK) return s;
+  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
 }
 
 const char* kda_status_string(kda_status s) {

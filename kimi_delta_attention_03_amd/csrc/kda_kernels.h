@@ -22,6 +22,10 @@ struct Stage12Args {
   int l2norm;
   float l2eps;
   int varlen;       // 1: chunk table in the workspace metadata
+  int gate_mode;    // 0: g is the log decay; 1: softplus; 2: lower-bound sigmoid (raw gate in g)
+  float gate_lb;    // lower bound of mode 2
+  const float* A_log;    // [H] (modes 1, 2)
+  const float* dt_bias;  // [H, K] or null (modes 1, 2)
   char* ws;         // workspace base
   size_t meta_bytes, rec_bytes, ncp;
   size_t off_chunk_tab;

@@ -8,12 +8,13 @@
 //   2. P    = x Wcat^T                     rocBLAS, bf16 x bf16 -> fp32 [BT, NP]
 //   3. prologue kernel: q, k, v = SiLU(conv4(P_qkv)) (+ L2 norm for q, k),
 //      beta = sigmoid(P_b); the two low-rank slices of P rounded to bf16 (R)
-//   4. g    = R_a Wau^T                    rocBLAS -> fp32 [BT, HD]
-//   5. gate kernel: g <- lb * sigmoid(exp(A_log_h) (g + dt_bias)), in place
-//   6. core: the two-kernel chunkwise forward on fp32 q, k, v, g, beta
-//   7. Gu   = R_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in P's space)
-//   8. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in q's space)
-//   9. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
+//   4. g    = R_a Wau^T                    rocBLAS -> fp32 [BT, HD] (raw gate)
+//   5. core: the two-kernel chunkwise forward on fp32 q, k, v, beta with the
+//      decay g = lb * sigmoid(exp(A_log_h) (g_raw + dt_bias)) applied inside
+//      stage 1+2 (no separate pass over g)
+//   6. Gu   = R_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in P's space)
+//   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in q's space)
+//   8. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
 // The plain projections are library GEMMs; every other step is a kernel of
 // this file or of the core. The elementwise kernels are HBM-bound: each reads
 // its inputs once with coalesced vector loads and writes its outputs once.
@@ -139,23 +140,6 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
         a.R[row * a.nr + c] = __builtin_bit_cast(uint16_t, v);
       }
     }
-  }
-}
-
-// g <- lb * sigmoid(exp(A_log_h) * (g + dt_bias)), four channels per thread
-__global__ __launch_bounds__(kLayerThreads) void layer_gate_kernel(float* g, const float* A_log,
-                                                                   const float* dt_bias, int64_t n4, int HD, int D,
-                                                                   float lb) {
-  for (int64_t i = (int64_t)blockIdx.x * kLayerThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kLayerThreads) {
-    const int c = (int)((i * 4) % HD);
-    float4 v = reinterpret_cast<float4*>(g)[i];
-    const float4 bias = *reinterpret_cast<const float4*>(dt_bias + c);
-    const float lam = expf(A_log[c / D]);  // the 4 channels share one head (D % 4 == 0)
-    v.x = lb * sigmoidf_(lam * (v.x + bias.x));
-    v.y = lb * sigmoidf_(lam * (v.y + bias.y));
-    v.z = lb * sigmoidf_(lam * (v.z + bias.z));
-    v.w = lb * sigmoidf_(lam * (v.w + bias.w));
-    reinterpret_cast<float4*>(g)[i] = v;
   }
 }
 
@@ -368,23 +352,22 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     else hipLaunchKernelGGL(layer_prologue_kernel<64>, grid, dim3(kLayerThreads), 0, stream, a);
     if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "prologue launch failed");
   }
-  // 4. decay-gate up projection, 5. gate activation
+  // 4. decay-gate up projection (raw gate)
   s = gemm_nt(hb, w->Wau, r, R, NR, g, HD, rocblas_datatype_f32_r, HD, BT, r, "decay gate");
   if (s != KDA_OK) return s;
-  {
-    const int64_t n4 = (int64_t)BT * HD / 4;
-    const unsigned blocks = (unsigned)std::min<int64_t>((n4 + kLayerThreads - 1) / kLayerThreads, 8192);
-    hipLaunchKernelGGL(layer_gate_kernel, dim3(blocks), dim3(kLayerThreads), 0, stream, g, w->A_log, w->dt_bias, n4,
-                       HD, D, p->gate_lower_bound);
-    if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "gate launch failed");
-  }
-  // 6. the chunkwise core in fp32
+  // 5. the chunkwise core in fp32, gate activation inside stage 1+2
   {
     kda_fwd_params c = core_params(p);
-    s = kda_chunk_fwd(&c, q, k, v, g, beta, nullptr, nullptr, o, nullptr, ws + L.off_core, L.core_bytes, stream);
+    kda_gate_params gp{};
+    gp.mode = KDA_GATE_LOWER_BOUND_SIGMOID;
+    gp.lower_bound = p->gate_lower_bound;
+    gp.A_log = w->A_log;
+    gp.dt_bias = w->dt_bias;
+    s = kda_chunk_fwd_gated(&c, &gp, q, k, v, g, beta, nullptr, nullptr, o, nullptr, ws + L.off_core, L.core_bytes,
+                            stream);
     if (s != KDA_OK) return s;
   }
-  // 7. output-gate up projection into P's space, 8. RMSNorm * gate -> y (bf16, in q's space)
+  // 6. output-gate up projection into P's space, 7. RMSNorm * gate -> y (bf16, in q's space)
   float* gu = P;
   s = gemm_nt(hb, w->Wgu, rg, R + r, NR, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
   if (s != KDA_OK) return s;
@@ -401,7 +384,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
                          p->norm_eps);
     if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "norm launch failed");
   }
-  // 9. x_new = y Wo^T
+  // 8. x_new = y Wo^T
   return gemm_nt(hb, w->Wo, HD, y, HD, x_new, M, rocblas_datatype_bf16_r, M, BT, HD, "output projection");
 }
 

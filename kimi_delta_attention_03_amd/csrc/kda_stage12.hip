@@ -104,7 +104,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const void* p, int64
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, n, 0x00020000);
 }
 
-template <typename T, int K, bool GF32>
+// GATE: g holds raw gate values and phase 1 applies the activation of the
+// Tokamax "chunk_kda_fwd design doc", section 9.1.3, with x = raw + dt_bias and
+// lambda = exp(A_log_h): g = -lambda softplus(x) (mode 1) or
+// g = lower_bound * sigmoid(lambda x) (mode 2). Rows past the end of a short
+// chunk keep g = 0 (identity decay), as for pre-activated gates.
+template <typename T, int K, bool GF32, bool GATE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1)))
 void stage12_kernel(Stage12Args a) {
   constexpr int C = kChunk;
@@ -181,6 +186,8 @@ void stage12_kernel(Stage12Args a) {
     u32x4 g[RPS][GL];
     typename Raw4<T>::type q[NKB][2];
     uint32_t b;
+    float gbias[GATE ? CPT : 1];  // dt_bias of this thread's gate channels (GATE only)
+    float alog;                   // A_log of the item's head (GATE only)
   };
   // the raw inputs are loaded in three groups, each as soon as the previous
   // item has consumed its registers: k, g, beta (phase 1), q (phase 2), v (phase 5)
@@ -212,6 +219,11 @@ void stage12_kernel(Stage12Args a) {
     }
     r.b = a.beta_f32 ? __builtin_amdgcn_raw_buffer_load_b32(rb, off_b, 0, 0)
                      : (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rb, off_b, 0, 0);
+    if constexpr (GATE) {
+      r.alog = a.A_log[it.h];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) r.gbias[c] = a.dt_bias ? a.dt_bias[(size_t)it.h * K + cg * CPT + c] : 0.f;
+    }
   };
   auto issue_v = [&](RawIn& r, const Item& it) {
     const __amdgpu_buffer_rsrc_t rv = rows_rsrc(a.v, it.tok0, it.h, H, RBV, it.len);
@@ -266,6 +278,8 @@ void stage12_kernel(Stage12Args a) {
       float run[CPT];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) run[c] = 0.f;
+      float lam = 0.f;
+      if constexpr (GATE) lam = expf(R.alog);
 #pragma unroll
       for (int rr = 0; rr < RPS; ++rr) {
 #pragma unroll
@@ -274,6 +288,16 @@ void stage12_kernel(Stage12Args a) {
           if constexpr (GF32) gv = __uint_as_float(R.g[rr][c / 4][c % 4]);
           else gv = (c & 1) ? __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] & 0xffff0000u)
                             : __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] << 16);
+          if constexpr (GATE) {
+            const float x = gv + R.gbias[c];
+            if (a.gate_mode == 1) {
+              const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus
+              gv = -lam * sp;
+            } else {
+              gv = a.gate_lb / (1.f + expf(-lam * x));            // lower_bound * sigmoid
+            }
+            if (seg * RPS + rr >= it.len) gv = 0.f;
+          }
           run[c] += gv;
         }
 #pragma unroll
@@ -565,12 +589,12 @@ void stage12_kernel(Stage12Args a) {
 
 }  // namespace
 
-template <typename T, int K, bool GF32>
-static hipError_t launch12(const Stage12Args& a, int nitems, hipStream_t s) {
+template <typename T, int K, bool GF32, bool GATE>
+static hipError_t launch12g(const Stage12Args& a, int nitems, hipStream_t s) {
   static int occ = -1;  // resident workgroups per CU (same for every MI355X)
   if (occ < 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stage12_kernel<T, K, GF32>, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stage12_kernel<T, K, GF32, GATE>, kThreads, 0) != hipSuccess ||
         n < 1)
       n = 1;
     occ = n;
@@ -580,8 +604,13 @@ static hipError_t launch12(const Stage12Args& a, int nitems, hipStream_t s) {
                                                hipSuccess || cus < 1)
     cus = 256;
   const int grid = nitems < occ * cus ? nitems : occ * cus;
-  hipLaunchKernelGGL((stage12_kernel<T, K, GF32>), dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((stage12_kernel<T, K, GF32, GATE>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int K, bool GF32>
+static hipError_t launch12(const Stage12Args& a, int nitems, hipStream_t s) {
+  return a.gate_mode ? launch12g<T, K, GF32, true>(a, nitems, s) : launch12g<T, K, GF32, false>(a, nitems, s);
 }
 
 hipError_t launch_stage12(const Stage12Args& a, int K, int bf16, int nblocks, hipStream_t s) {

@@ -23,7 +23,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["round_bf16", "CoreInputs", "core_inputs", "workload", "WORKLOADS",
-           "layer_inputs", "varlen_lengths"]
+           "layer_inputs", "varlen_lengths", "gate_inputs"]
 
 
 def round_bf16(x):
@@ -139,6 +139,19 @@ def workload(i, seed=None, **over):
         raise ValueError("workload 4 is the layer; use layer_inputs()")
     return core_inputs(cfg["B"], cfg["T"], cfg["H"], cfg["K"], cfg["V"], cfg["dtype"],
                        seed=seed, init_std=cfg["init_std"])
+
+
+def gate_inputs(B, T, H, K, seed=0, a_log_range=(0.5, 1.5), bias_std=0.5, dtype="bf16", clip=(-3.0, 2.0)):
+    """Raw gate values [B, T, H, K] ~ N(0,1) clipped to `clip` (rounded to bf16
+    for dtype "bf16"), A_log = log U[a_log_range] per head and dt_bias ~
+    N(0, bias_std^2) per (head, channel) as fp32."""
+    rng = np.random.default_rng(seed)
+    raw = np.clip(rng.standard_normal((B, T, H, K), dtype=np.float32), *clip).astype(np.float32)
+    if dtype == "bf16":
+        raw = round_bf16(raw)
+    A_log = np.log(rng.uniform(*a_log_range, size=H)).astype(np.float32)
+    dt_bias = (bias_std * rng.standard_normal((H, K))).astype(np.float32)
+    return raw, A_log, dt_bias
 
 
 def layer_inputs(B=4, T=8192, M=2048, H=16, D=128, rank=128, seed=1004):

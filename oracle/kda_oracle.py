@@ -59,6 +59,7 @@ __all__ = [
     "silu",
     "sigmoid",
     "rms_norm",
+    "gate_activation",
 ]
 
 
@@ -88,6 +89,27 @@ def silu(x):
 
 def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def gate_activation(g_raw, A_log, dt_bias, mode, lower_bound=None):
+    """Log decay from a raw gate ([Tokamax] 9.1.3, gate inside the kernel).
+
+    g_raw: [B, T, H, K]; A_log: [H]; dt_bias: [H, K] (or [H*K], or None).
+    x = g_raw + dt_bias and lambda_h = exp(A_log_h); then
+      mode "softplus":            g = -lambda_h * softplus(x)
+      mode "lower_bound_sigmoid": g = lower_bound * sigmoid(lambda_h * x)
+    softplus(x) = log(1 + e^x), evaluated as logaddexp(0, x).
+    """
+    x = _f64(g_raw)
+    H, K = x.shape[-2], x.shape[-1]
+    if dt_bias is not None:
+        x = x + _f64(dt_bias).reshape(H, K)
+    lam = np.exp(_f64(A_log)).reshape(H, 1)
+    if mode == "softplus":
+        return -lam * np.logaddexp(0.0, x)
+    if mode == "lower_bound_sigmoid":
+        return float(lower_bound) * expit(lam * x)
+    raise ValueError(mode)
 
 
 def segments(B, T, cu_seqlens):

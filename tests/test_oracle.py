@@ -455,3 +455,61 @@ def test_read_before_write_is_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_exact_recall_beta_one()
     monkeypatch.setattr(orc, "kda_recurrent", orig)
+
+
+# ---------------------------------------------------------------- gate activation
+# [Tokamax] 9.1.3: x = g_raw + dt_bias, lambda_h = exp(A_log_h);
+# softplus form g = -lambda softplus(x); lower-bound form g = a sigmoid(lambda x).
+
+def _gate_case():
+    H, K = 3, 4
+    A_log = np.log(np.array([0.5, 1.0, 2.0]))            # lambda = 0.5, 1, 2
+    dt_bias = np.arange(H * K, dtype=np.float64).reshape(H, K) * 0.25 - 1.0
+    return H, K, A_log, dt_bias
+
+
+def test_gate_softplus_closed_forms():
+    H, K, A_log, dt_bias = _gate_case()
+    lam = np.exp(A_log)[:, None]
+    # raw = -dt_bias -> x = 0 -> g = -lambda ln 2 (exactly, per head)
+    g0 = orc.gate_activation(-dt_bias[None, None], A_log, dt_bias, "softplus")[0, 0]
+    assert np.allclose(g0, -lam * np.log(2.0), rtol=0, atol=1e-15)
+    # large x: softplus(x) = x + log1p(e^-x) -> g = -lambda (x + e^-x) to 1e-30
+    x = 40.0
+    g1 = orc.gate_activation((x - dt_bias)[None, None], A_log, dt_bias, "softplus")[0, 0]
+    assert np.allclose(g1, -lam * x, rtol=1e-15, atol=0)
+    # very negative x: softplus(x) ~ e^x -> g ~ -lambda e^x
+    x = -30.0
+    g2 = orc.gate_activation((x - dt_bias)[None, None], A_log, dt_bias, "softplus")[0, 0]
+    assert np.allclose(g2, -lam * np.exp(x), rtol=1e-12, atol=0)
+
+
+def test_gate_lower_bound_sigmoid_closed_forms():
+    H, K, A_log, dt_bias = _gate_case()
+    lam = np.exp(A_log)[:, None]
+    a = -5.0
+    # x = 0 -> a / 2 for every head
+    g0 = orc.gate_activation(-dt_bias[None, None], A_log, dt_bias, "lower_bound_sigmoid", a)[0, 0]
+    assert np.allclose(g0, a / 2, rtol=0, atol=1e-15)
+    # lambda x = 1 per head (x = 1 / lambda) -> a / (1 + e^-1): pins lambda = exp(A_log)
+    raw = (1.0 / lam) - dt_bias
+    g1 = orc.gate_activation(raw[None, None], A_log, dt_bias, "lower_bound_sigmoid", a)[0, 0]
+    assert np.allclose(g1, a / (1.0 + np.exp(-1.0)), rtol=1e-15, atol=0)
+    # symmetry g(x) + g(-x) = a, and the range (a, 0)
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((2, 5, H, K)) * 4
+    gp = orc.gate_activation(x - dt_bias, A_log, dt_bias, "lower_bound_sigmoid", a)
+    gm = orc.gate_activation(-x - dt_bias, A_log, dt_bias, "lower_bound_sigmoid", a)
+    assert np.allclose(gp + gm, a, rtol=0, atol=1e-14)
+    assert np.all(gp < 0) and np.all(gp > a)
+
+
+def test_gate_matches_layer_gate():
+    """The layer oracle's decay gate is the lower-bound form with lb = -5."""
+    from kimi_delta_attention_03_amd.synthetic import layer_inputs
+    x, w = layer_inputs(B=1, T=16, M=32, H=2, D=8, rank=4, seed=5)
+    H, D = 2, 8
+    pre = (x.astype(np.float64) @ w["Wad"].T.astype(np.float64)) @ w["Wau"].T.astype(np.float64)
+    _, inter = orc.kda_layer_ref(x, w, H, D, chunk_size=16)
+    g = orc.gate_activation(pre.reshape(1, 16, H, D), w["A_log"], w["dt_bias"], "lower_bound_sigmoid", -5.0)
+    assert np.allclose(g, inter["g"], rtol=1e-12, atol=1e-14)
