@@ -158,6 +158,23 @@ typedef struct {
 
 kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* info);
 
+/* Affine summary of each sequence's chunks (Tokamax "chunk_kda_fwd design
+ * doc", sections 4.2 and 9.1.8): the recurrence is affine in the state, so for
+ * every initial state S0 the final state is M S0 + N, with
+ * M = prod over chunks of (Diag(gamma) - kg^T W) and N the final state reached
+ * from S0 = 0. Reads a workspace filled by kda_chunk_fwd_stage12 with the same
+ * parameters; writes M [N_seq, H, K, K] and N [N_seq, H, K, V] fp32 (N_seq = B
+ * or num_seqs). This is the per-rank building block of context parallelism
+ * along T. Requires K == V. */
+kda_status kda_chunk_affine_summary(const kda_fwd_params* p, const int32_t* cu_seqlens, float* M, float* N,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Merge step: S_out = M S0 + N for every (sequence, head), fp32, shapes as
+ * above (S0 and S_out [N_seq, H, K, V]); S_out must not alias S0 or M. Uses
+ * B (or num_seqs), H, K, V of p only. */
+kda_status kda_affine_apply(const kda_fwd_params* p, const float* M, const float* N, const float* S0, float* S_out,
+                            hipStream_t stream);
+
 /* One decode step of the token recurrence for B independent sequences
  * ("KDA Doesn't Care About the Future", section "Chunkwise KDA in Broad
  * Strokes", steps (0)-(5); Tokamax "chunk_kda_fwd design doc" section 9.1.2,

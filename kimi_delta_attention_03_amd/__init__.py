@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
 __all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
-           "KdaLayer", "layer_fwd", "decode_step"]
+           "KdaLayer", "layer_fwd", "decode_step", "affine_summary", "affine_apply"]
 
 
 def _torch():
@@ -172,6 +172,41 @@ def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, c
     return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
                       output_final_state, use_qk_l2norm, l2norm_eps, gate_mode=gate_mode, A_log=A_log,
                       dt_bias=dt_bias, gate_lower_bound=gate_lower_bound)()
+
+
+def affine_summary(q, k, v, g, beta, scale=None, cu_seqlens=None, use_qk_l2norm=False, l2norm_eps=1e-6,
+                   **gate):
+    """Affine summary (M, N) of each sequence (include/kda.h, kda_chunk_affine_summary):
+    for any initial state S0 the final state is M @ S0 + N. Runs stage 1+2 on
+    the inputs, then the summary; returns fp32 M [N, H, K, K] and N [N, H, K, V]."""
+    torch = _torch()
+    f = KdaForward(q, k, v, g, beta, scale, cu_seqlens=cu_seqlens, output_final_state=False,
+                   use_qk_l2norm=use_qk_l2norm, l2norm_eps=l2norm_eps, **gate)
+    if f.gate is not None:
+        raise KdaValueError(1, "affine_summary takes the activated log decay g (no gate_mode)")
+    f.stage12()
+    p = f.params
+    N = p.num_seqs if p.num_seqs else p.B
+    M = torch.empty((N, p.H, p.K, p.K), dtype=torch.float32, device=q.device)
+    Nst = torch.empty((N, p.H, p.K, p.V), dtype=torch.float32, device=q.device)
+    _lib.check(f._lib.kda_chunk_affine_summary(ctypes.byref(p), _ptr(cu_seqlens), _ptr(M), _ptr(Nst),
+                                               _ptr(f.workspace), f.workspace.numel(), f._stream()))
+    return M, Nst
+
+
+def affine_apply(M, N, S0, out=None):
+    """S = M @ S0 + N per (sequence, head) on the GPU (include/kda.h, kda_affine_apply)."""
+    torch = _torch()
+    lib = _lib.load()
+    n, H, K, V = N.shape
+    for t, shp in ((M, (n, H, K, K)), (S0, (n, H, K, V))):
+        if tuple(t.shape) != shp or t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous():
+            raise KdaValueError(1, f"expected contiguous fp32 GPU tensor of shape {shp}")
+    out = out if out is not None else torch.empty_like(S0)
+    p = make_params(n, 1, H, K, V, _lib.KDA_DTYPE_F32, _lib.KDA_DTYPE_F32, _lib.KDA_DTYPE_F32, 1.0)
+    _lib.check(lib.kda_affine_apply(ctypes.byref(p), _ptr(M), _ptr(N), _ptr(S0), _ptr(out),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    return out
 
 
 def decode_step(q, k, v, g, beta, state, scale=None, use_qk_l2norm=False, l2norm_eps=1e-6, out=None):

@@ -82,6 +82,8 @@ SIGNATURES = {
     "kda_abi_version": (ctypes.c_int32, []),
     "kda_chunk_fwd_gated": (ctypes.c_int, [_P, ctypes.POINTER(KdaGateParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_chunk_affine_summary": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_affine_apply": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp]),
     "kda_decode_step": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),

@@ -132,10 +132,10 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
 }
 
 kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float* fin, void* ws,
-                      const kda::Layout& L, hipStream_t stream) {
+                      const kda::Layout& L, hipStream_t stream, int affine_linear = 0) {
   const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
   if (nseq == 0) return KDA_OK;
-  if (p->T > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  if (p->T > 0 && !o && !fin) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
   if (o && !aligned(o, 16)) return fail(KDA_ERR_INVALID_ARG, "o must be 16-byte aligned");
   if ((init && !aligned(init, 16)) || (fin && !aligned(fin, 16)))
     return fail(KDA_ERR_INVALID_ARG, "states must be 16-byte aligned");
@@ -143,6 +143,8 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   a.init = init;
   a.final_state = fin;
   a.o = o;
+  a.init_identity = affine_linear;
+  a.zero_u = affine_linear;
   a.H = (int)p->H;
   const int64_t nunits = nseq * p->H;
   if (nunits > INT32_MAX / 16) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
@@ -279,6 +281,37 @@ kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* g
   s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream, gate);
   if (s != KDA_OK) return s;
   return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+}
+
+kda_status kda_chunk_affine_summary(const kda_fwd_params* p, const int32_t* cu_seqlens, float* M, float* N,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda::Layout L;
+  kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  if (!M || !N) return fail(KDA_ERR_INVALID_ARG, "M and N must be non-NULL");
+  if (!aligned(M, 16) || !aligned(N, 16)) return fail(KDA_ERR_INVALID_ARG, "M and N must be 16-byte aligned");
+  // N: the state reached from a zero start; M: the recurrence run on an identity
+  // start with U taken as zero (the linear part). No output is written.
+  s = do_stage34(p, nullptr, nullptr, N, workspace, L, stream, 0);
+  if (s != KDA_OK) return s;
+  return do_stage34(p, nullptr, nullptr, M, workspace, L, stream, 1);
+}
+
+kda_status kda_affine_apply(const kda_fwd_params* p, const float* M, const float* N, const float* S0, float* S_out,
+                            hipStream_t stream) {
+  g_msg[0] = 0;
+  if (!p) return fail(KDA_ERR_INVALID_ARG, "params is NULL");
+  if (p->H <= 0 || p->B < 0 || p->num_seqs < 0) return fail(KDA_ERR_INVALID_ARG, "bad B, H or num_seqs");
+  if (!(p->K == p->V && (p->K == 64 || p->K == 128)))
+    return fail(KDA_ERR_UNSUPPORTED, "GPU path supports K == V in {64, 128} (got K=%d V=%d)", p->K, p->V);
+  const int64_t nunits = (p->num_seqs > 0 ? p->num_seqs : p->B) * p->H;
+  if (nunits == 0) return KDA_OK;
+  if (nunits > INT32_MAX / 4) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  if (!M || !N || !S0 || !S_out) return fail(KDA_ERR_INVALID_ARG, "M, N, S0 and S_out must be non-NULL");
+  if (S_out == S0 || S_out == M) return fail(KDA_ERR_INVALID_ARG, "S_out must not alias S0 or M");
+  hipError_t e = kda::launch_affine_apply(M, N, S0, S_out, (int)nunits, p->K, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "affine apply launch: %s", hipGetErrorString(e));
+  return KDA_OK;
 }
 
 const char* kda_status_string(kda_status s) {

@@ -35,7 +35,9 @@ struct Stage12Args {
 struct Stage34Args {
   const float* init;   // [N, H, K, V] or null
   float* final_state;  // [N, H, K, V] or null
-  void* o;
+  void* o;             // or null: no output (affine summaries)
+  int init_identity;   // 1: the state starts at the identity (K == V)
+  int zero_u;          // 1: U is taken as zero (the linear part of the affine map)
   int H;
   int nunits;          // N * H
   int nt;              // fixed length: chunks per batch row
@@ -67,6 +69,9 @@ hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, s
                              size_t off_chunk_tab, size_t off_seq_tab, size_t off_order,
                              hipStream_t s);
 
+// S_out = M S0 + N for each of nunits (sequence, head) pairs, K == V
+hipError_t launch_affine_apply(const float* M, const float* N, const float* S0, float* S_out, int nunits, int K,
+                               hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int K, int bf16_qkv, int g_f32, int b_f32, hipStream_t s);
 
 // sets the thread-local message returned by kda_last_error and returns s

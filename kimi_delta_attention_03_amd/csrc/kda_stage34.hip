@@ -184,8 +184,11 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
     for (int m = 0; m < TPW; ++m) {
       const int rt = s * TPW + m;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        S[m][r] = a.init ? a.init[state_base + (size_t)(16 * rt + 4 * gq + r) * V] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        // identity start: state row 16 rt + 4 gq + r, column 16 vb + xi
+        const float id = (16 * rt + 4 * gq + r == 16 * vb + xi) ? 1.f : 0.f;
+        S[m][r] = a.init_identity ? id : a.init ? a.init[state_base + (size_t)(16 * rt + 4 * gq + r) * V] : 0.f;
+      }
       F4 y;
       cvt4(S[m], y);
       sS[rt][lane] = y;
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
           Sb[kb] = stack8<T>(sS[2 * kb][lane], sS[2 * kb + 1][lane]);
           accV = mma32(accV, f.w[kb], Sb[kb]);
         }
-        const floatx4 vn = widen4(f.u) - accV;
+        const floatx4 vn = (a.zero_u ? zero4() : widen4(f.u)) - accV;
         F4 vnT;
         cvt4(vn, vnT);
         sVn[r0][lane] = vnT;
@@ -303,7 +306,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
       const int row = 16 * r0 + xi;
       F4 y;
       cvt4(accO, y);
-      T* dst = row < len ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
+      T* dst = (row < len && out) ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
       *reinterpret_cast<F4*>(dst) = y;
     };
     // whole ring passes with a single exit (see the state waves)
@@ -315,7 +318,39 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   }
 }
 
+// S_out[:, j] = M S0[:, j] + N[:, j]; block = (pair u, 64 columns), wave w
+// handles rows w, w + 4, ...; each lane keeps its column of S0 in registers.
+template <int K>
+__global__ __launch_bounds__(256) void affine_apply_kernel(const float* M, const float* N, const float* S0,
+                                                            float* S_out) {
+  constexpr int V = K;
+  constexpr int NCB = V / 64;
+  const int u = blockIdx.x / NCB;
+  const int j = (blockIdx.x % NCB) * 64 + (threadIdx.x & 63);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const size_t base = (size_t)u * K * V;
+  float s0[K];
+#pragma unroll
+  for (int l = 0; l < K; ++l) s0[l] = S0[base + (size_t)l * V + j];
+  for (int i = w; i < K; i += 4) {
+    const float* mrow = M + (size_t)u * K * K + (size_t)i * K;
+    float acc = N[base + (size_t)i * V + j];
+#pragma unroll
+    for (int l = 0; l < K; ++l) acc += mrow[l] * s0[l];
+    S_out[base + (size_t)i * V + j] = acc;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_affine_apply(const float* M, const float* N, const float* S0, float* S_out, int nunits, int K,
+                               hipStream_t s) {
+  if (nunits <= 0) return hipSuccess;
+  const dim3 grid((unsigned)(nunits * (K / 64))), block(256);
+  if (K == 128) hipLaunchKernelGGL(affine_apply_kernel<128>, grid, block, 0, s, M, N, S0, S_out);
+  else hipLaunchKernelGGL(affine_apply_kernel<64>, grid, block, 0, s, M, N, S0, S_out);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s) {
   if (a.nunits <= 0) return hipSuccess;
