@@ -118,6 +118,66 @@ def cpu_baseline(x, target_s=15.0):
     }
 
 
+def bench_decode(args, torch, kda):
+    """One decode step for B sequences: the state (fp32 [B, H, K, V]) is read
+    and written once; q, k, g (K each), v, o (V each) and beta per (sequence,
+    head) are read or written once -> 8 K V + 2 (3 K + 2 V) + 2 bytes per head."""
+    B, H, K = 256, 32, 128
+    from kimi_delta_attention_03_amd.synthetic import core_inputs
+    x = core_inputs(B, 1, H, K, K, dtype="bf16", seed=1101, init_std=0.1)
+    dev = "cuda:0"
+    sl = lambda a: torch.from_numpy(a[:, 0].copy()).to(torch.bfloat16).to(dev)
+    q, k, v, g, beta = (sl(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    st = torch.from_numpy(x.initial_state).to(dev)
+    o = torch.empty((B, H, K), dtype=torch.bfloat16, device=dev)
+    step = lambda: kda.decode_step(q, k, v, g, beta, st, scale=x.scale, out=o)
+    for _ in range(args.warmup):
+        step()
+    ms = time_loop(step, args.steps, torch)
+    nbytes = B * H * (8 * K * K + 2 * (3 * K + 2 * K) + 2)
+    gbps = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "KDA decode step tokens/s (one token per sequence)", "value": B / (ms / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "dtype": "bf16 (fp32 state)", "data": "synthetic (seeded numpy generators)",
+        "config": {"workload": f"decode_bf16_B{B}_H{H}_K{K}", "B": B, "H": H, "K": K, "V": K},
+        "roofline": {"kernel": "decode", "bound": "hbm", "achieved": gbps, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": gbps * 1e9 / PEAK_HBM, "traffic": None, "alg_bytes_per_launch": nbytes},
+    }), flush=True)
+
+
+def bench_affine(args, torch, kda, WORKLOADS, workload):
+    """Affine summaries of a core workload: stage 1+2, then two stage-3+4
+    passes (zero start -> N, identity start -> M) that each read every record
+    (1128 B per token-head at K=V=128 bf16) and write their K x V states."""
+    x = workload(args.workload)
+    dev = "cuda:0"
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    to = lambda a: torch.from_numpy(a).to(dt).to(dev)
+    q, k, v, g, beta = (to(a) for a in (x.q, x.k, x.v, x.g, x.beta))
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens.astype(np.int32)).to(dev)
+    run = lambda: kda.affine_summary(q, k, v, g, beta, scale=x.scale, cu_seqlens=cu)
+    for _ in range(args.warmup):
+        run()
+    ms = time_loop(run, args.steps, torch)
+    B, T, H, K = x.q.shape
+    elem = 2 if x.dtype == "bf16" else 4
+    b12, b34 = alg_bytes_per_token_head(K, K, elem, elem, elem)
+    rec = b34 - K * elem
+    nseq = B if cu is None else len(x.cu_seqlens) - 1
+    nbytes = B * T * H * (b12 + 2 * rec) + 2 * nseq * H * K * K * 4
+    gbps = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "KDA affine chunk summaries tokens/s", "value": B * T / (ms / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "dtype": x.dtype, "data": "synthetic (seeded numpy generators)",
+        "config": {"workload": WORKLOADS[args.workload]["name"], "B": B, "T": T, "H": H, "K": K, "V": K},
+        "roofline": {"kernel": "stage12 + 2 x stage34 (summary)", "bound": "hbm", "achieved": gbps,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbps * 1e9 / PEAK_HBM, "traffic": None,
+                     "alg_bytes_per_launch": nbytes},
+    }), flush=True)
+
+
 def bench_layer(args, torch, kda):
     """The KDA layer around the core (workload 4): one step = the whole layer
     forward over a [B, T, M] bf16 input, inputs and weights resident in HBM."""
@@ -144,6 +204,9 @@ def bench_layer(args, torch, kda):
         "config": {"workload": cfg["name"], "B": B, "T": T, "M": M, "H": H, "D": D, "gate_rank": int(r),
                    "out_gate_rank": int(rg)},
         "gemm_tflops": gemm / (ms / 1e3) / 1e12, "core_gflop": core / 1e9,
+        "roofline": {"kernel": "whole layer (projection FLOPs over the step)", "bound": "mfma",
+                     "achieved": gemm / (ms / 1e3) / 1e12, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                     "frac": gemm / (ms / 1e3) / PEAK_BF16, "traffic": None},
     }), flush=True)
 
 
@@ -153,6 +216,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--mode", choices=["forward", "decode", "affine"], default="forward",
+                    help="decode: one kda_decode_step over B=256 sequences x H=32 (K=V=128, bf16); "
+                         "affine: stage 1+2 plus the affine summaries on the workload's shape")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -177,6 +243,10 @@ def main():
     from kimi_delta_attention_03_amd.synthetic import WORKLOADS, workload
     if args.workload == 4:
         return bench_layer(args, torch, kda)
+    if args.mode == "decode":
+        return bench_decode(args, torch, kda)
+    if args.mode == "affine":
+        return bench_affine(args, torch, kda, WORKLOADS, workload)
 
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
