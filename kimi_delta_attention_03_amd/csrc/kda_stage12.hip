@@ -128,7 +128,7 @@ void stage12_kernel(Stage12Args a) {
   constexpr int RPS = C / SEG;         // rows per segment
   constexpr int GB = CPT * (GF32 ? 4 : 2);       // gate bytes per thread and row
   constexpr int GL = GB / 16 > 0 ? GB / 16 : 1;  // 16-byte gate loads per row (8-byte if GB == 8)
-  constexpr bool kPrefetch = (E == 2);  // fp32 lacks the registers: load at item start
+  constexpr bool kPrefetch = true;      // fp32 runs one wave per SIMD and has the registers too
   static_assert(NCH * kThreads == C * CPR, "tile split");
   static_assert(kThreads % CPR == 0, "rows per step");
 
