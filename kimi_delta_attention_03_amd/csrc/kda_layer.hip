@@ -4,15 +4,16 @@
 // gate of the Tokamax "chunk_kda_fwd design doc", section 9.1.3).
 //
 // Order of work on the caller's stream (BT = B * T tokens, HD = H * D):
-//   1. Wcat = [Wqkv; Wb; Wad; Wgd] (device copies, rows of width M)
-//   2. P    = x Wcat^T                     rocBLAS, bf16 x bf16 -> fp32 [BT, NP]
-//   3. prologue kernel: q, k, v = SiLU(conv4(P_qkv)) (+ L2 norm for q, k),
-//      beta = sigmoid(P_b); the two low-rank slices of P rounded to bf16 (R)
-//   4. g    = R_a Wau^T                    rocBLAS -> fp32 [BT, HD] (raw gate)
+//   1. Wcat = [Wqkv; Wad; Wgd; Wb] (device copies, rows of width M): the
+//      low-rank slices of P start at 16-byte aligned columns
+//   2. P    = x Wcat^T                     rocBLAS, bf16 x bf16 (fp32 accumulation) -> bf16 [BT, NP]
+//   3. prologue kernel: q, k, v = SiLU(conv4(P_qkv)) (+ L2 norm for q, k) in
+//      fp32, beta = sigmoid(P_b)
+//   4. g    = P_a Wau^T                    rocBLAS -> fp32 [BT, HD] (raw gate; P_a read in place)
 //   5. core: the two-kernel chunkwise forward on fp32 q, k, v, beta with the
 //      decay g = lb * sigmoid(exp(A_log_h) (g_raw + dt_bias)) applied inside
 //      stage 1+2 (no separate pass over g)
-//   6. Gu   = R_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in P's space)
+//   6. Gu   = P_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in k's space)
 //   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in q's space)
 //   8. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
 // The plain projections are library GEMMs; every other step is a kernel of
@@ -38,6 +39,7 @@ constexpr int kLayerThreads = 256;
 constexpr int kTile = 64;  // tokens per prologue wave
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, kWave);
@@ -45,15 +47,14 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 struct PrologueArgs {
-  const float* P;      // [BT, ldp]
+  const uint16_t* P;   // [BT, ldp] bf16 bits
   int64_t ldp;
   const float* conv[3];
   float* out[3];       // q, k, v [BT, HD]
   float* beta;         // [BT, H]
-  uint16_t* R;         // [BT, nr] bf16 bits: the low-rank slices
   int64_t T;           // tokens per batch row
   int H, nt;           // heads, 64-token tiles per row
-  int off_b, off_r, nr;
+  int off_b;
   float l2eps;
   int64_t nwaves;      // B * nt * H * 3
 };
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
   const int HD = a.H * D;
   const int c0 = h * D + CPL * lane;
   const int64_t row0 = b * a.T + (int64_t)tile * kTile;  // first token row of the tile
-  const float* src = a.P + s * HD + c0;
+  const uint16_t* src = a.P + s * HD + c0;
   float wgt[CPL][4];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
   for (int m = 0; m < 3; ++m) {
     const int64_t t = (int64_t)tile * kTile - 3 + m;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) win[j][m] = t >= 0 ? src[(row0 - 3 + m) * a.ldp + j] : 0.f;
+    for (int j = 0; j < CPL; ++j) win[j][m] = t >= 0 ? bf16f(src[(row0 - 3 + m) * a.ldp + j]) : 0.f;
   }
   float* dst = a.out[s] + c0;
   for (int tb = 0; tb < kTile; tb += 8) {
@@ -97,10 +98,11 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       if constexpr (CPL == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(src + (row0 + tb + i) * a.ldp);
-        xin[i][0] = v.x; xin[i][1] = v.y;
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(src + (row0 + tb + i) * a.ldp);
+        xin[i][0] = __uint_as_float(v << 16);
+        xin[i][1] = __uint_as_float(v & 0xffff0000u);
       } else {
-        xin[i][0] = src[(row0 + tb + i) * a.ldp];
+        xin[i][0] = bf16f(src[(row0 + tb + i) * a.ldp]);
       }
     }
 #pragma unroll
@@ -129,17 +131,7 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
   if (s == 0) {
     // beta of the tile's 64 tokens for this head, one token per lane
     const int64_t row = row0 + lane;
-    a.beta[row * a.H + h] = sigmoidf_(a.P[row * a.ldp + a.off_b + h]);
-  }
-  if (s == 1 && h == 0) {
-    // low-rank slices of the tile, rounded to bf16 (round to nearest even)
-    for (int i = 0; i < kTile; ++i) {
-      const int64_t row = row0 + i;
-      for (int c = lane; c < a.nr; c += kWave) {
-        const __bf16 v = (__bf16)a.P[row * a.ldp + a.off_r + c];
-        a.R[row * a.nr + c] = __builtin_bit_cast(uint16_t, v);
-      }
-    }
+    a.beta[row * a.H + h] = sigmoidf_(bf16f(a.P[row * a.ldp + a.off_b + h]));
   }
 }
 
@@ -177,8 +169,8 @@ __global__ __launch_bounds__(kLayerThreads) void layer_norm_gate_kernel(const fl
 
 struct LayerLayout {
   int64_t BT;
-  int HD, NP, NR;
-  size_t off_wcat, off_P, off_R, off_q, off_k, off_v, off_g, off_beta, off_o, off_core, total;
+  int HD, NP;
+  size_t off_wcat, off_P, off_q, off_k, off_v, off_g, off_beta, off_o, off_core, total;
   size_t core_bytes;
 };
 
@@ -210,8 +202,8 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
     return fail_msg(KDA_ERR_INVALID_ARG, "gate_lower_bound must be in [-5, 0) (the core's decay range)");
   L->BT = p->B * p->T;
   L->HD = p->H * p->D;
-  L->NP = 3 * L->HD + p->H + p->gate_rank + p->out_gate_rank;
-  L->NR = p->gate_rank + p->out_gate_rank;
+  // P's row stride, padded to 8 columns so that every row starts 16-byte aligned
+  L->NP = (int)((3 * (int64_t)L->HD + p->H + p->gate_rank + p->out_gate_rank + 7) / 8 * 8);
   if (L->BT > INT32_MAX / 2 || (int64_t)L->NP * p->M > INT32_MAX || (int64_t)L->HD > 65536)
     return fail_msg(KDA_ERR_UNSUPPORTED, "layer too large for 32-bit GEMM sizes");
   kda_fwd_params c = core_params(p);
@@ -223,10 +215,9 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
   size_t off = 0;
   auto take = [&](size_t bytes) { const size_t o = off; off = up256(off + bytes); return o; };
   L->off_wcat = take((size_t)L->NP * p->M * 2);
-  L->off_P = take(BT * L->NP * 4);        // later the output-gate projection [BT, HD] fp32
-  L->off_R = take(BT * L->NR * 2);
+  L->off_P = take(BT * L->NP * 2);        // bf16
   L->off_q = take(BT * HD * 4);           // later y (bf16)
-  L->off_k = take(BT * HD * 4);
+  L->off_k = take(BT * HD * 4);           // later the output-gate projection [BT, HD] fp32
   L->off_v = take(BT * HD * 4);
   L->off_g = take(BT * HD * 4);
   L->off_beta = take(BT * p->H * 4);
@@ -308,12 +299,12 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
   if (rocblas_set_stream(hb, stream) != rocblas_status_success) return fail_msg(KDA_ERR_HIP, "rocblas_set_stream failed");
 
   char* ws = static_cast<char*>(workspace);
-  const int M = p->M, H = p->H, D = p->D, HD = L.HD, NP = L.NP, NR = L.NR;
+  const int M = p->M, H = p->H, D = p->D, HD = L.HD, NP = L.NP;
   const int BT = (int)L.BT;
   const int r = p->gate_rank, rg = p->out_gate_rank;
   uint16_t* wcat = reinterpret_cast<uint16_t*>(ws + L.off_wcat);
-  float* P = reinterpret_cast<float*>(ws + L.off_P);
-  uint16_t* R = reinterpret_cast<uint16_t*>(ws + L.off_R);
+  uint16_t* P = reinterpret_cast<uint16_t*>(ws + L.off_P);
+  const int off_r = 3 * HD;      // column of the first low-rank activation in P
   float* q = reinterpret_cast<float*>(ws + L.off_q);
   float* k = reinterpret_cast<float*>(ws + L.off_k);
   float* v = reinterpret_cast<float*>(ws + L.off_v);
@@ -325,7 +316,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
   const size_t rowb = (size_t)M * 2;
   size_t at = 0;
   const struct { const void* src; size_t rows; } parts[] = {
-      {w->Wqkv, (size_t)3 * HD}, {w->Wb, (size_t)H}, {w->Wad, (size_t)r}, {w->Wgd, (size_t)rg}};
+      {w->Wqkv, (size_t)3 * HD}, {w->Wad, (size_t)r}, {w->Wgd, (size_t)rg}, {w->Wb, (size_t)H}};
   for (const auto& pt : parts) {
     if (hipMemcpyAsync(reinterpret_cast<char*>(wcat) + at, pt.src, pt.rows * rowb, hipMemcpyDeviceToDevice, stream) !=
         hipSuccess)
@@ -333,7 +324,8 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     at += pt.rows * rowb;
   }
   // 2. P = x Wcat^T
-  s = gemm_nt(hb, wcat, M, x, M, P, NP, rocblas_datatype_f32_r, NP, BT, M, "input projections");
+  const int NW = 3 * HD + r + rg + H;  // rows of Wcat (columns of P in use)
+  s = gemm_nt(hb, wcat, M, x, M, P, NP, rocblas_datatype_bf16_r, NW, BT, M, "input projections");
   if (s != KDA_OK) return s;
   // 3. prologue
   {
@@ -341,9 +333,9 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     a.P = P; a.ldp = NP;
     a.conv[0] = w->conv_q; a.conv[1] = w->conv_k; a.conv[2] = w->conv_v;
     a.out[0] = q; a.out[1] = k; a.out[2] = v;
-    a.beta = beta; a.R = R;
+    a.beta = beta;
     a.T = p->T; a.H = H; a.nt = (int)(p->T / kTile);
-    a.off_b = 3 * HD; a.off_r = 3 * HD + H; a.nr = NR;
+    a.off_b = 3 * HD + r + rg;
     a.l2eps = p->l2_eps;
     a.nwaves = p->B * a.nt * (int64_t)H * 3;
     const int wpb = kLayerThreads / kWave;
@@ -353,7 +345,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "prologue launch failed");
   }
   // 4. decay-gate up projection (raw gate)
-  s = gemm_nt(hb, w->Wau, r, R, NR, g, HD, rocblas_datatype_f32_r, HD, BT, r, "decay gate");
+  s = gemm_nt(hb, w->Wau, r, P + off_r, NP, g, HD, rocblas_datatype_f32_r, HD, BT, r, "decay gate");
   if (s != KDA_OK) return s;
   // 5. the chunkwise core in fp32, gate activation inside stage 1+2
   {
@@ -367,9 +359,10 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
                             stream);
     if (s != KDA_OK) return s;
   }
-  // 6. output-gate up projection into P's space, 7. RMSNorm * gate -> y (bf16, in q's space)
-  float* gu = P;
-  s = gemm_nt(hb, w->Wgu, rg, R + r, NR, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
+  // 6. output-gate up projection into k's space (k is dead after the core),
+  // 7. RMSNorm * gate -> y (bf16, in q's space)
+  float* gu = k;
+  s = gemm_nt(hb, w->Wgu, rg, P + off_r + r, NP, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
   if (s != KDA_OK) return s;
   uint16_t* y = reinterpret_cast<uint16_t*>(q);
   {

@@ -155,13 +155,13 @@ def test_layer_workspace_formula(lib):
     p = LP()
     n = ctypes.c_size_t(0)
     assert lib.kda_layer_fwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
-    BT, HD, NP, NR = 256, 256, 3 * 256 + 2 + 32 + 128, 32 + 128
+    BT, HD = 256, 256
+    NP = (3 * 256 + 2 + 32 + 128 + 7) // 8 * 8
     up = lambda x: (x + 255) // 256 * 256
     core = make_params(2, 128, 2, 128, 128, 0, 0, 0, 128 ** -0.5)
     cb = ctypes.c_size_t(0)
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(core), ctypes.byref(cb)) == 0
-    want = (up(NP * 256 * 2) + up(BT * NP * 4) + up(BT * NR * 2) + 5 * up(BT * HD * 4)
-            + up(BT * 2 * 4) + up(cb.value))
+    want = (up(NP * 256 * 2) + up(BT * NP * 2) + 5 * up(BT * HD * 4) + up(BT * 2 * 4) + up(cb.value))
     assert n.value == want
 
 
