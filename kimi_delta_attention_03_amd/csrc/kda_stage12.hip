@@ -25,6 +25,8 @@
 // Inputs are read with buffer loads whose descriptor covers exactly the valid
 // rows of the chunk: rows past the end of a short (variable-length) chunk read
 // as zeros, so no load sits behind a branch.
+#include <atomic>
+
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -591,13 +593,17 @@ void stage12_kernel(Stage12Args a) {
 
 template <typename T, int K, bool GF32, bool GATE>
 static hipError_t launch12g(const Stage12Args& a, int nitems, hipStream_t s) {
-  static int occ = -1;  // resident workgroups per CU (same for every MI355X)
+  // resident workgroups per CU (the same for every MI355X), computed once;
+  // concurrent first calls compute the same value
+  static std::atomic<int> occ_cache{-1};
+  int occ = occ_cache.load(std::memory_order_relaxed);
   if (occ < 0) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, stage12_kernel<T, K, GF32, GATE>, kThreads, 0) != hipSuccess ||
         n < 1)
       n = 1;
     occ = n;
+    occ_cache.store(n, std::memory_order_relaxed);
   }
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
