@@ -34,6 +34,9 @@ Parity status:
   kda_recurrent, kda_chunkwise, varlen handling, l2norm,
   chunk_affine_summary     -> pinned (closed forms, invariants, exact recall,
                               brute force and cross-checks in tests/).
+  kda_recurrent_vjp        -> pinned (central finite differences of
+                              kda_recurrent, the beta = 0 closed form and
+                              the varlen / l2norm cases in tests/).
   kda_layer_ref            -> partly pinned: its convolution is pinned against
                               numpy.convolve, its norm and gate by their
                               defining properties, and causality end to end;
@@ -60,6 +63,7 @@ __all__ = [
     "sigmoid",
     "rms_norm",
     "gate_activation",
+    "kda_recurrent_vjp",
 ]
 
 
@@ -365,6 +369,63 @@ def compose_affine(first, second):
     Pa, Sa = first
     Pb, Sb = second
     return Pb @ Pa, Pb @ Sa + Sb
+
+
+# --------------------------------------------------------------------------
+# Backward: the vector-Jacobian product of the token recurrence ([Tokamax]
+# 4.3.4 and 6.1: the backward returns dq, dk, dv, dg, dbeta and the optional
+# dh0 of the same forward map (O, S_final) = F(Q, K, V, G, D_beta, S_0))
+# --------------------------------------------------------------------------
+def kda_recurrent_vjp(q, k, v, g, beta, scale, d_o, d_final=None, initial_state=None,
+                      cu_seqlens=None, use_qk_l2norm=False, eps=1e-6):
+    """Gradients of <d_o, o> + <d_final, final_state> for kda_recurrent.
+
+    The forward is the same token recurrence (decay, prediction error, delta
+    write, read after the write), restated with torch float64 CPU tensors so
+    that reverse-mode differentiation (torch.autograd, a library routine)
+    gives the exact vector-Jacobian product. With use_qk_l2norm the gradients
+    are those of the un-normalised q and k. Returns a dict with dq, dk, dv,
+    dg, dbeta (shapes of the inputs) and dh0 ([N, H, K, V]), float64 numpy.
+    """
+    import torch
+
+    def leaf(a):
+        return torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+
+    qt, kt, vt, gt, bt = (leaf(a) for a in (q, k, v, g, beta))
+    B, T, H, K = qt.shape
+    V = vt.shape[-1]
+    segs = segments(B, T, cu_seqlens)
+    h0 = leaf(np.zeros((len(segs), H, K, V)) if initial_state is None else initial_state)
+    qn, kn = qt, kt
+    if use_qk_l2norm:
+        qn = qt / torch.clamp(torch.sqrt((qt * qt).sum(-1, keepdim=True)), min=eps)
+        kn = kt / torch.clamp(torch.sqrt((kt * kt).sum(-1, keepdim=True)), min=eps)
+    outs = [[None] * T for _ in range(B)]
+    finals = []
+    for n, (b, s0, s1) in enumerate(segs):
+        S = h0[n]
+        for t in range(s0, s1):
+            S_bar = torch.exp(gt[b, t])[:, :, None] * S
+            e = vt[b, t] - torch.einsum("hkv,hk->hv", S_bar, kn[b, t])
+            S = S_bar + bt[b, t][:, None, None] * kn[b, t][:, :, None] * e[:, None, :]
+            outs[b][t] = scale * torch.einsum("hkv,hk->hv", S, qn[b, t])
+        finals.append(S)
+    zero_row = torch.zeros((H, V), dtype=torch.float64)
+    o = torch.stack([torch.stack([r if r is not None else zero_row for r in row]) for row in outs]) \
+        if T > 0 else torch.zeros((B, 0, H, V), dtype=torch.float64)
+    loss = (o * torch.as_tensor(np.asarray(d_o, dtype=np.float64))).sum()
+    if d_final is not None and finals:
+        fin = torch.stack(finals)
+        loss = loss + (fin * torch.as_tensor(np.asarray(d_final, dtype=np.float64))).sum()
+    leaves = (qt, kt, vt, gt, bt, h0)
+    if loss.requires_grad:
+        grads = torch.autograd.grad(loss, leaves, allow_unused=True)
+    else:
+        grads = (None,) * len(leaves)
+    names = ("dq", "dk", "dv", "dg", "dbeta", "dh0")
+    return {nm: (np.zeros(lf.shape) if gr is None else gr.detach().numpy())
+            for nm, lf, gr in zip(names, leaves, grads)}
 
 
 # --------------------------------------------------------------------------
