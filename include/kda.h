@@ -188,6 +188,31 @@ kda_status kda_affine_apply(const kda_fwd_params* p, const float* M, const float
 kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k, const void* v,
                            const void* g, const void* beta, float* state, void* o, hipStream_t stream);
 
+/* Backward of kda_chunk_fwd: the gradients of <d_o, o> + <d_final_state, final_state>
+ * with respect to q, k, v, g, beta and initial_state (Tokamax "chunk_kda_fwd design doc",
+ * sections 4.3.4 and 6.1: the backward returns dq, dk, dv, dg, dbeta and the optional dh0
+ * of the same forward map, rebuilding the chunk intermediates from the inputs rather than
+ * keeping them from the forward).
+ *   p, q, k, v, g, beta, initial_state, cu_seqlens: exactly as passed to kda_chunk_fwd
+ *     (g is the log decay: the gate activation of kda_chunk_fwd_gated has no backward here).
+ *   d_o:           [B, T, H, V] in qkv_dtype, the gradient of o (rows of every token used).
+ *   d_final_state: [N, H, K, V] fp32 or NULL (zero).
+ *   dq, dk, dg:    [B, T, H, K] fp32;  dv: [B, T, H, V] fp32;  dbeta: [B, T, H] fp32.
+ *     With use_qk_l2norm, dq and dk are the gradients of the un-normalised q and k.
+ *   d_initial_state: [N, H, K, V] fp32 or NULL (not written).
+ * All arithmetic is fp32. Every pointer is a device pointer owned by the caller; inputs
+ * are not modified. The workspace (kda_chunk_bwd_workspace_bytes, 256-byte aligned) holds
+ * the chunk map and one fp32 slab per (chunk, head) of intermediates. Asynchronous on
+ * `stream`; no allocation, no host synchronisation. Errors: as kda_chunk_fwd; nothing is
+ * launched when a check fails. */
+kda_status kda_chunk_bwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes);
+kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                         const void* g, const void* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, const void* d_o, const float* d_final_state,
+                         float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status s);
 

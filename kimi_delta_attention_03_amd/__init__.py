@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
 __all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
-           "KdaLayer", "layer_fwd", "decode_step", "affine_summary", "affine_apply"]
+           "KdaLayer", "layer_fwd", "decode_step", "affine_summary", "affine_apply",
+           "chunk_bwd", "KdaBackward"]
 
 
 def _torch():
@@ -60,6 +61,45 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _core_params(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens, use_qk_l2norm, l2norm_eps):
+    """Shape, dtype and placement checks shared by the forward and backward
+    bindings; returns the kda_fwd_params and the number of sequences N."""
+    torch = _torch()
+    if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape:
+        raise KdaValueError(1, "q, k, g must be [B, T, H, K] with equal shapes")
+    B, T, H, K = q.shape
+    if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
+        raise KdaValueError(1, "v must be [B, T, H, V]")
+    V = v.shape[3]
+    if tuple(beta.shape) != (B, T, H):
+        raise KdaValueError(1, "beta must be [B, T, H]")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise KdaValueError(1, "q, k, v must share a dtype")
+    tensors = [q, k, v, g, beta]
+    for t in tensors:
+        if not t.is_cuda:
+            raise KdaValueError(1, "inputs must be on the GPU")
+        if not t.is_contiguous():
+            raise KdaValueError(1, "inputs must be contiguous")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
+            raise KdaValueError(1, "cu_seqlens must be a 1-D int32 GPU tensor")
+        num_seqs = cu_seqlens.numel() - 1
+        if num_seqs < 1:
+            raise KdaValueError(1, "cu_seqlens needs at least 2 entries")
+    N = num_seqs if num_seqs else B
+    if initial_state is not None:
+        if (tuple(initial_state.shape) != (N, H, K, V) or initial_state.dtype != torch.float32
+                or not initial_state.is_cuda or not initial_state.is_contiguous()):
+            raise KdaValueError(1, f"initial_state must be contiguous fp32 [{N}, {H}, {K}, {V}] on the GPU")
+    if scale is None:
+        scale = K ** -0.5
+    params = make_params(B, T, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale,
+                         chunk_size, use_qk_l2norm, l2norm_eps, num_seqs)
+    return params, N
+
+
 class KdaForward:
     """A bound forward call: checked inputs, preallocated outputs and workspace.
 
@@ -72,38 +112,10 @@ class KdaForward:
                  out=None, workspace=None, gate_mode=None, A_log=None, dt_bias=None, gate_lower_bound=-5.0):
         torch = _torch()
         lib = _lib.load()
-        if q.dim() != 4 or k.shape != q.shape or g.shape != q.shape:
-            raise KdaValueError(1, "q, k, g must be [B, T, H, K] with equal shapes")
+        self.params, N = _core_params(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
+                                      use_qk_l2norm, l2norm_eps)
         B, T, H, K = q.shape
-        if v.dim() != 4 or tuple(v.shape[:3]) != (B, T, H):
-            raise KdaValueError(1, "v must be [B, T, H, V]")
         V = v.shape[3]
-        if tuple(beta.shape) != (B, T, H):
-            raise KdaValueError(1, "beta must be [B, T, H]")
-        if k.dtype != q.dtype or v.dtype != q.dtype:
-            raise KdaValueError(1, "q, k, v must share a dtype")
-        tensors = [q, k, v, g, beta]
-        for t in tensors:
-            if not t.is_cuda:
-                raise KdaValueError(1, "inputs must be on the GPU")
-            if not t.is_contiguous():
-                raise KdaValueError(1, "inputs must be contiguous")
-        num_seqs = 0
-        if cu_seqlens is not None:
-            if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda or cu_seqlens.dim() != 1:
-                raise KdaValueError(1, "cu_seqlens must be a 1-D int32 GPU tensor")
-            num_seqs = cu_seqlens.numel() - 1
-            if num_seqs < 1:
-                raise KdaValueError(1, "cu_seqlens needs at least 2 entries")
-        N = num_seqs if num_seqs else B
-        if initial_state is not None:
-            if (tuple(initial_state.shape) != (N, H, K, V) or initial_state.dtype != torch.float32
-                    or not initial_state.is_cuda or not initial_state.is_contiguous()):
-                raise KdaValueError(1, f"initial_state must be contiguous fp32 [{N}, {H}, {K}, {V}] on the GPU")
-        if scale is None:
-            scale = K ** -0.5
-        self.params = make_params(B, T, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale,
-                                  chunk_size, use_qk_l2norm, l2norm_eps, num_seqs)
         nbytes = ctypes.c_size_t(0)
         _lib.check(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(self.params), ctypes.byref(nbytes)))
         dev = q.device
@@ -172,6 +184,68 @@ def chunk_fwd(q, k, v, g, beta, scale=None, chunk_size=64, initial_state=None, c
     return KdaForward(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
                       output_final_state, use_qk_l2norm, l2norm_eps, gate_mode=gate_mode, A_log=A_log,
                       dt_bias=dt_bias, gate_lower_bound=gate_lower_bound)()
+
+
+class KdaBackward:
+    """A bound backward call (kda_chunk_bwd): the gradients of
+    <d_o, o> + <d_final_state, final_state> for the forward with the same
+    arguments. Outputs dq, dk, dv, dg, dbeta (fp32, the inputs' shapes) and
+    dh0 ([N, H, K, V] fp32, when requested) are preallocated; calling the
+    object runs the backward on the current stream and returns them as a dict.
+    """
+
+    def __init__(self, q, k, v, g, beta, d_o, scale=None, initial_state=None, cu_seqlens=None,
+                 d_final_state=None, use_qk_l2norm=False, l2norm_eps=1e-6, output_dh0=True, workspace=None):
+        torch = _torch()
+        self._lib = _lib.load()
+        self.params, N = _core_params(q, k, v, g, beta, scale, 64, initial_state, cu_seqlens, use_qk_l2norm,
+                                      l2norm_eps)
+        B, T, H, K = q.shape
+        V = v.shape[3]
+        if (tuple(d_o.shape) != (B, T, H, V) or d_o.dtype != q.dtype or not d_o.is_cuda
+                or not d_o.is_contiguous()):
+            raise KdaValueError(1, "d_o must be contiguous [B, T, H, V] in q's dtype on the GPU")
+        if d_final_state is not None and (tuple(d_final_state.shape) != (N, H, K, V)
+                                          or d_final_state.dtype != torch.float32 or not d_final_state.is_cuda
+                                          or not d_final_state.is_contiguous()):
+            raise KdaValueError(1, f"d_final_state must be contiguous fp32 [{N}, {H}, {K}, {V}] on the GPU")
+        nbytes = ctypes.c_size_t(0)
+        _lib.check(self._lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(self.params), ctypes.byref(nbytes)))
+        dev = q.device
+        if workspace is None or workspace.numel() < nbytes.value:
+            workspace = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
+        self.workspace = workspace
+        f32 = torch.float32
+        self.grads = {
+            "dq": torch.empty((B, T, H, K), dtype=f32, device=dev),
+            "dk": torch.empty((B, T, H, K), dtype=f32, device=dev),
+            "dv": torch.empty((B, T, H, V), dtype=f32, device=dev),
+            "dg": torch.empty((B, T, H, K), dtype=f32, device=dev),
+            "dbeta": torch.empty((B, T, H), dtype=f32, device=dev),
+            "dh0": torch.empty((N, H, K, V), dtype=f32, device=dev) if output_dh0 else None,
+        }
+        self.inputs = (q, k, v, g, beta, d_o)
+        self.initial_state = initial_state
+        self.d_final_state = d_final_state
+        self.cu_seqlens = cu_seqlens
+
+    def __call__(self):
+        q, k, v, g, beta, d_o = self.inputs
+        gr = self.grads
+        _lib.check(self._lib.kda_chunk_bwd(
+            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.initial_state),
+            _ptr(self.cu_seqlens), _ptr(d_o), _ptr(self.d_final_state), _ptr(gr["dq"]), _ptr(gr["dk"]),
+            _ptr(gr["dv"]), _ptr(gr["dg"]), _ptr(gr["dbeta"]), _ptr(gr["dh0"]), _ptr(self.workspace),
+            self.workspace.numel(), ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)))
+        return gr
+
+
+def chunk_bwd(q, k, v, g, beta, d_o, scale=None, initial_state=None, cu_seqlens=None, d_final_state=None,
+              use_qk_l2norm=False, l2norm_eps=1e-6):
+    """Backward of chunk_fwd (g is the log decay). Returns a dict of fp32
+    gradients dq, dk, dv, dg, dbeta and dh0."""
+    return KdaBackward(q, k, v, g, beta, d_o, scale, initial_state, cu_seqlens, d_final_state,
+                       use_qk_l2norm, l2norm_eps)()
 
 
 def affine_summary(q, k, v, g, beta, scale=None, cu_seqlens=None, use_qk_l2norm=False, l2norm_eps=1e-6,

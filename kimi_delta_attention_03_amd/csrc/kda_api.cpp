@@ -268,6 +268,82 @@ kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k
   return KDA_OK;
 }
 
+kda_status kda_chunk_bwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes) {
+  kda_status s = check_params(p);
+  if (s != KDA_OK) return s;
+  if (!bytes) return fail(KDA_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = kda::bwd_workspace_bytes(layout_of(p), p->H);
+  return KDA_OK;
+}
+
+kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  kda_status s = check_params(p);
+  if (s != KDA_OK) return s;
+  if (p->num_seqs > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "num_seqs > 0 needs cu_seqlens");
+  if (p->num_seqs == 0 && cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens given but num_seqs == 0");
+  if (cu_seqlens && !aligned(cu_seqlens, 4)) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens must be 4-byte aligned");
+  const kda::Layout L = layout_of(p);
+  const size_t need = kda::bwd_workspace_bytes(L, p->H);
+  if (!workspace) return fail(KDA_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need) return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, need);
+  const bool any_tokens = p->B > 0 && p->T > 0;
+  if (any_tokens) {
+    if (!q || !k || !v || !g || !beta || !d_o)
+      return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta and d_o must be non-NULL");
+    if (!dq || !dk || !dv || !dg || !dbeta)
+      return fail(KDA_ERR_INVALID_ARG, "dq, dk, dv, dg and dbeta must be non-NULL");
+    const size_t ea = p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
+    for (const void* t : {q, k, v, d_o})
+      if (!aligned(t, ea)) return fail(KDA_ERR_INVALID_ARG, "q, k, v and d_o must be aligned to their element size");
+    if (!aligned(g, p->g_dtype == KDA_DTYPE_BF16 ? 2 : 4) || !aligned(beta, p->beta_dtype == KDA_DTYPE_BF16 ? 2 : 4))
+      return fail(KDA_ERR_INVALID_ARG, "g and beta must be aligned to their element size");
+    for (const float* t : {dq, dk, dv, dg, dbeta})
+      if (!aligned(t, 4)) return fail(KDA_ERR_INVALID_ARG, "gradient outputs must be 4-byte aligned");
+  }
+  for (const float* t : {initial_state, d_final_state, (const float*)d_initial_state})
+    if (t && !aligned(t, 4)) return fail(KDA_ERR_INVALID_ARG, "states must be 4-byte aligned");
+  const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
+  const int64_t nunits = nseq * p->H;
+  if (nunits * (p->V / 16) > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  char* w = static_cast<char*>(workspace);
+  const int varlen = p->num_seqs > 0;
+  if (varlen) {
+    hipError_t e = kda::launch_varlen_map(cu_seqlens, p->num_seqs, p->T, w, L.ncp, L.off_chunk_tab, L.off_seq_tab,
+                                          L.off_order, stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
+  }
+  kda::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.d_o = d_o;
+  a.init = initial_state;
+  a.d_final = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dh0 = d_initial_state;
+  a.bf16_qkv = p->qkv_dtype == KDA_DTYPE_BF16;
+  a.g_f32 = p->g_dtype == KDA_DTYPE_F32;
+  a.beta_f32 = p->beta_dtype == KDA_DTYPE_F32;
+  a.H = (int)p->H;
+  a.scale = p->scale;
+  a.l2norm = p->use_qk_l2norm != 0;
+  a.l2eps = p->l2norm_eps;
+  a.varlen = varlen;
+  a.nunits = (int)nunits;
+  a.nt = varlen ? 0 : (int)(p->T / 64);
+  a.ws = w;
+  a.meta_bytes = L.meta_bytes;
+  a.ncp = L.ncp;
+  a.off_chunk_tab = L.off_chunk_tab;
+  a.off_seq_tab = L.off_seq_tab;
+  a.sl = kda::make_bwd_slab(p->K, p->V);
+  const size_t nitems = any_tokens ? L.ncp * (size_t)p->H : 0;
+  if (nitems > (size_t)INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = kda::launch_bwd(a, p->K, (int)nitems, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
 kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* gate, const void* q, const void* k,
                                const void* v, const void* g, const void* beta, const float* initial_state,
                                const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,

@@ -62,6 +62,35 @@ struct DecodeArgs {
   int nunits;          // N * H
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const void* d_o;          // [B, T, H, V], q's dtype
+  const float* init;        // [N, H, K, V] or null
+  const float* d_final;     // [N, H, K, V] or null
+  float* dq;                // [B, T, H, K]
+  float* dk;
+  float* dv;                // [B, T, H, V]
+  float* dg;                // [B, T, H, K]
+  float* dbeta;             // [B, T, H]
+  float* dh0;               // [N, H, K, V] or null
+  int bf16_qkv, g_f32, beta_f32;
+  int H;
+  float scale;
+  int l2norm;
+  float l2eps;
+  int varlen;
+  int nunits;               // N * H
+  int nt;                   // fixed length: chunks per batch row
+  char* ws;
+  size_t meta_bytes, ncp;
+  size_t off_chunk_tab, off_seq_tab;
+  BwdSlab sl;
+};
+
 // bf16 == 1 selects the bf16 instantiation (bf16 q/k/v, bf16 intermediates).
 hipError_t launch_stage12(const Stage12Args& a, int K, int bf16, int nblocks, hipStream_t s);
 hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s);
@@ -72,6 +101,8 @@ hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, s
 // S_out = M S0 + N for each of nunits (sequence, head) pairs, K == V
 hipError_t launch_affine_apply(const float* M, const float* N, const float* S0, float* S_out, int nunits, int K,
                                hipStream_t s);
+// backward: chunk-term recompute, chunk-start states, state gradients, chunk gradients
+hipError_t launch_bwd(const BwdArgs& a, int K, int nitems, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int K, int bf16_qkv, int g_f32, int b_f32, hipStream_t s);
 
 // sets the thread-local message returned by kda_last_error and returns s

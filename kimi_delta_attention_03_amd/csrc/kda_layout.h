@@ -94,4 +94,49 @@ static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, i
   return L;
 }
 
+// Backward workspace: the same metadata region as the forward, then one fp32
+// slab per (chunk slot p, head h), chunk-major (index p * H + h). Offsets are
+// in floats from the slab start; matrices are row-major with the chunk row
+// (64) or the key channel (K) first, as named.
+struct BwdSlab {
+  // chunk terms recomputed from the inputs (natural-log gates)
+  size_t qn, kn, G, qg, kg, w, kb;   // [64][K]: normalised q, k; cumsum; s q e^G; k e^(Gl-G); A Kb; beta k e^G
+  size_t u, vb;                      // [64][V]: A Vb; beta v
+  size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
+  size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
+  // chunk-start state and the gradient of the chunk-end state
+  size_t S, dS;                      // [K][V]
+  // per-chunk gradients
+  size_t dO, vn, dvn, dvb;           // [64][V]
+  size_t dqg, dw, dkg, dkb, dqn, dkn, dG;  // [64][K]
+  size_t daqk, da, t1, dl;           // [64][64]
+  size_t dgam;                       // [K]
+  size_t floats;                     // slab size
+};
+
+static inline BwdSlab make_bwd_slab(int K, int V) {
+  BwdSlab s{};
+  size_t o = 0;
+  auto take = [&](size_t n) { const size_t r = o; o += n; return r; };
+  const size_t C = kChunk, CK = C * (size_t)K, CV = C * (size_t)V, CC = C * C;
+  s.qn = take(CK); s.kn = take(CK); s.G = take(CK); s.qg = take(CK); s.kg = take(CK); s.w = take(CK);
+  s.kb = take(CK);
+  s.u = take(CV); s.vb = take(CV);
+  s.aqk = take(CC); s.a = take(CC); s.m = take(CC);
+  s.beta = take(C); s.gam = take((size_t)K); s.nq = take(C); s.nk = take(C);
+  s.S = take((size_t)K * V); s.dS = take((size_t)K * V);
+  s.dO = take(CV); s.vn = take(CV); s.dvn = take(CV); s.dvb = take(CV);
+  s.dqg = take(CK); s.dw = take(CK); s.dkg = take(CK); s.dkb = take(CK); s.dqn = take(CK); s.dkn = take(CK);
+  s.dG = take(CK);
+  s.daqk = take(CC); s.da = take(CC); s.t1 = take(CC); s.dl = take(CC);
+  s.dgam = take((size_t)K);
+  s.floats = round_up(o, 64);
+  return s;
+}
+
+// total backward workspace bytes (metadata of the forward layout + slabs)
+static inline size_t bwd_workspace_bytes(const Layout& L, int64_t H) {
+  return L.meta_bytes + L.ncp * (size_t)H * make_bwd_slab(L.K, L.V).floats * sizeof(float);
+}
+
 }  // namespace kda

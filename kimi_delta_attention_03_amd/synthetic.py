@@ -110,6 +110,17 @@ def core_inputs(B, T, H, K, V, dtype="bf16", seed=0, init_std=None, lengths=None
                       meta={"seed": seed, "B": B, "T": T, "H": H, "K": K, "V": V})
 
 
+def grad_inputs(B, T, H, V, N, K=None, seed=0, dtype="bf16", final=True):
+    """Incoming gradients for the backward: d_o [B, T, H, V] ~ N(0,1) (rounded to
+    bf16 for dtype "bf16") and d_final [N, H, K, V] ~ N(0,1) fp32 (or None)."""
+    rng = np.random.default_rng(seed)
+    d_o = rng.standard_normal((B, T, H, V), dtype=np.float32)
+    if dtype == "bf16":
+        d_o = round_bf16(d_o)
+    d_final = rng.standard_normal((N, H, K if K is not None else V, V), dtype=np.float32) if final else None
+    return d_o, d_final
+
+
 # The five workloads of this project, smallest first. Index 2 is the headline.
 WORKLOADS = {
     0: dict(name="tiny_fp32", B=1, H=2, T=256, K=64, V=64, dtype="fp32", init_std=None, seed=1000),
