@@ -178,6 +178,79 @@ def bench_affine(args, torch, kda, WORKLOADS, workload):
     }), flush=True)
 
 
+def bwd_flops_per_chunk_head(C, K, V):
+    """Algorithmic FLOPs of each backward launch per (chunk, head), causal
+    triangles counted as triangles (tri = C(C+1)/2 pairs):
+      prep         Aqk, M (2 tri K each), the unit-triangular inverse (C^3/3),
+                   W = A Kb and U = A Vb (2 tri K, 2 tri V)
+      states_fwd   Vn = U - W S and S' = gamma S + KG^T Vn (2 C K V each)
+      states_bwd   dVn = Aqk^T dO + KG dS' (2 tri V + 2 C K V),
+                   dS = Qg^T dO - W^T dVn (2 x 2 C K V)
+      chunk        Vn, dVn (as above), dQg, dW, dKG (3 x 2 C K V), dAqk (2 tri V),
+                   dgamma (2 K V), dA (2 tri (K + V)), dKb, dVb (2 tri K, 2 tri V),
+                   A^T dA A^T (2 C^3 / 3), four gated sums (4 x 2 tri K), ~20 C K
+                   elementwise"""
+    tri = C * (C + 1) / 2
+    ckv = 2.0 * C * K * V
+    return {
+        "prep": 4 * tri * K + C ** 3 / 3 + 2 * tri * (K + V),
+        "states_fwd": 2 * ckv,
+        "states_bwd": 2 * tri * V + 3 * ckv,
+        "chunk": (ckv + 2 * tri * V + ckv + 3 * ckv + 2 * tri * V + 2 * K * V + 2 * tri * (K + V)
+                  + 2 * tri * (K + V) + 2 * C ** 3 / 3 + 8 * tri * K + 20 * C * K),
+    }
+
+
+def bench_backward(args, torch, kda, WORKLOADS, workload):
+    """The backward (kda_chunk_bwd) on a core workload's shape: one step = all
+    four launches for d_o ~ N(0,1) and d_final ~ N(0,1); each launch is also
+    timed alone (in order, over one workspace) for the roofline entry."""
+    from kimi_delta_attention_03_amd.synthetic import grad_inputs
+    x = workload(args.workload)
+    dev = "cuda:0"
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    to = lambda a, d: torch.from_numpy(a).to(d).to(dev)
+    q, k, v, g, beta = (to(a, dt) for a in (x.q, x.k, x.v, x.g, x.beta))
+    init = None if x.initial_state is None else to(x.initial_state, torch.float32)
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens.astype(np.int32)).to(dev)
+    B, T, H, K = x.q.shape
+    V = x.v.shape[3]
+    N = B if cu is None else len(x.cu_seqlens) - 1
+    d_o, d_f = grad_inputs(B, T, H, V, N, K=K, seed=WORKLOADS[args.workload]["seed"] + 50, dtype=x.dtype)
+    call = kda.KdaBackward(q, k, v, g, beta, to(d_o, dt), scale=x.scale, initial_state=init, cu_seqlens=cu,
+                           d_final_state=to(d_f, torch.float32))
+    for _ in range(args.warmup):
+        call()
+    ms = time_loop(call, args.steps, torch)
+    names = {1: "prep", 2: "states_fwd", 4: "states_bwd", 8: "chunk"}
+    reps = max(1, min(args.kernel_reps, 5))
+    stage_ms = {}
+    for bit, nm in names.items():
+        # every stage reads what the earlier ones wrote: run the earlier ones first, then time this one
+        if bit > 1:
+            call(bit - 1)
+        stage_ms[nm] = time_loop(lambda: call(bit), reps, torch)
+    if cu is not None:
+        nchunk_heads = int(sum(-(-int(L) // 64) for L in np.diff(x.cu_seqlens))) * H
+    else:
+        nchunk_heads = B * (T // 64) * H
+    fl = bwd_flops_per_chunk_head(64, K, V)
+    dom = max(stage_ms, key=stage_ms.get)
+    ach = fl[dom] * nchunk_heads / (stage_ms[dom] / 1e3) / 1e12
+    print(json.dumps({
+        "metric": "KDA chunk-bwd tokens/s (dq, dk, dv, dg, dbeta, dh0)", "value": B * T / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{x.dtype} inputs, f32 arithmetic and gradients", "data": "synthetic (seeded numpy generators)",
+        "config": {"workload": WORKLOADS[args.workload]["name"] + "_backward", "B": B, "T": T, "H": H, "K": K,
+                   "V": V},
+        "stage_ms": stage_ms,
+        "roofline": {"kernel": f"bwd_{dom}", "bound": "alu", "achieved": ach, "peak": PEAK_FP32 / 1e12,
+                     "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": None,
+                     "alg_flops_per_launch": fl[dom] * nchunk_heads},
+    }), flush=True)
+
+
 def bench_layer(args, torch, kda):
     """The KDA layer around the core (workload 4): one step = the whole layer
     forward over a [B, T, M] bf16 input, inputs and weights resident in HBM."""
@@ -216,9 +289,10 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--mode", choices=["forward", "decode", "affine"], default="forward",
+    ap.add_argument("--mode", choices=["forward", "decode", "affine", "backward"], default="forward",
                     help="decode: one kda_decode_step over B=256 sequences x H=32 (K=V=128, bf16); "
-                         "affine: stage 1+2 plus the affine summaries on the workload's shape")
+                         "affine: stage 1+2 plus the affine summaries on the workload's shape; "
+                         "backward: kda_chunk_bwd on the workload's shape")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -247,6 +321,8 @@ def main():
         return bench_decode(args, torch, kda)
     if args.mode == "affine":
         return bench_affine(args, torch, kda, WORKLOADS, workload)
+    if args.mode == "backward":
+        return bench_backward(args, torch, kda, WORKLOADS, workload)
 
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()

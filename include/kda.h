@@ -213,6 +213,19 @@ kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, 
                          float* d_initial_state, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* kda_chunk_bwd split into its four launches, for timing each: `stages` is a bit mask
+ * (1: rebuild the chunk terms into the workspace, 2: chunk-start states, 4: state
+ * gradients and d_initial_state, 8: every other gradient). Each stage reads what the
+ * earlier ones left in the same workspace, so stages run in increasing order over one
+ * workspace reproduce kda_chunk_bwd exactly; 15 is kda_chunk_bwd. Arguments, errors and
+ * ownership as kda_chunk_bwd; KDA_ERR_INVALID_ARG for a mask outside [1, 15]. */
+kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta,
+                                const float* initial_state, const int32_t* cu_seqlens,
+                                const void* d_o, const float* d_final_state, float* dq, float* dk,
+                                float* dv, float* dg, float* dbeta, float* d_initial_state,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status s);
 

@@ -229,11 +229,14 @@ class KdaBackward:
         self.d_final_state = d_final_state
         self.cu_seqlens = cu_seqlens
 
-    def __call__(self):
+    def __call__(self, stages=15):
+        """Run the backward (or, for timing, the launches in the `stages` bit
+        mask: 1 chunk terms, 2 chunk-start states, 4 state gradients, 8 chunk
+        gradients) and return the gradients."""
         q, k, v, g, beta, d_o = self.inputs
         gr = self.grads
-        _lib.check(self._lib.kda_chunk_bwd(
-            ctypes.byref(self.params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.initial_state),
+        _lib.check(self._lib.kda_chunk_bwd_stages(
+            ctypes.byref(self.params), stages, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(self.initial_state),
             _ptr(self.cu_seqlens), _ptr(d_o), _ptr(self.d_final_state), _ptr(gr["dq"]), _ptr(gr["dk"]),
             _ptr(gr["dv"]), _ptr(gr["dg"]), _ptr(gr["dbeta"]), _ptr(gr["dh0"]), _ptr(self.workspace),
             self.workspace.numel(), ctypes.c_void_p(_torch().cuda.current_stream().cuda_stream)))

@@ -276,10 +276,12 @@ kda_status kda_chunk_bwd_workspace_bytes(const kda_fwd_params* p, size_t* bytes)
   return KDA_OK;
 }
 
-kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
-                         const void* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
-                         const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
-                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const void* q, const void* k,
+                                const void* v, const void* g, const void* beta, const float* initial_state,
+                                const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, float* dq,
+                                float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (stages < 1 || stages > 15) return fail(KDA_ERR_INVALID_ARG, "stages must be a mask in [1, 15] (got %d)", stages);
   kda_status s = check_params(p);
   if (s != KDA_OK) return s;
   if (p->num_seqs > 0 && !cu_seqlens) return fail(KDA_ERR_INVALID_ARG, "num_seqs > 0 needs cu_seqlens");
@@ -311,7 +313,7 @@ kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, 
   if (nunits * (p->V / 16) > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
   char* w = static_cast<char*>(workspace);
   const int varlen = p->num_seqs > 0;
-  if (varlen) {
+  if (varlen && (stages & 1)) {
     hipError_t e = kda::launch_varlen_map(cu_seqlens, p->num_seqs, p->T, w, L.ncp, L.off_chunk_tab, L.off_seq_tab,
                                           L.off_order, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
@@ -339,9 +341,17 @@ kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, 
   a.sl = kda::make_bwd_slab(p->K, p->V);
   const size_t nitems = any_tokens ? L.ncp * (size_t)p->H : 0;
   if (nitems > (size_t)INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "grid too large");
-  hipError_t e = kda::launch_bwd(a, p->K, (int)nitems, stream);
+  hipError_t e = kda::launch_bwd(a, p->K, (int)nitems, stages, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return KDA_OK;
+}
+
+kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const float* initial_state, const int32_t* cu_seqlens, const void* d_o,
+                         const float* d_final_state, float* dq, float* dk, float* dv, float* dg, float* dbeta,
+                         float* d_initial_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kda_chunk_bwd_stages(p, 15, q, k, v, g, beta, initial_state, cu_seqlens, d_o, d_final_state, dq, dk, dv, dg,
+                              dbeta, d_initial_state, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* gate, const void* q, const void* k,

@@ -519,22 +519,24 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdArgs a) {
   }
 }
 
+// stages: bit 0 prep, bit 1 chunk-start states, bit 2 state gradients, bit 3 chunk gradients
 template <int K>
-hipError_t launch_k(const BwdArgs& a, int nitems, hipStream_t s) {
+hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   const int nvb = K / 16;
-  if (nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+  if ((stages & 1) && nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
   if (a.nunits > 0) {
-    if (nitems > 0) hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
-    hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
+    if ((stages & 2) && nitems > 0)
+      hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
+    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
   }
-  if (nitems > 0) hipLaunchKernelGGL(bwd_chunk_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+  if ((stages & 8) && nitems > 0) hipLaunchKernelGGL(bwd_chunk_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd(const BwdArgs& a, int K, int nitems, hipStream_t s) {
-  return K == 128 ? launch_k<128>(a, nitems, s) : launch_k<64>(a, nitems, s);
+hipError_t launch_bwd(const BwdArgs& a, int K, int nitems, int stages, hipStream_t s) {
+  return K == 128 ? launch_k<128>(a, nitems, stages, s) : launch_k<64>(a, nitems, stages, s);
 }
 
 }  // namespace kda

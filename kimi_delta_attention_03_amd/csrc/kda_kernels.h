@@ -102,7 +102,8 @@ hipError_t launch_varlen_map(const int32_t* cu, int nseq, int64_t T, char* ws, s
 hipError_t launch_affine_apply(const float* M, const float* N, const float* S0, float* S_out, int nunits, int K,
                                hipStream_t s);
 // backward: chunk-term recompute, chunk-start states, state gradients, chunk gradients
-hipError_t launch_bwd(const BwdArgs& a, int K, int nitems, hipStream_t s);
+// stages: bit mask of the four launches (1 prep, 2 states, 4 state gradients, 8 chunk gradients)
+hipError_t launch_bwd(const BwdArgs& a, int K, int nitems, int stages, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, int K, int bf16_qkv, int g_f32, int b_f32, hipStream_t s);
 
 // sets the thread-local message returned by kda_last_error and returns s

@@ -124,3 +124,62 @@ def test_bwd_empty_fixed_length():
     torch.cuda.synchronize()
     assert torch.equal(gr["dh0"], d_f)
     assert gr["dq"].numel() == 0
+
+
+def _bwd_full(x, d_o, d_f):
+    import torch
+    import kimi_delta_attention_03_amd as kda
+    d = dev_inputs(x)
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    gr = kda.chunk_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], to_dev(d_o, dt), scale=x.scale,
+                       initial_state=d["initial_state"], cu_seqlens=d["cu_seqlens"],
+                       d_final_state=to_dev(d_f, torch.float32))
+    torch.cuda.synchronize()
+    out = {n: host(t) for n, t in gr.items()}
+    del gr, d
+    torch.cuda.empty_cache()
+    return out
+
+
+def test_bwd_workload1_one_head_whole_sequence():
+    """Workload 1 (B=2, H=16, T=4096, K=V=128, bf16) runs whole on the GPU;
+    the oracle differentiates batch row 1, head 11 over all 4096 tokens."""
+    from kimi_delta_attention_03_amd.synthetic import workload
+    _say("bwd workload 1 full size, oracle on (b=1, h=11)")
+    x = workload(1)
+    B, T, H, K = x.q.shape
+    d_o, d_f = grad_inputs(B, T, H, K, B, K=K, seed=1051, dtype=x.dtype)
+    gr = _bwd_full(x, d_o, d_f)
+    b, h = 1, 11
+    sl = lambda a: a[b:b + 1, :, h:h + 1]
+    ref = orc.kda_recurrent_vjp(sl(x.q), sl(x.k), sl(x.v), sl(x.g), x.beta[b:b + 1, :, h:h + 1], x.scale,
+                                sl(d_o), d_f[b:b + 1, h:h + 1], None)
+    errs = {n: rel_err(gr[n][b:b + 1, :, h:h + 1] if n != "dh0" else gr[n][b:b + 1, h:h + 1], ref[n])
+            for n in NAMES}
+    check(errs, TOL["bf16"])
+
+
+def test_bwd_headline_suffix_two_heads():
+    """Headline shape (B=1, H=32, T=32768, bf16, initial state ~ N(0, 0.1)) whole
+    on the GPU. The gradients of the last 256 tokens depend on the past only
+    through the state entering them: the oracle runs its forward recurrence over
+    the first T - 256 tokens, then differentiates the last 256 from that state,
+    for heads 0 and 29."""
+    from kimi_delta_attention_03_amd.synthetic import workload
+    _say("bwd headline full size, oracle on the last 256 tokens of heads 0 and 29")
+    x = workload(2)
+    B, T, H, K = x.q.shape
+    d_o, d_f = grad_inputs(B, T, H, K, B, K=K, seed=1052, dtype=x.dtype)
+    gr = _bwd_full(x, d_o, d_f)
+    n = 256
+    t0 = T - n
+    for h in (0, 29):
+        hs = slice(h, h + 1)
+        _, S_mid = orc.kda_recurrent(x.q[:, :t0, hs], x.k[:, :t0, hs], x.v[:, :t0, hs], x.g[:, :t0, hs],
+                                     x.beta[:, :t0, hs], x.scale, initial_state=x.initial_state[:, hs])
+        tail = lambda a: a[:, t0:, hs]
+        ref = orc.kda_recurrent_vjp(tail(x.q), tail(x.k), tail(x.v), tail(x.g), x.beta[:, t0:, hs], x.scale,
+                                    tail(d_o), d_f[:, hs], S_mid)
+        errs = {nm: rel_err(gr[nm][:, t0:, hs], ref[nm]) for nm in ("dq", "dk", "dv", "dg", "dbeta")}
+        _say(f"  head {h}")
+        check(errs, TOL["bf16"])
