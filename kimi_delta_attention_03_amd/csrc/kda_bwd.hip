@@ -26,7 +26,8 @@
 //   prep        per (chunk, head): the chunk terms above, from the inputs
 //   states_fwd  per (sequence, head, 16 columns): chunk-start states, in order
 //   states_bwd  per (sequence, head, 16 columns): dS' per chunk, in reverse; dh0
-//   chunk       per (chunk, head): every other gradient
+//   chunk       per (chunk, head): every other gradient, as two launches (the
+//               matrix products, then the elementwise and gated-sum rules)
 // Every intermediate lives in a per-(chunk, head) fp32 slab of the workspace.
 #include "kda_device.h"
 #include "kda_kernels.h"
@@ -81,35 +82,71 @@ __device__ __forceinline__ void seq_chunks(const BwdArgs& a, int seq, int& p0, i
   }
 }
 
-// out(i, j) = sum_kk fa(i, kk) fb(kk, j) for an M x N result, 4 x 4 outputs per
-// thread and pass
-template <int M, int N, typename FA, typename FB, typename FO>
-__device__ __forceinline__ void wg_mm(int KD, FA fa, FB fb, FO fo) {
-  constexpr int TN = N / 4;
-  constexpr int NT = (M / 4) * TN;
-  for (int t = threadIdx.x; t < NT; t += kBT) {
-    const int i0 = (t / TN) * 4, j0 = (t % TN) * 4;
-    float acc[4][4];
+// out(i, j) = sum_kk A(i, kk) B(kk, j) for an M x N result over KD (a multiple
+// of 16), with A(i, kk) = A[i * lda + kk] (TA: A[kk * lda + i]) and B(kk, j) =
+// B[kk * ldb + j] (TB: B[j * ldb + kk]). 16-deep slices of both operands are
+// staged in LDS (smem: 16 (M + 4) + 16 (N + 4) floats) with loads that run
+// along the contiguous index; each thread accumulates 4 rows x M N / 1024
+// columns. Ends with a barrier, before the epilogue calls.
+template <int M, int N, bool TA, bool TB, typename FO>
+__device__ __forceinline__ void lds_mm(int KD, const float* A, int lda, const float* B, int ldb, float* smem,
+                                       FO fo) {
+  constexpr int KS = 16;
+  constexpr int NC = M * N / (kBT * 4);
+  constexpr int NCG = N / NC;
+  constexpr int SA = M + 4, SB = N + 4;
+  static_assert(NC % 4 == 0 && (M / 4) * NCG == kBT, "thread tiling");
+  float* sa = smem;
+  float* sb = smem + KS * SA;
+  const int tid = threadIdx.x;
+  const int rg = tid / NCG, cg = tid % NCG;
+  float acc[4][NC];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-    for (int kk = 0; kk < KD; ++kk) {
-      float av[4], bv[4];
+    for (int c = 0; c < NC; ++c) acc[r][c] = 0.f;
+  for (int k0 = 0; k0 < KD; k0 += KS) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = fa(i0 + r, kk);
+    for (int e = tid; e < M * KS; e += kBT) {
+      if (TA) {
+        const int kk = e / M, i = e % M;
+        sa[kk * SA + i] = A[(size_t)(k0 + kk) * lda + i];
+      } else {
+        const int i = e / KS, kk = e % KS;
+        sa[kk * SA + i] = A[(size_t)i * lda + k0 + kk];
+      }
+    }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = fb(kk, j0 + c);
+    for (int e = tid; e < N * KS; e += kBT) {
+      if (TB) {
+        const int j = e / KS, kk = e % KS;
+        sb[kk * SB + j] = B[(size_t)j * ldb + k0 + kk];
+      } else {
+        const int kk = e / N, j = e % N;
+        sb[kk * SB + j] = B[(size_t)(k0 + kk) * ldb + j];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const floatx4 a4 = *reinterpret_cast<const floatx4*>(sa + kk * SA + 4 * rg);
+      float b[NC];
+#pragma unroll
+      for (int c = 0; c < NC; c += 4) {
+        const floatx4 b4 = *reinterpret_cast<const floatx4*>(sb + kk * SB + NC * cg + c);
+        b[c] = b4[0]; b[c + 1] = b4[1]; b[c + 2] = b4[2]; b[c + 3] = b4[3];
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+        for (int c = 0; c < NC; ++c) acc[r][c] += a4[r] * b[c];
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) fo(i0 + r, j0 + c, acc[r][c]);
+    __syncthreads();
   }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) fo(4 * rg + r, NC * cg + c, acc[r][c]);
 }
 
 // ---------------------------------------------------------------- prep
@@ -210,14 +247,21 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // A = (I + L)^-1 by forward substitution, thread j -> column j
+  // A = (I + L)^-1 by forward substitution, lane j of wave 0 -> column j, kept
+  // in registers: x_i = delta_ij - sum_{m<i} L_im x_m, where the rows above the
+  // diagonal come out zero by themselves (right-hand side e_j)
   if (tid < C) {
     const int j = tid;
+    float x[C];
+#pragma unroll
     for (int i = 0; i < C; ++i) {
-      float x = (i == j) ? 1.f : 0.f;
-      for (int m = j; m < i; ++m) x -= sL[i * CP + m] * sA[m * CP + j];
-      sA[i * CP + j] = i >= j ? x : 0.f;
+      float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < i; ++m) acc -= sL[i * CP + m] * x[m];
+      x[i] = acc;
     }
+#pragma unroll
+    for (int i = 0; i < C; ++i) sA[i * CP + j] = x[i];
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += kBT) sl[o.a + e] = sA[(e / C) * CP + e % C];
@@ -247,240 +291,358 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------- chunk-start states
+// One workgroup per (sequence, head, 16-column block) walks the chunks in order.
+// Wave w keeps state rows [16 TPW w, 16 TPW (w + 1)) of the block as fp32 MFMA
+// accumulators (16x16x4: lane (g, i) = (l / 16, l % 16) holds rows 4 g + r,
+// column i of a 16 x 16 tile; an A operand lane holds row i, reduction index g of
+// a 4-deep slice, a B operand lane reduction index g, column i). The next
+// chunk's operands are loaded into registers while the current chunk computes.
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 template <int K>
 __global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
-  constexpr int V = K, KP = K + 1, NVB = V / 16;
-  __shared__ float sW[C * KP], sKG[C * KP];
-  __shared__ float sU[C * 17], sVn[C * 17], sS[K * 17], sGam[K];
+  constexpr int V = K, KP = K + 4, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
+  __shared__ __attribute__((aligned(16))) float sW[C * KP], sKG[C * KP];
+  __shared__ __attribute__((aligned(16))) float sU[C * 20];
+  __shared__ float sVn[C * 17], sS[K * 17], sGam[K];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = (int)blockIdx.x / NVB, vb = (int)blockIdx.x % NVB;
   if (u >= a.nunits) return;
   const int seq = u / a.H, h = u % a.H;
   const BwdSlab& o = a.sl;
   int p0, nch;
   seq_chunks(a, seq, p0, nch);
-  const int c = tid & 15;
-  const int col = 16 * vb + c;
-  for (int d = tid >> 4; d < K; d += 16) sS[d * 17 + c] = a.init ? a.init[((size_t)u * K + d) * V + col] : 0.f;
-  __syncthreads();
+  const int col = 16 * vb + xi;
+
+  floatx4 S[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * (TPW * w + t) + 4 * gq + r;
+      S[t][r] = a.init ? a.init[((size_t)u * K + row) * V + col] : 0.f;
+    }
+  // prefetch registers: W and KG as float4 (chunk-row-major), the U block, gamma
+  floatx4 rW[NF], rKG[NF], rU;
+  float rG = 0.f;
+  auto fetch = [&](int cc) {
+    const float* sl = slab_of(a, p0 + cc, h);
+#pragma unroll
+    for (int m = 0; m < NF; ++m) {
+      rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (tid + kBT * m));
+      rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (tid + kBT * m));
+    }
+    rU = *reinterpret_cast<const floatx4*>(sl + o.u + (tid >> 2) * V + 16 * vb + 4 * (tid & 3));
+    if (tid < K) rG = sl[o.gam + tid];
+  };
+  if (nch > 0) fetch(0);
   for (int cc = 0; cc < nch; ++cc) {
+    __syncthreads();  // the previous chunk's operands are no longer read
+#pragma unroll
+    for (int m = 0; m < NF; ++m) {
+      const int e = 4 * (tid + kBT * m), r = e / K, d = e % K;
+      *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
+      *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
+    }
+    *reinterpret_cast<floatx4*>(sU + (tid >> 2) * 20 + 4 * (tid & 3)) = rU;
+    if (tid < K) sGam[tid] = rG;
     float* sl = slab_of(a, p0 + cc, h);
-    for (int d = tid >> 4; d < K; d += 16) sl[o.S + d * V + col] = sS[d * 17 + c];
-    for (int e = tid; e < C * K; e += kBT) {
-      const int r = e / K, d = e % K;
-      sW[r * KP + d] = sl[o.w + e];
-      sKG[r * KP + d] = sl[o.kg + e];
-    }
-    for (int e = tid; e < C * 16; e += kBT) sU[(e >> 4) * 17 + (e & 15)] = sl[o.u + (e >> 4) * V + 16 * vb + (e & 15)];
-    if (tid < K) sGam[tid] = sl[o.gam + tid];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + t) + 4 * gq + r;
+        sl[o.S + row * V + col] = S[t][r];  // chunk-start state
+        sS[row * 17 + xi] = S[t][r];
+      }
+    if (cc + 1 < nch) fetch(cc + 1);
     __syncthreads();
-    for (int i = tid >> 4; i < C; i += 16) {
-      float acc = 0.f;
-      for (int d = 0; d < K; ++d) acc += sW[i * KP + d] * sS[d * 17 + c];
-      sVn[i * 17 + c] = sU[i * 17 + c] - acc;
+    // Vn rows 16 w .. 16 w + 15 = U - W S
+    {
+      floatx4 acc = zero4();
+#pragma unroll 8
+      for (int k0 = 0; k0 < K; k0 += 4)
+        acc = mfma4(sW[(16 * w + xi) * KP + k0 + gq], sS[(k0 + gq) * 17 + xi], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * w + 4 * gq + r;
+        sVn[i * 17 + xi] = sU[i * 20 + xi] - acc[r];
+      }
     }
     __syncthreads();
-    for (int d = tid >> 4; d < K; d += 16) {
-      float acc = sGam[d] * sS[d * 17 + c];
-      for (int i = 0; i < C; ++i) acc += sKG[i * KP + d] * sVn[i * 17 + c];
-      sS[d * 17 + c] = acc;
+    // S = Diag(gamma) S + KG^T Vn
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int rt = TPW * w + t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) S[t][r] *= sGam[16 * rt + 4 * gq + r];
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 4)
+        S[t] = mfma4(sKG[(k0 + gq) * KP + 16 * rt + xi], sVn[(k0 + gq) * 17 + xi], S[t]);
     }
-    __syncthreads();
   }
 }
 
 // ------------------------------------------------------------ state gradients
+// Same layout as above, chunks in reverse: wave w keeps rows of dS (the
+// gradient of the state at the current chunk boundary) as accumulators.
 template <int K>
 __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
-  constexpr int V = K, KP = K + 1, CP = C + 1, NVB = V / 16;
-  __shared__ float sAq[C * CP], sKG[C * KP], sQG[C * KP], sW[C * KP];
+  constexpr int V = K, KP = K + 4, CP = C + 4, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
+  constexpr int NA = C * C / 4 / kBT;
+  __shared__ __attribute__((aligned(16))) float sKG[C * KP], sQG[C * KP], sW[C * KP], sAq[C * CP];
   __shared__ float sdO[C * 17], sdVn[C * 17], sdS[K * 17], sGam[K];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int u = (int)blockIdx.x / NVB, vb = (int)blockIdx.x % NVB;
   if (u >= a.nunits) return;
   const int seq = u / a.H, h = u % a.H;
   const BwdSlab& o = a.sl;
   int p0, nch;
   seq_chunks(a, seq, p0, nch);
-  const int c = tid & 15;
-  const int col = 16 * vb + c;
+  const int col = 16 * vb + xi;
   const int qf32 = !a.bf16_qkv;
-  for (int d = tid >> 4; d < K; d += 16)
-    sdS[d * 17 + c] = a.d_final ? a.d_final[((size_t)u * K + d) * V + col] : 0.f;
-  __syncthreads();
-  for (int cc = nch - 1; cc >= 0; --cc) {
+
+  floatx4 dS[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * (TPW * w + t) + 4 * gq + r;
+      dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
+    }
+  floatx4 rKG[NF], rQG[NF], rW[NF], rA[NA];
+  float rO[4];
+  float rG = 0.f;
+  auto fetch = [&](int cc) {
+    const float* sl = slab_of(a, p0 + cc, h);
+#pragma unroll
+    for (int m = 0; m < NF; ++m) {
+      rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (tid + kBT * m));
+      rQG[m] = *reinterpret_cast<const floatx4*>(sl + o.qg + 4 * (tid + kBT * m));
+      rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (tid + kBT * m));
+    }
+#pragma unroll
+    for (int m = 0; m < NA; ++m) rA[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (tid + kBT * m));
     const ItemB it = chunk_of(a, p0 + cc, h);
+    const int r = tid >> 2, c0 = 16 * vb + 4 * (tid & 3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      rO[c] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * a.H + h) * V + c0 + c, qf32) : 0.f;
+    if (tid < K) rG = sl[o.gam + tid];
+  };
+  if (nch > 0) fetch(nch - 1);
+  for (int cc = nch - 1; cc >= 0; --cc) {
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NF; ++m) {
+      const int e = 4 * (tid + kBT * m), r = e / K, d = e % K;
+      *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
+      *reinterpret_cast<floatx4*>(sQG + r * KP + d) = rQG[m];
+      *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
+    }
+#pragma unroll
+    for (int m = 0; m < NA; ++m) {
+      const int e = 4 * (tid + kBT * m);
+      *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = rA[m];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sdO[(tid >> 2) * 17 + 4 * (tid & 3) + c] = rO[c];
+    if (tid < K) sGam[tid] = rG;
     float* sl = slab_of(a, p0 + cc, h);
-    for (int d = tid >> 4; d < K; d += 16) sl[o.dS + d * V + col] = sdS[d * 17 + c];
-    for (int e = tid; e < C * K; e += kBT) {
-      const int r = e / K, d = e % K;
-      sKG[r * KP + d] = sl[o.kg + e];
-      sQG[r * KP + d] = sl[o.qg + e];
-      sW[r * KP + d] = sl[o.w + e];
-    }
-    for (int e = tid; e < C * C; e += kBT) sAq[(e / C) * CP + e % C] = sl[o.aqk + e];
-    for (int e = tid; e < C * 16; e += kBT) {
-      const int r = e >> 4, cl = e & 15;
-      sdO[r * 17 + cl] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * a.H + h) * V + 16 * vb + cl, qf32) : 0.f;
-    }
-    if (tid < K) sGam[tid] = sl[o.gam + tid];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + t) + 4 * gq + r;
+        sl[o.dS + row * V + col] = dS[t][r];  // gradient of the chunk-end state
+        sdS[row * 17 + xi] = dS[t][r];
+      }
+    if (cc > 0) fetch(cc - 1);
     __syncthreads();
-    for (int i = tid >> 4; i < C; i += 16) {
-      float acc = 0.f;
-      for (int r = i; r < C; ++r) acc += sAq[r * CP + i] * sdO[r * 17 + c];
-      for (int d = 0; d < K; ++d) acc += sKG[i * KP + d] * sdS[d * 17 + c];
-      sdVn[i * 17 + c] = acc;
-    }
-    __syncthreads();
-    for (int d = tid >> 4; d < K; d += 16) {
-      float acc = sGam[d] * sdS[d * 17 + c];
-      for (int r = 0; r < C; ++r) acc += sQG[r * KP + d] * sdO[r * 17 + c] - sW[r * KP + d] * sdVn[r * 17 + c];
-      sdS[d * 17 + c] = acc;
+    // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS'
+    {
+      floatx4 acc = zero4();
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 4)
+        acc = mfma4(sAq[(k0 + gq) * CP + 16 * w + xi], sdO[(k0 + gq) * 17 + xi], acc);
+#pragma unroll 8
+      for (int k0 = 0; k0 < K; k0 += 4)
+        acc = mfma4(sKG[(16 * w + xi) * KP + k0 + gq], sdS[(k0 + gq) * 17 + xi], acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sdVn[(16 * w + 4 * gq + r) * 17 + xi] = acc[r];
     }
     __syncthreads();
+    // dS = Diag(gamma) dS' + Qg^T dO - W^T dVn
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int rt = TPW * w + t;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dS[t][r] *= sGam[16 * rt + 4 * gq + r];
+#pragma unroll 8
+      for (int k0 = 0; k0 < C; k0 += 4) {
+        dS[t] = mfma4(sQG[(k0 + gq) * KP + 16 * rt + xi], sdO[(k0 + gq) * 17 + xi], dS[t]);
+        dS[t] = mfma4(-sW[(k0 + gq) * KP + 16 * rt + xi], sdVn[(k0 + gq) * 17 + xi], dS[t]);
+      }
+    }
   }
-  if (a.dh0)
-    for (int d = tid >> 4; d < K; d += 16) a.dh0[((size_t)u * K + d) * V + col] = sdS[d * 17 + c];
+  if (a.dh0) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + t) + 4 * gq + r;
+        a.dh0[((size_t)u * K + row) * V + col] = dS[t][r];
+      }
+  }
 }
 
 // ------------------------------------------------------------ chunk gradients
+// pointers to the slab arrays of one (chunk, head)
+struct SlabPtrs {
+  float *QN, *KN, *G, *QG, *KG, *W, *KB, *U, *VB, *AQK, *A, *Mm, *BETA, *GAM, *S, *DS, *DO, *VN, *DVN, *DVB, *DQG,
+      *DW, *DKG, *DKB, *DQN, *DKN, *DG, *DAQK, *DA, *T1, *DL, *DGAM;
+};
+__device__ __forceinline__ SlabPtrs slab_ptrs(float* sl, const BwdSlab& o) {
+  SlabPtrs P;
+  P.QN = sl + o.qn; P.KN = sl + o.kn; P.G = sl + o.G; P.QG = sl + o.qg; P.KG = sl + o.kg; P.W = sl + o.w;
+  P.KB = sl + o.kb; P.U = sl + o.u; P.VB = sl + o.vb; P.AQK = sl + o.aqk; P.A = sl + o.a; P.Mm = sl + o.m;
+  P.BETA = sl + o.beta; P.GAM = sl + o.gam; P.S = sl + o.S; P.DS = sl + o.dS; P.DO = sl + o.dO; P.VN = sl + o.vn;
+  P.DVN = sl + o.dvn; P.DVB = sl + o.dvb; P.DQG = sl + o.dqg; P.DW = sl + o.dw; P.DKG = sl + o.dkg;
+  P.DKB = sl + o.dkb; P.DQN = sl + o.dqn; P.DKN = sl + o.dkn; P.DG = sl + o.dG; P.DAQK = sl + o.daqk;
+  P.DA = sl + o.da; P.T1 = sl + o.t1; P.DL = sl + o.dl; P.DGAM = sl + o.dgam;
+  return P;
+}
+
+// the matrix products of the chunk reverse step
 template <int K>
-__global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
   constexpr int V = K;
-  __shared__ float sDot[2 * C];
+  __shared__ __attribute__((aligned(16))) float smem[16 * (C + 4) + 16 * (K + 4)];
+  const int tid = threadIdx.x;
+  if ((int)blockIdx.x >= items_in_use(a)) return;
+  const ItemB it = chunk_of(a, (int)blockIdx.x / a.H, (int)blockIdx.x % a.H);
+  const SlabPtrs P = slab_ptrs(slab_of(a, it.p, it.h), a.sl);
+  const int qf32 = !a.bf16_qkv;
+
+  for (int e = tid; e < C * V; e += kBT) {
+    const int r = e / V, d = e % V;
+    P.DO[e] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * a.H + it.h) * V + d, qf32) : 0.f;
+  }
+  if (tid < K) {
+    float acc = 0.f;
+    for (int v = 0; v < V; ++v) acc += P.S[tid * V + v] * P.DS[tid * V + v];
+    P.DGAM[tid] = acc;
+  }
+  __syncthreads();
+  // Vn = U - W S;  dVn = Aqk^T dO + KG dS'
+  lds_mm<C, V, false, false>(K, P.W, K, P.S, V, smem,
+                             [&](int i, int j, float x) { P.VN[i * V + j] = P.U[i * V + j] - x; });
+  lds_mm<C, V, true, false>(C, P.AQK, C, P.DO, V, smem, [&](int i, int j, float x) { P.DVN[i * V + j] = x; });
+  lds_mm<C, V, false, false>(K, P.KG, K, P.DS, V, smem, [&](int i, int j, float x) { P.DVN[i * V + j] += x; });
+  __syncthreads();
+  // dQg = dO S^T, dW = -dVn S^T, dKG = Vn dS'^T, dAqk = Tril(dO Vn^T)
+  lds_mm<C, K, false, true>(V, P.DO, V, P.S, V, smem, [&](int i, int j, float x) { P.DQG[i * K + j] = x; });
+  lds_mm<C, K, false, true>(V, P.DVN, V, P.S, V, smem, [&](int i, int j, float x) { P.DW[i * K + j] = -x; });
+  lds_mm<C, K, false, true>(V, P.VN, V, P.DS, V, smem, [&](int i, int j, float x) { P.DKG[i * K + j] = x; });
+  lds_mm<C, C, false, true>(V, P.DO, V, P.VN, V, smem,
+                            [&](int i, int j, float x) { P.DAQK[i * C + j] = j <= i ? x : 0.f; });
+  __syncthreads();
+  // dA = dW Kb^T + dVn Vb^T;  dKb = A^T dW;  dVb = A^T dVn
+  lds_mm<C, C, false, true>(K, P.DW, K, P.KB, K, smem, [&](int i, int j, float x) { P.DA[i * C + j] = x; });
+  lds_mm<C, C, false, true>(V, P.DVN, V, P.VB, V, smem, [&](int i, int j, float x) { P.DA[i * C + j] += x; });
+  lds_mm<C, K, true, false>(C, P.A, C, P.DW, K, smem, [&](int i, int j, float x) { P.DKB[i * K + j] = x; });
+  lds_mm<C, V, true, false>(C, P.A, C, P.DVN, V, smem, [&](int i, int j, float x) { P.DVB[i * V + j] = x; });
+  __syncthreads();
+  // dL = -StrictTril(A^T dA A^T)
+  lds_mm<C, C, true, false>(C, P.A, C, P.DA, C, smem, [&](int i, int j, float x) { P.T1[i * C + j] = x; });
+  __syncthreads();
+  lds_mm<C, C, false, true>(C, P.T1, C, P.A, C, smem,
+                            [&](int i, int j, float x) { P.DL[i * C + j] = j < i ? -x : 0.f; });
+}
+
+// the elementwise and gated-sum rules, the L2-norm backward and the reverse
+// cumsum; the operands of the gated sums are staged in LDS
+template <int K>
+__global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
+  constexpr int V = K;
+  __shared__ float sG[C * K], sKN[C * K], sQN[C * K];
+  __shared__ float sDAQK[C * C], sDM[C * C];  // dAqk and dM = Diag(beta) dL
+  __shared__ float sBeta[C], sDot[2 * C];
   const int tid = threadIdx.x;
   if ((int)blockIdx.x >= items_in_use(a)) return;
   const ItemB it = chunk_of(a, (int)blockIdx.x / a.H, (int)blockIdx.x % a.H);
   const BwdSlab& o = a.sl;
   float* sl = slab_of(a, it.p, it.h);
+  const SlabPtrs P = slab_ptrs(sl, o);
   const int H = a.H;
   const int qf32 = !a.bf16_qkv;
   const float s = a.scale;
-  float* const QN = sl + o.qn;
-  float* const KN = sl + o.kn;
-  float* const G = sl + o.G;
-  float* const QG = sl + o.qg;
-  float* const KG = sl + o.kg;
-  float* const W = sl + o.w;
-  float* const KB = sl + o.kb;
-  float* const U = sl + o.u;
-  float* const VB = sl + o.vb;
-  float* const AQK = sl + o.aqk;
-  float* const A = sl + o.a;
-  float* const Mm = sl + o.m;
-  float* const BETA = sl + o.beta;
-  float* const GAM = sl + o.gam;
-  float* const S = sl + o.S;
-  float* const DS = sl + o.dS;
-  float* const DO = sl + o.dO;
-  float* const VN = sl + o.vn;
-  float* const DVN = sl + o.dvn;
-  float* const DVB = sl + o.dvb;
-  float* const DQG = sl + o.dqg;
-  float* const DW = sl + o.dw;
-  float* const DKG = sl + o.dkg;
-  float* const DKB = sl + o.dkb;
-  float* const DQN = sl + o.dqn;
-  float* const DKN = sl + o.dkn;
-  float* const DG = sl + o.dG;
-  float* const DAQK = sl + o.daqk;
-  float* const DA = sl + o.da;
-  float* const T1 = sl + o.t1;
-  float* const DL = sl + o.dl;
-  float* const DGAM = sl + o.dgam;
 
-  for (int e = tid; e < C * V; e += kBT) {
-    const int r = e / V, d = e % V;
-    DO[e] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * H + it.h) * V + d, qf32) : 0.f;
+  if (tid < C) sBeta[tid] = P.BETA[tid];
+  for (int e = tid; e < C * K; e += kBT) {
+    sG[e] = P.G[e];
+    sKN[e] = P.KN[e];
+    sQN[e] = P.QN[e];
   }
   __syncthreads();
-  // Vn = U - W S;  dVn = Aqk^T dO + KG dS'
-  wg_mm<C, V>(K, [&](int i, int kk) { return W[i * K + kk]; }, [&](int kk, int j) { return S[kk * V + j]; },
-              [&](int i, int j, float x) { VN[i * V + j] = U[i * V + j] - x; });
-  wg_mm<C, V>(C + K,
-              [&](int i, int kk) { return kk < C ? AQK[kk * C + i] : KG[i * K + kk - C]; },
-              [&](int kk, int j) { return kk < C ? DO[kk * V + j] : DS[(kk - C) * V + j]; },
-              [&](int i, int j, float x) { DVN[i * V + j] = x; });
-  __syncthreads();
-  // dQg = dO S^T, dW = -dVn S^T, dKG = Vn dS'^T, dAqk = Tril(dO Vn^T), dgamma
-  wg_mm<C, K>(V, [&](int i, int kk) { return DO[i * V + kk]; }, [&](int kk, int j) { return S[j * V + kk]; },
-              [&](int i, int j, float x) { DQG[i * K + j] = x; });
-  wg_mm<C, K>(V, [&](int i, int kk) { return DVN[i * V + kk]; }, [&](int kk, int j) { return S[j * V + kk]; },
-              [&](int i, int j, float x) { DW[i * K + j] = -x; });
-  wg_mm<C, K>(V, [&](int i, int kk) { return VN[i * V + kk]; }, [&](int kk, int j) { return DS[j * V + kk]; },
-              [&](int i, int j, float x) { DKG[i * K + j] = x; });
-  wg_mm<C, C>(V, [&](int i, int kk) { return DO[i * V + kk]; }, [&](int kk, int j) { return VN[j * V + kk]; },
-              [&](int i, int j, float x) { DAQK[i * C + j] = j <= i ? x : 0.f; });
-  if (tid < K) {
-    float acc = 0.f;
-    for (int v = 0; v < V; ++v) acc += S[tid * V + v] * DS[tid * V + v];
-    DGAM[tid] = acc;
+  for (int e = tid; e < C * C; e += kBT) {
+    sDAQK[e] = P.DAQK[e];
+    sDM[e] = sBeta[e / C] * P.DL[e];
   }
-  __syncthreads();
-  // dA = dW Kb^T + dVn Vb^T;  dKb = A^T dW;  dVb = A^T dVn
-  wg_mm<C, C>(K + V,
-              [&](int i, int kk) { return kk < K ? DW[i * K + kk] : DVN[i * V + kk - K]; },
-              [&](int kk, int j) { return kk < K ? KB[j * K + kk] : VB[j * V + kk - K]; },
-              [&](int i, int j, float x) { DA[i * C + j] = x; });
-  wg_mm<C, K>(C, [&](int i, int kk) { return A[kk * C + i]; }, [&](int kk, int j) { return DW[kk * K + j]; },
-              [&](int i, int j, float x) { DKB[i * K + j] = x; });
-  wg_mm<C, V>(C, [&](int i, int kk) { return A[kk * C + i]; }, [&](int kk, int j) { return DVN[kk * V + j]; },
-              [&](int i, int j, float x) { DVB[i * V + j] = x; });
-  __syncthreads();
-  // dL = -StrictTril(A^T dA A^T)
-  wg_mm<C, C>(C, [&](int i, int kk) { return A[kk * C + i]; }, [&](int kk, int j) { return DA[kk * C + j]; },
-              [&](int i, int j, float x) { T1[i * C + j] = x; });
-  __syncthreads();
-  wg_mm<C, C>(C, [&](int i, int kk) { return T1[i * C + kk]; }, [&](int kk, int j) { return A[j * C + kk]; },
-              [&](int i, int j, float x) { DL[i * C + j] = j < i ? -x : 0.f; });
   __syncthreads();
 
   // per element: thread -> channel d, rows i = tid / K + (256 / K) m
   {
     const int d = tid % K;
     constexpr int RS = kBT / K;
-    const float Gl = G[(C - 1) * K + d];
+    const float Gl = sG[(C - 1) * K + d];
     for (int i = tid / K; i < C; i += RS) {
-      const float Gi = G[i * K + d], qi = QN[i * K + d], ki = KN[i * K + d], bi = BETA[i];
+      const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
       float sAq = 0.f, sMq = 0.f;  // query side: keys j <= i
       for (int j = 0; j <= i; ++j) {
-        const float kE = KN[j * K + d] * __expf(Gi - G[j * K + d]);
-        sAq += DAQK[i * C + j] * kE;
-        sMq += bi * DL[i * C + j] * kE;
+        const float kE = sKN[j * K + d] * __expf(Gi - sG[j * K + d]);
+        sAq += sDAQK[i * C + j] * kE;
+        sMq += sDM[i * C + j] * kE;
       }
       float sAk = 0.f, sMk = 0.f;  // key side: queries r >= i
       for (int r = i; r < C; ++r) {
-        const float E = __expf(G[r * K + d] - Gi);
-        sAk += DAQK[r * C + i] * QN[r * K + d] * E;
-        sMk += BETA[r] * DL[r * C + i] * KN[r * K + d] * E;
+        const float E = __expf(sG[r * K + d] - Gi);
+        sAk += sDAQK[r * C + i] * sQN[r * K + d] * E;
+        sMk += sDM[r * C + i] * sKN[r * K + d] * E;
       }
       const float eg = __expf(Gi);
-      const float dqg = DQG[i * K + d], dkb = DKB[i * K + d], dkg = DKG[i * K + d];
-      DQN[i * K + d] = s * eg * dqg + s * sAq;
-      DKN[i * K + d] = dkb * bi * eg + dkg * __expf(Gl - Gi) + s * sAk + sMq + sMk;
-      float dG = dqg * QG[i * K + d] + dkb * KB[i * K + d] - dkg * KG[i * K + d] + qi * s * sAq - ki * s * sAk +
-                 ki * sMq - ki * sMk;
+      const float dqg = P.DQG[i * K + d], dkb = P.DKB[i * K + d], dkg = P.DKG[i * K + d];
+      P.DQN[i * K + d] = s * eg * dqg + s * sAq;
+      P.DKN[i * K + d] = dkb * bi * eg + dkg * __expf(Gl - Gi) + s * sAk + sMq + sMk;
+      float dG = dqg * P.QG[i * K + d] + dkb * P.KB[i * K + d] - dkg * P.KG[i * K + d] + qi * s * sAq -
+                 ki * s * sAk + ki * sMq - ki * sMk;
       if (i == C - 1) {
-        float dGl = DGAM[d] * GAM[d];
-        for (int r = 0; r < C; ++r) dGl += DKG[r * K + d] * KG[r * K + d];
+        float dGl = P.DGAM[d] * P.GAM[d];
+        for (int r = 0; r < C; ++r) dGl += P.DKG[r * K + d] * P.KG[r * K + d];
         dG += dGl;
       }
-      DG[i * K + d] = dG;
+      P.DG[i * K + d] = dG;
     }
   }
   // dbeta and dv: thread -> row
   if (tid < C) {
     const int i = tid;
-    float db = 0.f;
     if (i < it.len) {
+      float db = 0.f;
       const size_t vrow = ((size_t)(it.tok0 + i) * H + it.h) * V;
       for (int v = 0; v < V; ++v) {
-        const float dvb = DVB[i * V + v];
+        const float dvb = P.DVB[i * V + v];
         db += dvb * ldx(a.v, vrow + v, qf32);
-        a.dv[vrow + v] = BETA[i] * dvb;
+        a.dv[vrow + v] = sBeta[i] * dvb;
       }
-      for (int d = 0; d < K; ++d) db += DKB[i * K + d] * KN[i * K + d] * __expf(G[i * K + d]);
-      for (int j = 0; j < i; ++j) db += DL[i * C + j] * Mm[i * C + j];
+      for (int d = 0; d < K; ++d) db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
+      for (int j = 0; j < i; ++j) db += P.DL[i * C + j] * P.Mm[i * C + j];
       a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
     }
   }
@@ -488,8 +650,8 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdArgs a) {
   // L2-norm backward: row dot products q^ . dq^ and k^ . dk^
   if (tid < 2 * C) {
     const int r = tid % C;
-    const float* X = tid < C ? QN : KN;
-    const float* D = tid < C ? DQN : DKN;
+    const float* X = tid < C ? sQN : sKN;
+    const float* D = tid < C ? P.DQN : P.DKN;
     float acc = 0.f;
     for (int d = 0; d < K; ++d) acc += X[r * K + d] * D[r * K + d];
     sDot[tid] = acc;
@@ -499,11 +661,11 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdArgs a) {
     const int r = e / K, d = e % K;
     if (r >= it.len) continue;
     const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
-    float gq = DQN[e], gk = DKN[e];
+    float gq = P.DQN[e], gk = P.DKN[e];
     if (a.l2norm) {
       const float nq = sl[o.nq + r], nk = sl[o.nk + r];
-      gq = nq > a.l2eps ? (gq - QN[e] * sDot[r]) / nq : gq / a.l2eps;
-      gk = nk > a.l2eps ? (gk - KN[e] * sDot[C + r]) / nk : gk / a.l2eps;
+      gq = nq > a.l2eps ? (gq - sQN[e] * sDot[r]) / nq : gq / a.l2eps;
+      gk = nk > a.l2eps ? (gk - sKN[e] * sDot[C + r]) / nk : gk / a.l2eps;
     }
     a.dq[idx] = gq;
     a.dk[idx] = gk;
@@ -513,7 +675,7 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_kernel(BwdArgs a) {
     const int d = tid;
     float run = 0.f;
     for (int r = C - 1; r >= 0; --r) {
-      run += DG[r * K + d];
+      run += P.DG[r * K + d];
       if (r < it.len) a.dg[((size_t)(it.tok0 + r) * H + it.h) * K + d] = run;
     }
   }
@@ -529,7 +691,10 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
       hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
     if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
   }
-  if ((stages & 8) && nitems > 0) hipLaunchKernelGGL(bwd_chunk_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+  if ((stages & 8) && nitems > 0) {
+    hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+    hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+  }
   return hipGetLastError();
 }
 
