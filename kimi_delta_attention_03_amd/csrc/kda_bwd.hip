@@ -82,6 +82,12 @@ __device__ __forceinline__ void seq_chunks(const BwdArgs& a, int seq, int& p0, i
   }
 }
 
+// fp32 16x16x4 MFMA step: lane (g, i) = (l / 16, l % 16) gives A[i][g] and
+// B[g][i] of a 4-deep slice; the accumulator lane holds rows 4 g + r, column i
+__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // out(i, j) = sum_kk A(i, kk) B(kk, j) for an M x N result over KD (a multiple
 // of 16), with A(i, kk) = A[i * lda + kk] (TA: A[kk * lda + i]) and B(kk, j) =
 // B[kk * ldb + j] (TB: B[j * ldb + kk]). 16-deep slices of both operands are
@@ -226,23 +232,45 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   if (tid < K) sl[o.gam + tid] = __expf(sG[(C - 1) * KP + tid]);
   if (tid < C) sl[o.beta + tid] = sB[tid];
 
-  // relation tiles: thread -> row i, columns j = tid % 4 + 4 m
+  // relation tiles (query block ib, key block jb <= ib) on fp32 MFMA with the
+  // key block's first row as reference: q_i exp(G_i - rho) <= |q_i| for i in
+  // block ib >= jb, k_j exp(rho - G_j) spans at most 15 steps of decay
   {
-    const int i = tid >> 2;
-    for (int m = 0; m < C / 4; ++m) {
-      const int j = (tid & 3) + 4 * m;
-      float aq = 0.f, mm = 0.f;
-      if (j <= i) {
-        for (int d = 0; d < K; ++d) {
-          const float kj = sK[j * KP + d] * __expf(sG[i * KP + d] - sG[j * KP + d]);
-          aq += sQ[i * KP + d] * kj;
-          mm += sK[i * KP + d] * kj;
-        }
+    const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    for (int t = w; t < 10; t += 4) {
+      // t -> (ib, jb) over the 10 causal block pairs
+      const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      const int jb = t - ib * (ib + 1) / 2;
+      floatx4 accQ = zero4(), accK = zero4();
+      const int i = 16 * ib + xi, j = 16 * jb + xi;
+#pragma unroll 4
+      for (int k0 = 0; k0 < K; k0 += 4) {
+        const int d = k0 + gq;
+        const float rho = sG[(16 * jb) * KP + d];
+        const float ei = __expf(sG[i * KP + d] - rho);
+        const float kj = sK[j * KP + d] * __expf(rho - sG[j * KP + d]);
+        accQ = mfma4(sQ[i * KP + d] * ei, kj, accQ);
+        accK = mfma4(sK[i * KP + d] * ei, kj, accK);
       }
-      const float mv = j < i ? mm : 0.f;
-      sl[o.aqk + i * C + j] = a.scale * aq;
-      sl[o.m + i * C + j] = mv;
-      sL[i * CP + j] = sB[i] * mv;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 16 * ib + 4 * gq + r, jj = 16 * jb + xi;
+        const float aq = jj <= ii ? a.scale * accQ[r] : 0.f;
+        const float mv = jj < ii ? accK[r] : 0.f;
+        sl[o.aqk + ii * C + jj] = aq;
+        sl[o.m + ii * C + jj] = mv;
+        sL[ii * CP + jj] = sB[ii] * mv;
+      }
+    }
+    // the blocks above the diagonal are zero
+    for (int e = tid; e < C * C; e += kBT) {
+      const int ii = e / C, jj = e % C;
+      if (jj / 16 > ii / 16) {
+        sl[o.aqk + e] = 0.f;
+        sl[o.m + e] = 0.f;
+        sL[ii * CP + jj] = 0.f;
+      }
     }
   }
   __syncthreads();
@@ -266,26 +294,28 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
   for (int e = tid; e < C * C; e += kBT) sl[o.a + e] = sA[(e / C) * CP + e % C];
 
-  // W = A Kb, U = A Vb: thread -> channel d, rows i = tid / K + (256 / K) m
+  // W = A Kb, U = A Vb on fp32 MFMA: output tile (row block ib, 16 channels ct),
+  // reduction over the key rows j < 16 (ib + 1) (A is lower triangular)
   {
-    const int d = tid % K;
-    constexpr int RS = kBT / K;
-    float kb[C], vb[C];
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      kb[j] = sB[j] * sK[j * KP + d] * __expf(sG[j * KP + d]);
-      vb[j] = sl[o.vb + j * V + d];
-    }
-    for (int i = tid / K; i < C; i += RS) {
-      float w = 0.f, u = 0.f;
-#pragma unroll
-      for (int j = 0; j < C; ++j) {  // A is zero above the diagonal
-        const float aij = sA[i * CP + j];
-        w += aij * kb[j];
-        u += aij * vb[j];
+    const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    constexpr int NCT = K / 16;
+    for (int t = w; t < 4 * NCT; t += 4) {
+      const int ib = t / NCT, ct = t % NCT;
+      const int d = 16 * ct + xi;
+      floatx4 accW = zero4(), accU = zero4();
+      for (int k0 = 0; k0 < 16 * (ib + 1); k0 += 4) {
+        const int j = k0 + gq;
+        const float aij = sA[(16 * ib + xi) * CP + j];
+        accW = mfma4(aij, sB[j] * sK[j * KP + d] * __expf(sG[j * KP + d]), accW);
+        accU = mfma4(aij, sl[o.vb + j * V + d], accU);
       }
-      sl[o.w + i * K + d] = w;
-      sl[o.u + i * V + d] = u;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ii = 16 * ib + 4 * gq + r;
+        sl[o.w + ii * K + d] = accW[r];
+        sl[o.u + ii * V + d] = accU[r];
+      }
     }
   }
 }
@@ -297,9 +327,6 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
 // column i of a 16 x 16 tile; an A operand lane holds row i, reduction index g of
 // a 4-deep slice, a B operand lane reduction index g, column i). The next
 // chunk's operands are loaded into registers while the current chunk computes.
-__device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int K>
 __global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
@@ -567,14 +594,27 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
 }
 
 // the elementwise and gated-sum rules, the L2-norm backward and the reverse
-// cumsum; the operands of the gated sums are staged in LDS
+// cumsum. The four gated sums (per row i, channel d; P = dAqk, dM = Diag(beta) dL,
+// E_ij = exp(G_i - G_j))
+//   query side  sum_{j<=i} P_ij k_j E_ij,   sum_{j<i} dM_ij k_j E_ij
+//   key side    sum_{r>=i} P_ri q_r E_ri,   sum_{r>i} dM_ri k_r E_ri
+// run as fp32 MFMA products over 16-row blocks with one reference per block
+// (the rebasing of "KDA Doesn't Care About the Future", section "The rebasing
+// trick"): with rho_b = G of the first row of block b, a key j of block b
+// carries exp(rho_b - G_j) (at most 15 steps of decay) and the query row
+// exp(G_i - rho_b) <= 1 for i >= 16 b; the key side uses the reference of row
+// i's own block the same way.
 template <int K>
 __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
   constexpr int V = K;
-  __shared__ float sG[C * K], sKN[C * K], sQN[C * K];
-  __shared__ float sDAQK[C * C], sDM[C * C];  // dAqk and dM = Diag(beta) dL
-  __shared__ float sBeta[C], sDot[2 * C];
+  constexpr int CP = C + 4;
+  constexpr int NCT = K / 16;  // 16-channel column tiles
+  __shared__ __attribute__((aligned(16))) float sG[C * K], sKN[C * K], sQN[C * K];
+  __shared__ float sP[C * CP], sDM[C * CP];  // dAqk and dM = Diag(beta) dL
+  __shared__ float sBeta[C], sDot[2 * C], sDGl[K];
   const int tid = threadIdx.x;
+  const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.x >= items_in_use(a)) return;
   const ItemB it = chunk_of(a, (int)blockIdx.x / a.H, (int)blockIdx.x % a.H);
   const BwdSlab& o = a.sl;
@@ -585,66 +625,100 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
   const float s = a.scale;
 
   if (tid < C) sBeta[tid] = P.BETA[tid];
-  for (int e = tid; e < C * K; e += kBT) {
-    sG[e] = P.G[e];
-    sKN[e] = P.KN[e];
-    sQN[e] = P.QN[e];
+  for (int e = tid; e < C * K / 4; e += kBT) {
+    reinterpret_cast<floatx4*>(sG)[e] = reinterpret_cast<const floatx4*>(P.G)[e];
+    reinterpret_cast<floatx4*>(sKN)[e] = reinterpret_cast<const floatx4*>(P.KN)[e];
+    reinterpret_cast<floatx4*>(sQN)[e] = reinterpret_cast<const floatx4*>(P.QN)[e];
+  }
+  // gradient of the last row's cumulative gate through KG and gamma
+  if (tid < K) {
+    float acc = P.DGAM[tid] * P.GAM[tid];
+    for (int r = 0; r < C; ++r) acc += P.DKG[r * K + tid] * P.KG[r * K + tid];
+    sDGl[tid] = acc;
   }
   __syncthreads();
   for (int e = tid; e < C * C; e += kBT) {
-    sDAQK[e] = P.DAQK[e];
-    sDM[e] = sBeta[e / C] * P.DL[e];
+    sP[(e / C) * CP + e % C] = P.DAQK[e];
+    sDM[(e / C) * CP + e % C] = sBeta[e / C] * P.DL[e];
   }
   __syncthreads();
 
-  // per element: thread -> channel d, rows i = tid / K + (256 / K) m
-  {
-    const int d = tid % K;
-    constexpr int RS = kBT / K;
-    const float Gl = sG[(C - 1) * K + d];
-    for (int i = tid / K; i < C; i += RS) {
+  // output tiles (row block ib, channel tile ct): wave w takes every 4th
+  for (int tile = w; tile < 4 * NCT; tile += 4) {
+    const int ib = tile / NCT, ct = tile % NCT;
+    const int d = 16 * ct + xi;
+    floatx4 qa = zero4(), qm = zero4(), ka = zero4(), km = zero4();
+    // query side: key blocks b <= ib
+    for (int b = 0; b <= ib; ++b) {
+      const float rho = sG[(16 * b) * K + d];
+      floatx4 accA = zero4(), accM = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const int j = 16 * b + k0 + gq;
+        const float kf = sKN[j * K + d] * __expf(rho - sG[j * K + d]);
+        accA = mfma4(sP[(16 * ib + xi) * CP + j], kf, accA);
+        accM = mfma4(sDM[(16 * ib + xi) * CP + j], kf, accM);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __expf(sG[(16 * ib + 4 * gq + r) * K + d] - rho);
+        qa[r] += e * accA[r];
+        qm[r] += e * accM[r];
+      }
+    }
+    // key side: query blocks b >= ib, reference of block ib
+    {
+      const float rho = sG[(16 * ib) * K + d];
+      for (int b = ib; b < 4; ++b) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int r = 16 * b + k0 + gq;
+          const float e = __expf(sG[r * K + d] - rho);
+          ka = mfma4(sP[r * CP + 16 * ib + xi], sQN[r * K + d] * e, ka);
+          km = mfma4(sDM[r * CP + 16 * ib + xi], sKN[r * K + d] * e, km);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float f = __expf(rho - sG[(16 * ib + 4 * gq + r) * K + d]);
+        ka[r] *= f;
+        km[r] *= f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ib + 4 * gq + r;
       const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
-      float sAq = 0.f, sMq = 0.f;  // query side: keys j <= i
-      for (int j = 0; j <= i; ++j) {
-        const float kE = sKN[j * K + d] * __expf(Gi - sG[j * K + d]);
-        sAq += sDAQK[i * C + j] * kE;
-        sMq += sDM[i * C + j] * kE;
-      }
-      float sAk = 0.f, sMk = 0.f;  // key side: queries r >= i
-      for (int r = i; r < C; ++r) {
-        const float E = __expf(sG[r * K + d] - Gi);
-        sAk += sDAQK[r * C + i] * sQN[r * K + d] * E;
-        sMk += sDM[r * C + i] * sKN[r * K + d] * E;
-      }
+      const float Gl = sG[(C - 1) * K + d];
       const float eg = __expf(Gi);
       const float dqg = P.DQG[i * K + d], dkb = P.DKB[i * K + d], dkg = P.DKG[i * K + d];
-      P.DQN[i * K + d] = s * eg * dqg + s * sAq;
-      P.DKN[i * K + d] = dkb * bi * eg + dkg * __expf(Gl - Gi) + s * sAk + sMq + sMk;
-      float dG = dqg * P.QG[i * K + d] + dkb * P.KB[i * K + d] - dkg * P.KG[i * K + d] + qi * s * sAq -
-                 ki * s * sAk + ki * sMq - ki * sMk;
-      if (i == C - 1) {
-        float dGl = P.DGAM[d] * P.GAM[d];
-        for (int r = 0; r < C; ++r) dGl += P.DKG[r * K + d] * P.KG[r * K + d];
-        dG += dGl;
-      }
+      P.DQN[i * K + d] = s * eg * dqg + s * qa[r];
+      P.DKN[i * K + d] = dkb * bi * eg + dkg * __expf(Gl - Gi) + s * ka[r] + qm[r] + km[r];
+      float dG = dqg * P.QG[i * K + d] + dkb * P.KB[i * K + d] - dkg * P.KG[i * K + d] + qi * s * qa[r] -
+                 ki * s * ka[r] + ki * qm[r] - ki * km[r];
+      if (i == C - 1) dG += sDGl[d];
       P.DG[i * K + d] = dG;
     }
   }
-  // dbeta and dv: thread -> row
-  if (tid < C) {
-    const int i = tid;
+  __syncthreads();
+  // dbeta and dv: four threads per row, each over a quarter of the channels
+  {
+    const int i = tid >> 2, part = tid & 3;
+    float db = 0.f;
     if (i < it.len) {
-      float db = 0.f;
       const size_t vrow = ((size_t)(it.tok0 + i) * H + it.h) * V;
-      for (int v = 0; v < V; ++v) {
+      for (int v = part * (V / 4); v < (part + 1) * (V / 4); ++v) {
         const float dvb = P.DVB[i * V + v];
         db += dvb * ldx(a.v, vrow + v, qf32);
         a.dv[vrow + v] = sBeta[i] * dvb;
       }
-      for (int d = 0; d < K; ++d) db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
-      for (int j = 0; j < i; ++j) db += P.DL[i * C + j] * P.Mm[i * C + j];
-      a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
+      for (int d = part * (K / 4); d < (part + 1) * (K / 4); ++d)
+        db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
+      for (int j = part; j < i; j += 4) db += P.DL[i * C + j] * P.Mm[i * C + j];
     }
+    db += __shfl_xor(db, 1, 64);
+    db += __shfl_xor(db, 2, 64);
+    if (part == 0 && i < it.len) a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
   }
   __syncthreads();
   // L2-norm backward: row dot products q^ . dq^ and k^ . dk^
@@ -661,14 +735,14 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
     const int r = e / K, d = e % K;
     if (r >= it.len) continue;
     const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
-    float gq = P.DQN[e], gk = P.DKN[e];
+    float gradq = P.DQN[e], gradk = P.DKN[e];
     if (a.l2norm) {
       const float nq = sl[o.nq + r], nk = sl[o.nk + r];
-      gq = nq > a.l2eps ? (gq - sQN[e] * sDot[r]) / nq : gq / a.l2eps;
-      gk = nk > a.l2eps ? (gk - sKN[e] * sDot[C + r]) / nk : gk / a.l2eps;
+      gradq = nq > a.l2eps ? (gradq - sQN[e] * sDot[r]) / nq : gradq / a.l2eps;
+      gradk = nk > a.l2eps ? (gradk - sKN[e] * sDot[C + r]) / nk : gradk / a.l2eps;
     }
-    a.dq[idx] = gq;
-    a.dk[idx] = gk;
+    a.dq[idx] = gradq;
+    a.dk[idx] = gradk;
   }
   // dg = reverse cumsum of dG over the chunk
   if (tid < K) {
