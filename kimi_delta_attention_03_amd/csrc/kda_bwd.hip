@@ -36,6 +36,8 @@ namespace kda {
 namespace {
 
 constexpr int kBT = 256;  // threads per workgroup
+constexpr int kBW = 512;  // threads of the per-chunk rebuild and elementwise kernels
+constexpr int kNWW = kBW / 64;
 constexpr int C = kChunk;
 
 __device__ __forceinline__ float ldx(const void* p, size_t i, int f32) {
@@ -157,7 +159,7 @@ __device__ __forceinline__ void lds_mm(int KD, const float* A, int lda, const fl
 
 // ---------------------------------------------------------------- prep
 template <int K>
-__global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
   constexpr int V = K;
   constexpr int KP = K + 1;
   constexpr int CP = C + 1;
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   const int qf32 = !a.bf16_qkv;
 
   // rows of q, k, g (rows past the chunk end are zero tokens)
-  for (int e = tid; e < C * K; e += kBT) {
+  for (int e = tid; e < C * K; e += kBW) {
     const int r = e / K, d = e % K;
     float qv = 0.f, kv = 0.f, gv = 0.f;
     if (r < it.len) {
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
 
   // elementwise terms
-  for (int e = tid; e < C * K; e += kBT) {
+  for (int e = tid; e < C * K; e += kBW) {
     const int r = e / K, d = e % K;
     const float G = sG[r * KP + d], Gl = sG[(C - 1) * KP + d];
     const float qn = sQ[r * KP + d], kn = sK[r * KP + d];
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
     sl[o.kg + e] = kn * __expf(Gl - G);
     sl[o.kb + e] = sB[r] * kn * eg;
   }
-  for (int e = tid; e < C * V; e += kBT) {
+  for (int e = tid; e < C * V; e += kBW) {
     const int r = e / V, d = e % V;
     const float vv = r < it.len ? ldx(a.v, ((size_t)(it.tok0 + r) * H + it.h) * V + d, qf32) : 0.f;
     sl[o.vb + e] = sB[r] * vv;
@@ -238,7 +240,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
   {
     const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    for (int t = w; t < 10; t += 4) {
+    for (int t = w; t < 10; t += kNWW) {
       // t -> (ib, jb) over the 10 causal block pairs
       const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
       const int jb = t - ib * (ib + 1) / 2;
@@ -264,7 +266,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
       }
     }
     // the blocks above the diagonal are zero
-    for (int e = tid; e < C * C; e += kBT) {
+    for (int e = tid; e < C * C; e += kBW) {
       const int ii = e / C, jj = e % C;
       if (jj / 16 > ii / 16) {
         sl[o.aqk + e] = 0.f;
@@ -292,7 +294,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
     for (int i = 0; i < C; ++i) sA[i * CP + j] = x[i];
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += kBT) sl[o.a + e] = sA[(e / C) * CP + e % C];
+  for (int e = tid; e < C * C; e += kBW) sl[o.a + e] = sA[(e / C) * CP + e % C];
 
   // W = A Kb, U = A Vb on fp32 MFMA: output tile (row block ib, 16 channels ct),
   // reduction over the key rows j < 16 (ib + 1) (A is lower triangular)
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(kBT) void bwd_prep_kernel(BwdArgs a) {
     const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     constexpr int NCT = K / 16;
-    for (int t = w; t < 4 * NCT; t += 4) {
+    for (int t = w; t < 4 * NCT; t += kNWW) {
       const int ib = t / NCT, ct = t % NCT;
       const int d = 16 * ct + xi;
       floatx4 accW = zero4(), accU = zero4();
@@ -605,7 +607,7 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
 // exp(G_i - rho_b) <= 1 for i >= 16 b; the key side uses the reference of row
 // i's own block the same way.
 template <int K>
-__global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   constexpr int V = K;
   constexpr int CP = C + 4;
   constexpr int NCT = K / 16;  // 16-channel column tiles
@@ -625,7 +627,7 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
   const float s = a.scale;
 
   if (tid < C) sBeta[tid] = P.BETA[tid];
-  for (int e = tid; e < C * K / 4; e += kBT) {
+  for (int e = tid; e < C * K / 4; e += kBW) {
     reinterpret_cast<floatx4*>(sG)[e] = reinterpret_cast<const floatx4*>(P.G)[e];
     reinterpret_cast<floatx4*>(sKN)[e] = reinterpret_cast<const floatx4*>(P.KN)[e];
     reinterpret_cast<floatx4*>(sQN)[e] = reinterpret_cast<const floatx4*>(P.QN)[e];
@@ -637,14 +639,14 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
     sDGl[tid] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += kBT) {
+  for (int e = tid; e < C * C; e += kBW) {
     sP[(e / C) * CP + e % C] = P.DAQK[e];
     sDM[(e / C) * CP + e % C] = sBeta[e / C] * P.DL[e];
   }
   __syncthreads();
 
   // output tiles (row block ib, channel tile ct): wave w takes every 4th
-  for (int tile = w; tile < 4 * NCT; tile += 4) {
+  for (int tile = w; tile < 4 * NCT; tile += kNWW) {
     const int ib = tile / NCT, ct = tile % NCT;
     const int d = 16 * ct + xi;
     floatx4 qa = zero4(), qm = zero4(), ka = zero4(), km = zero4();
@@ -701,23 +703,24 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // dbeta and dv: four threads per row, each over a quarter of the channels
+  // dbeta and dv: eight threads per row, each over an eighth of the channels
   {
-    const int i = tid >> 2, part = tid & 3;
+    const int i = tid >> 3, part = tid & 7;
     float db = 0.f;
     if (i < it.len) {
       const size_t vrow = ((size_t)(it.tok0 + i) * H + it.h) * V;
-      for (int v = part * (V / 4); v < (part + 1) * (V / 4); ++v) {
+      for (int v = part * (V / 8); v < (part + 1) * (V / 8); ++v) {
         const float dvb = P.DVB[i * V + v];
         db += dvb * ldx(a.v, vrow + v, qf32);
         a.dv[vrow + v] = sBeta[i] * dvb;
       }
-      for (int d = part * (K / 4); d < (part + 1) * (K / 4); ++d)
+      for (int d = part * (K / 8); d < (part + 1) * (K / 8); ++d)
         db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
-      for (int j = part; j < i; j += 4) db += P.DL[i * C + j] * P.Mm[i * C + j];
+      for (int j = part; j < i; j += 8) db += P.DL[i * C + j] * P.Mm[i * C + j];
     }
     db += __shfl_xor(db, 1, 64);
     db += __shfl_xor(db, 2, 64);
+    db += __shfl_xor(db, 4, 64);
     if (part == 0 && i < it.len) a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
   }
   __syncthreads();
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
     sDot[tid] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < C * K; e += kBT) {
+  for (int e = tid; e < C * K; e += kBW) {
     const int r = e / K, d = e % K;
     if (r >= it.len) continue;
     const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_elem_kernel(BwdArgs a) {
 template <int K>
 hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   const int nvb = K / 16;
-  if ((stages & 1) && nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+  if ((stages & 1) && nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
   if (a.nunits > 0) {
     if ((stages & 2) && nitems > 0)
       hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
@@ -767,7 +770,7 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   }
   if ((stages & 8) && nitems > 0) {
     hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
-    hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+    hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
   }
   return hipGetLastError();
 }
