@@ -36,7 +36,7 @@ namespace kda {
 namespace {
 
 constexpr int kBT = 256;  // threads per workgroup
-constexpr int kBW = 512;  // threads of the per-chunk rebuild and elementwise kernels
+constexpr int kBW = 1024;  // threads of the per-chunk rebuild and elementwise kernels
 constexpr int kNWW = kBW / 64;
 constexpr int C = kChunk;
 
@@ -703,24 +703,24 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     }
   }
   __syncthreads();
-  // dbeta and dv: eight threads per row, each over an eighth of the channels
+  // dbeta and dv: TPR consecutive threads per row, each over a share of the channels
   {
-    const int i = tid >> 3, part = tid & 7;
+    constexpr int TPR = kBW / C;
+    const int i = tid / TPR, part = tid % TPR;
     float db = 0.f;
     if (i < it.len) {
       const size_t vrow = ((size_t)(it.tok0 + i) * H + it.h) * V;
-      for (int v = part * (V / 8); v < (part + 1) * (V / 8); ++v) {
+      for (int v = part * (V / TPR); v < (part + 1) * (V / TPR); ++v) {
         const float dvb = P.DVB[i * V + v];
         db += dvb * ldx(a.v, vrow + v, qf32);
         a.dv[vrow + v] = sBeta[i] * dvb;
       }
-      for (int d = part * (K / 8); d < (part + 1) * (K / 8); ++d)
+      for (int d = part * (K / TPR); d < (part + 1) * (K / TPR); ++d)
         db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
-      for (int j = part; j < i; j += 8) db += P.DL[i * C + j] * P.Mm[i * C + j];
+      for (int j = part; j < i; j += TPR) db += P.DL[i * C + j] * P.Mm[i * C + j];
     }
-    db += __shfl_xor(db, 1, 64);
-    db += __shfl_xor(db, 2, 64);
-    db += __shfl_xor(db, 4, 64);
+#pragma unroll
+    for (int off = 1; off < TPR; off <<= 1) db += __shfl_xor(db, off, 64);
     if (part == 0 && i < it.len) a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
   }
   __syncthreads();
