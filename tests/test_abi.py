@@ -202,3 +202,45 @@ def test_decode_rejects_bad_params_before_launch(lib):
     assert lib.kda_decode_step(ctypes.byref(p), vp, vp, vp, vp, vp, None, vp, None) == 1
     p = make_params(0, 1, 4, 128, 128, 1, 1, 1, 0.1)           # empty batch: nothing to do
     assert lib.kda_decode_step(ctypes.byref(p), None, None, None, None, None, None, None, None) == 0
+
+
+def test_backward_workspace_formula(lib):
+    """Backward workspace = forward metadata + one fp32 slab per (chunk slot, head):
+    14 [64 x K] + 6 [64 x V] + 7 [64 x 64] matrices, 3 row vectors, 2 [K] vectors and
+    2 [K x V] states, rounded up to 64 floats."""
+    for K in (64, 128):
+        p = P(K=K, V=K, B=2, T=256, H=3)
+        n = ctypes.c_size_t(0)
+        assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+        info = _lib.KdaWorkspaceInfo()
+        assert lib.kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
+        slab = 14 * 64 * K + 6 * 64 * K + 7 * 64 * 64 + 3 * 64 + 2 * K + 2 * K * K
+        slab = (slab + 63) // 64 * 64
+        assert n.value == info.records_offset + info.chunk_slots * 3 * slab * 4
+
+
+def test_backward_rejects_before_launch(lib):
+    """Bad stage masks, workspace, pointers and alignment are reported without a launch."""
+    p = P()
+    null = None
+    fake = ctypes.c_void_p(1 << 20)
+    n = ctypes.c_size_t(0)
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
+    args = [null] * 15                            # q, k, v, g, beta, h0, cu, d_o, d_final, 6 gradients
+    assert lib.kda_chunk_bwd(ctypes.byref(p), *args, null, 0, null) == 3          # no workspace
+    assert lib.kda_chunk_bwd(ctypes.byref(p), *args, fake, 1024, null) == 3       # too small
+    assert b"too small" in lib.kda_last_error()
+    assert lib.kda_chunk_bwd(ctypes.byref(p), *args, fake, n.value, null) == 1    # inputs missing
+    vp = ctypes.c_void_p(4096)
+    ins = [vp] * 5 + [null, null, vp, null]      # q, k, v, g, beta, h0, cu, d_o, d_final
+    assert lib.kda_chunk_bwd(ctypes.byref(p), *ins, null, null, null, null, null, null, fake, n.value, null) == 1
+    assert b"dq" in lib.kda_last_error()          # gradient outputs missing
+    mis = ctypes.c_void_p(4096 + 1)               # odd: misaligned for bf16 and fp32 alike
+    outs = [vp] * 5 + [null]
+    assert lib.kda_chunk_bwd(ctypes.byref(p), mis, *ins[1:], *outs, fake, n.value, null) == 1
+    assert b"aligned" in lib.kda_last_error()
+    for bad in (0, 16, -1):
+        assert lib.kda_chunk_bwd_stages(ctypes.byref(p), bad, *ins, *outs, fake, n.value, null) == 1
+    pv = P(num_seqs=2, T=100)                      # varlen without cu_seqlens
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(pv), ctypes.byref(n)) == 0
+    assert lib.kda_chunk_bwd(ctypes.byref(pv), *ins, *outs, fake, n.value, null) == 1
