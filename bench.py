@@ -54,6 +54,7 @@ def alg_bytes_per_token_head(K, V, elem, gelem, belem):
 KERNEL_SOURCES = {
     "stage12": ["kda_stage12.hip", "kda_device.h", "kda_layout.h", "kda_kernels.h"],
     "stage34": ["kda_stage34.hip", "kda_device.h", "kda_layout.h", "kda_kernels.h"],
+    "bwd": ["kda_bwd.hip", "kda_device.h", "kda_layout.h", "kda_kernels.h"],
 }
 
 
@@ -236,6 +237,16 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
         nchunk_heads = B * (T // 64) * H
     fl = bwd_flops_per_chunk_head(64, K, V)
     dom = max(stage_ms, key=stage_ms.get)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_bwd(x, d_o, d_f)
+    # measured HBM bytes of the dominant launch(es) from the committed counter runs, if taken on this source
+    traffic = None
+    tp = os.path.join(ROOT, "profiles", f"traffic_kda_bwd_{WORKLOADS[args.workload]['name']}.json")
+    if os.path.exists(tp):
+        rec = json.load(open(tp))
+        names = {"prep": ["bwd_prep_kernel"], "states_fwd": ["bwd_states_fwd_kernel"],
+                 "states_bwd": ["bwd_states_bwd_kernel"], "chunk": ["bwd_chunk_mm_kernel", "bwd_chunk_elem_kernel"]}
+        if rec.get("source_sha256_16") == kernel_source_hash("bwd") and all(n in rec["kernels"] for n in names[dom]):
+            traffic = sum(rec["kernels"][n]["traffic_bytes"] for n in names[dom])
     ach = fl[dom] * nchunk_heads / (stage_ms[dom] / 1e3) / 1e12
     print(json.dumps({
         "metric": "KDA chunk-bwd tokens/s (dq, dk, dv, dg, dbeta, dh0)", "value": B * T / (ms / 1e3),
@@ -246,9 +257,36 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
                    "V": V},
         "stage_ms": stage_ms,
         "roofline": {"kernel": f"bwd_{dom}", "bound": "alu", "achieved": ach, "peak": PEAK_FP32 / 1e12,
-                     "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": None,
+                     "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": traffic,
                      "alg_flops_per_launch": fl[dom] * nchunk_heads},
+        "cpu_baseline": cpu,
     }), flush=True)
+
+
+def cpu_baseline_bwd(x, d_o, d_f, target_s=10.0):
+    """Time the float64 backward oracle (reverse-mode differentiation of the token
+    recurrence) on one head of the workload, over a prefix grown to about
+    target_s of work; tokens/s scaled to all heads."""
+    import oracle.kda_oracle as orc
+    B, T, H, K = x.q.shape
+    tok = 128
+    while True:
+        t0 = time.perf_counter()
+        c0 = time.process_time()
+        sl = lambda a: a[:1, :tok, :1]
+        orc.kda_recurrent_vjp(sl(x.q), sl(x.k), sl(x.v), sl(x.g), x.beta[:1, :tok, :1], x.scale, sl(d_o),
+                              d_f[:1, :1], None if x.initial_state is None else x.initial_state[:1, :1])
+        wall = time.perf_counter() - t0
+        cpu = time.process_time() - c0
+        if wall * 2 >= target_s or tok * 2 > T:
+            break
+        tok = min(T, tok * max(2, int(target_s / max(wall, 1e-3) / 2)))
+    return {
+        "value": tok / wall / H, "unit": "tokens/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "sample": f"float64 backward oracle (torch autograd over the token recurrence) on head 0 of {H}, "
+                  f"first {tok} of {T} tokens ({wall:.1f} s wall, {cpu:.1f} s CPU); tokens/s scaled to all "
+                  f"{H} heads; host has {len(os.sched_getaffinity(0))} usable cores",
+    }
 
 
 def bench_layer(args, torch, kda):

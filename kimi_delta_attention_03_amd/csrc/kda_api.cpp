@@ -310,7 +310,7 @@ kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const v
     if (t && !aligned(t, 4)) return fail(KDA_ERR_INVALID_ARG, "states must be 4-byte aligned");
   const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
   const int64_t nunits = nseq * p->H;
-  if (nunits * (p->V / 16) > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  if ((nunits + 8) * (p->V / 16) > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
   char* w = static_cast<char*>(workspace);
   const int varlen = p->num_seqs > 0;
   if (varlen && (stages & 1)) {

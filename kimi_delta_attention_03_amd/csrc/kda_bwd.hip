@@ -339,7 +339,10 @@ __global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int u = (int)blockIdx.x / NVB, vb = (int)blockIdx.x % NVB;
+  // the NVB workgroups of one (sequence, head) get ids congruent modulo 8: with
+  // round-robin dispatch over the 8 XCDs they share one L2 for the chunk operands
+  const int bid = (int)blockIdx.x, slot = bid >> 3;
+  const int u = (slot / NVB) * 8 + (bid & 7), vb = slot % NVB;
   if (u >= a.nunits) return;
   const int seq = u / a.H, h = u % a.H;
   const BwdSlab& o = a.sl;
@@ -428,7 +431,10 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int u = (int)blockIdx.x / NVB, vb = (int)blockIdx.x % NVB;
+  // the NVB workgroups of one (sequence, head) get ids congruent modulo 8: with
+  // round-robin dispatch over the 8 XCDs they share one L2 for the chunk operands
+  const int bid = (int)blockIdx.x, slot = bid >> 3;
+  const int u = (slot / NVB) * 8 + (bid & 7), vb = slot % NVB;
   if (u >= a.nunits) return;
   const int seq = u / a.H, h = u % a.H;
   const BwdSlab& o = a.sl;
@@ -762,11 +768,12 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
 template <int K>
 hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   const int nvb = K / 16;
+  const unsigned sgrid = (unsigned)((a.nunits + 7) / 8 * 8 * nvb);  // see the XCD mapping above
   if ((stages & 1) && nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
   if (a.nunits > 0) {
     if ((stages & 2) && nitems > 0)
-      hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
-    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(a.nunits * nvb), dim3(kBT), 0, s, a);
+      hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(sgrid), dim3(kBT), 0, s, a);
+    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(kBT), 0, s, a);
   }
   if ((stages & 8) && nitems > 0) {
     hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
