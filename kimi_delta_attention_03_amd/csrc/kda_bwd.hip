@@ -698,11 +698,12 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
       const int i = 16 * ib + 4 * gq + r;
       const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
       const float Gl = sG[(C - 1) * K + d];
-      const float eg = __expf(Gi);
+      const float eg = __expf(Gi), egl = __expf(Gl - Gi);
       const float dqg = P.DQG[i * K + d], dkb = P.DKB[i * K + d], dkg = P.DKG[i * K + d];
       P.DQN[i * K + d] = s * eg * dqg + s * qa[r];
-      P.DKN[i * K + d] = dkb * bi * eg + dkg * __expf(Gl - Gi) + s * ka[r] + qm[r] + km[r];
-      float dG = dqg * P.QG[i * K + d] + dkb * P.KB[i * K + d] - dkg * P.KG[i * K + d] + qi * s * qa[r] -
+      P.DKN[i * K + d] = dkb * bi * eg + dkg * egl + s * ka[r] + qm[r] + km[r];
+      // Qg = s q e^G, Kb = beta k e^G and KG = k e^(Gl - G) rebuilt from the staged rows
+      float dG = dqg * (s * qi * eg) + dkb * (bi * ki * eg) - dkg * (ki * egl) + qi * s * qa[r] -
                  ki * s * ka[r] + ki * qm[r] - ki * km[r];
       if (i == C - 1) dG += sDGl[d];
       P.DG[i * K + d] = dG;
