@@ -22,13 +22,15 @@
 // to dq, dk, dv, dg (reverse cumsum of dG), dbeta; with the optional L2 norm,
 // dq = (dq^ - q^ (q^ . dq^)) / |q| (or dq^ / eps where the norm is clamped).
 //
-// Four launches:
+// Four stages, five launches:
 //   prep        per (chunk, head): the chunk terms above, from the inputs
 //   states_fwd  per (sequence, head, 16 columns): chunk-start states, in order
 //   states_bwd  per (sequence, head, 16 columns): dS' per chunk, in reverse; dh0
 //   chunk       per (chunk, head): every other gradient, as two launches (the
 //               matrix products, then the elementwise and gated-sum rules)
 // Every intermediate lives in a per-(chunk, head) fp32 slab of the workspace.
+// The per-chunk kernels are latency-bound chains of phases and run 16 waves
+// per workgroup; the two state passes are bound by their per-chunk chain.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
