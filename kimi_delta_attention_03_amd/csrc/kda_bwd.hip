@@ -395,28 +395,35 @@ __global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
       }
     if (cc + 1 < nch) fetch(cc + 1);
     __syncthreads();
-    // Vn rows 16 w .. 16 w + 15 = U - W S
+    // Vn rows 16 w .. 16 w + 15 = U - W S (four independent accumulator chains)
     {
-      floatx4 acc = zero4();
-#pragma unroll 8
-      for (int k0 = 0; k0 < K; k0 += 4)
-        acc = mfma4(sW[(16 * w + xi) * KP + k0 + gq], sS[(k0 + gq) * 17 + xi], acc);
+      floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+      for (int k0 = 0; k0 < K; k0 += 16)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          acc[c] = mfma4(sW[(16 * w + xi) * KP + k0 + 4 * c + gq], sS[(k0 + 4 * c + gq) * 17 + xi], acc[c]);
+      const floatx4 ws = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * gq + r;
-        sVn[i * 17 + xi] = sU[i * 20 + xi] - acc[r];
+        sVn[i * 17 + xi] = sU[i * 20 + xi] - ws[r];
       }
     }
     __syncthreads();
-    // S = Diag(gamma) S + KG^T Vn
+    // S = Diag(gamma) S + KG^T Vn (two accumulator chains per tile)
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
       const int rt = TPW * w + t;
 #pragma unroll
       for (int r = 0; r < 4; ++r) S[t][r] *= sGam[16 * rt + 4 * gq + r];
-#pragma unroll 8
-      for (int k0 = 0; k0 < C; k0 += 4)
+      floatx4 acc2 = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < C; k0 += 8) {
         S[t] = mfma4(sKG[(k0 + gq) * KP + 16 * rt + xi], sVn[(k0 + gq) * 17 + xi], S[t]);
+        acc2 = mfma4(sKG[(k0 + 4 + gq) * KP + 16 * rt + xi], sVn[(k0 + 4 + gq) * 17 + xi], acc2);
+      }
+      S[t] += acc2;
     }
   }
 }
