@@ -148,9 +148,10 @@ def bench_decode(args, torch, kda):
 
 
 def bench_affine(args, torch, kda, WORKLOADS, workload):
-    """Affine summaries of a core workload: stage 1+2, then two stage-3+4
-    passes (zero start -> N, identity start -> M) that each read every record
-    (1128 B per token-head at K=V=128 bf16) and write their K x V states."""
+    """Affine summaries of a core workload: stage 1+2 (reads the inputs, writes
+    the records), then two stage-3+4 passes without output (zero start -> N,
+    identity start -> M) that each read the records' W, kg, U and gamma
+    (2K + V elements + 4K/64 bytes per token-head) and write their K x V states."""
     x = workload(args.workload)
     dev = "cuda:0"
     dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
@@ -163,10 +164,10 @@ def bench_affine(args, torch, kda, WORKLOADS, workload):
     ms = time_loop(run, args.steps, torch)
     B, T, H, K = x.q.shape
     elem = 2 if x.dtype == "bf16" else 4
-    b12, b34 = alg_bytes_per_token_head(K, K, elem, elem, elem)
-    rec = b34 - K * elem
+    b12, _ = alg_bytes_per_token_head(K, K, elem, elem, elem)
+    summ = (2 * K + K) * elem + 4 * K / 64       # W, kg, U, gamma
     nseq = B if cu is None else len(x.cu_seqlens) - 1
-    nbytes = B * T * H * (b12 + 2 * rec) + 2 * nseq * H * K * K * 4
+    nbytes = B * T * H * (b12 + 2 * summ) + 2 * nseq * H * K * K * 4
     gbps = nbytes / (ms / 1e3) / 1e9
     print(json.dumps({
         "metric": "KDA affine chunk summaries tokens/s", "value": B * T / (ms / 1e3), "unit": "tokens/s",

@@ -79,7 +79,7 @@ __device__ __forceinline__ void bload4(floatx4& d, __amdgpu_buffer_rsrc_t r, int
 // fragments 64 * 4 elements. Every lane-byte loaded here passes the CU's
 // vector-memory path, whose rate bounds a chunk step, so nothing is loaded
 // twice: gamma comes as one float per lane and is spread by lane shuffles.
-template <typename T, int K>
+template <typename T, int K, bool OUT>
 __device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc_t rs, int soff,
                                          const Stage34Args& a, int r, int lane_off, int vb) {
   constexpr int NKB = K / 32;
@@ -88,14 +88,16 @@ __device__ __forceinline__ void load_row(RowFrags<T, K>& f, __amdgpu_buffer_rsrc
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) {
     bload(f.w[kb], rs, lane_off, soff + (int)a.off_w + (r * NKB + kb) * F8B);
-    bload(f.qg[kb], rs, lane_off, soff + (int)a.off_qg + (r * NKB + kb) * F8B);
+    if constexpr (OUT) bload(f.qg[kb], rs, lane_off, soff + (int)a.off_qg + (r * NKB + kb) * F8B);
   }
   // every wave issues both Aqk loads (no branch around a load keeps the
   // compiler's memory-counter waits exact); rows < 32 have no second block and
   // point that load past the end of the record, where it reads zeros without
-  // touching memory
-  bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + aq_frag(r, 0) * F8B);
-  bload(f.aq[1], rs, lane_off, r >= 2 ? soff + (int)a.off_aq + aq_frag(r, 1) * F8B : (int)a.rec_bytes);
+  // touching memory. Without an output (OUT false) qg and Aqk are not needed.
+  if constexpr (OUT) {
+    bload(f.aq[0], rs, lane_off, soff + (int)a.off_aq + aq_frag(r, 0) * F8B);
+    bload(f.aq[1], rs, lane_off, r >= 2 ? soff + (int)a.off_aq + aq_frag(r, 1) * F8B : (int)a.rec_bytes);
+  }
   bload4(f.u, rs, lane_off, soff + (int)a.off_u + (vb * 4 + r) * F4B);
 }
 
@@ -114,7 +116,9 @@ __device__ __forceinline__ void load_state(StateFrags<T, K>& f, __amdgpu_buffer_
                                         rs, gam_off, soff + (int)a.off_gam + 64 * TPW * s, 0));
 }
 
-template <typename T, int K, int NB>
+// OUT false: no output o (affine summaries, final state only); the row waves
+// then load neither qg nor Aqk and skip the output products.
+template <typename T, int K, int NB, bool OUT>
 __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   constexpr int C = kChunk;
   constexpr int V = K;
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
     RowFrags<T, K> F[NB];
     auto issue = [&](RowFrags<T, K>& f, int c) {
       const int cc = c < last ? c : last;
-      load_row<T, K>(f, rec_rsrc(cc), 0, a, r0, lane_off, vb);
+      load_row<T, K, OUT>(f, rec_rsrc(cc), 0, a, r0, lane_off, vb);
     };
     // prologue loads in chunk order (see the state waves)
 #pragma unroll
@@ -292,22 +296,26 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
       // leaves as one vector store per lane
       floatx4 accO = zero4();
       if (c < nch) {
+        if constexpr (OUT) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) accO = mma32(accO, Sb[kb], f.qg[kb]);
-        const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
-        const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
-        // intra-chunk part, causal: row block r0 reads V_new blocks <= r0
-        accO = mma32(accO, Vb0, f.aq[0]);
-        if (r0 >= 2) accO = mma32(accO, Vb1, f.aq[1]);
+          for (int kb = 0; kb < NKB; ++kb) accO = mma32(accO, Sb[kb], f.qg[kb]);
+          const F8 Vb0 = stack8<T>(sVn[0][lane], sVn[1][lane]);
+          const F8 Vb1 = stack8<T>(sVn[2][lane], sVn[3][lane]);
+          // intra-chunk part, causal: row block r0 reads V_new blocks <= r0
+          accO = mma32(accO, Vb0, f.aq[0]);
+          if (r0 >= 2) accO = mma32(accO, Vb1, f.aq[1]);
+        }
         lds_sync();  // state after chunk c published
       }
-      // rows past the end of a short chunk, and every row of a step past the
-      // last chunk, store into the sink: the store is never under a branch
-      const int row = 16 * r0 + xi;
-      F4 y;
-      cvt4(accO, y);
-      T* dst = (row < len && out) ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
-      *reinterpret_cast<F4*>(dst) = y;
+      if constexpr (OUT) {
+        // rows past the end of a short chunk, and every row of a step past the
+        // last chunk, store into the sink: the store is never under a branch
+        const int row = 16 * r0 + xi;
+        F4 y;
+        cvt4(accO, y);
+        T* dst = (row < len && out) ? out + ((size_t)(tok0 + row) * H + h) * V + 16 * vb + 4 * gq : sink;
+        *reinterpret_cast<F4*>(dst) = y;
+      }
     };
     // whole ring passes with a single exit (see the state waves)
     const int npass = (nch + NB - 1) / NB;
@@ -357,12 +365,22 @@ hipError_t launch_stage34(const Stage34Args& a, int K, int bf16, hipStream_t s) 
   const int nvb = K / 16;
   const int units8 = (a.nunits + 7) / 8;
   dim3 grid(units8 * 8 * nvb), block(kThreads34);
-  if (bf16) {
-    if (K == 128) hipLaunchKernelGGL((stage34_kernel<kda::bf16, 128, 4>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage34_kernel<kda::bf16, 64, 4>), grid, block, 0, s, a);
+  if (a.o) {
+    if (bf16) {
+      if (K == 128) hipLaunchKernelGGL((stage34_kernel<kda::bf16, 128, 4, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((stage34_kernel<kda::bf16, 64, 4, true>), grid, block, 0, s, a);
+    } else {
+      if (K == 128) hipLaunchKernelGGL((stage34_kernel<float, 128, 2, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((stage34_kernel<float, 64, 4, true>), grid, block, 0, s, a);
+    }
   } else {
-    if (K == 128) hipLaunchKernelGGL((stage34_kernel<float, 128, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage34_kernel<float, 64, 4>), grid, block, 0, s, a);
+    if (bf16) {
+      if (K == 128) hipLaunchKernelGGL((stage34_kernel<kda::bf16, 128, 4, false>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((stage34_kernel<kda::bf16, 64, 4, false>), grid, block, 0, s, a);
+    } else {
+      if (K == 128) hipLaunchKernelGGL((stage34_kernel<float, 128, 2, false>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((stage34_kernel<float, 64, 4, false>), grid, block, 0, s, a);
+    }
   }
   return hipGetLastError();
 }
