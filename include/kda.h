@@ -134,7 +134,9 @@ kda_status kda_chunk_fwd_stage12(const kda_fwd_params* p, const void* q, const v
 
 /* Stage 3+4 alone (Tokamax design doc section 4.3): reads a workspace filled
  * by kda_chunk_fwd_stage12 with the same parameters and writes o and
- * final_state. */
+ * final_state. With cu_seqlens it rebuilds the chunk map first, so a workspace
+ * that stage 1+2 has not filled yields meaningless values but no access outside
+ * the buffers. */
 kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_state,
                                  const int32_t* cu_seqlens, void* o, float* final_state,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -217,7 +219,9 @@ kda_status kda_chunk_bwd(const kda_fwd_params* p, const void* q, const void* k, 
  * (1: rebuild the chunk terms into the workspace, 2: chunk-start states, 4: state
  * gradients and d_initial_state, 8: every other gradient). Each stage reads what the
  * earlier ones left in the same workspace, so stages run in increasing order over one
- * workspace reproduce kda_chunk_bwd exactly; 15 is kda_chunk_bwd. Arguments, errors and
+ * workspace reproduce kda_chunk_bwd exactly; 15 is kda_chunk_bwd. With cu_seqlens every
+ * call rebuilds the chunk map, so a stage run on a workspace the earlier stages have not
+ * filled yields meaningless values but no access outside the buffers. Arguments, errors and
  * ownership as kda_chunk_bwd; KDA_ERR_INVALID_ARG for a mask outside [1, 15]. */
 kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const void* q, const void* k,
                                 const void* v, const void* g, const void* beta,

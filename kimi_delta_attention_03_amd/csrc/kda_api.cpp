@@ -131,10 +131,19 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
   return KDA_OK;
 }
 
+// build_map: (re)build the variable-length chunk map first. The entry points that
+// run stage 3+4 on its own do, so that a workspace not prepared by stage 1+2 still
+// holds valid tables and every access stays in bounds.
 kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float* fin, void* ws,
-                      const kda::Layout& L, hipStream_t stream, int affine_linear = 0) {
+                      const kda::Layout& L, hipStream_t stream, int affine_linear = 0, bool build_map = false,
+                      const int32_t* cu = nullptr) {
   const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
   if (nseq == 0) return KDA_OK;
+  if (build_map && p->num_seqs > 0) {
+    hipError_t e = kda::launch_varlen_map(cu, p->num_seqs, p->T, static_cast<char*>(ws), L.ncp, L.off_chunk_tab,
+                                          L.off_seq_tab, L.off_order, stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
+  }
   if (p->T > 0 && !o && !fin) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
   if (o && !aligned(o, 16)) return fail(KDA_ERR_INVALID_ARG, "o must be 16-byte aligned");
   if ((init && !aligned(init, 16)) || (fin && !aligned(fin, 16)))
@@ -222,7 +231,7 @@ kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_s
   kda::Layout L;
   kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
   if (s != KDA_OK) return s;
-  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+  return do_stage34(p, initial_state, o, final_state, workspace, L, stream, 0, true, cu_seqlens);
 }
 
 kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
@@ -313,7 +322,7 @@ kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const v
   if ((nunits + 8) * (p->V / 16) > INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
   char* w = static_cast<char*>(workspace);
   const int varlen = p->num_seqs > 0;
-  if (varlen && (stages & 1)) {
+  if (varlen) {  // every call: later stages alone still see valid chunk tables
     hipError_t e = kda::launch_varlen_map(cu_seqlens, p->num_seqs, p->T, w, L.ncp, L.off_chunk_tab, L.off_seq_tab,
                                           L.off_order, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
@@ -378,7 +387,7 @@ kda_status kda_chunk_affine_summary(const kda_fwd_params* p, const int32_t* cu_s
   if (!aligned(M, 16) || !aligned(N, 16)) return fail(KDA_ERR_INVALID_ARG, "M and N must be 16-byte aligned");
   // N: the state reached from a zero start; M: the recurrence run on an identity
   // start with U taken as zero (the linear part). No output is written.
-  s = do_stage34(p, nullptr, nullptr, N, workspace, L, stream, 0);
+  s = do_stage34(p, nullptr, nullptr, N, workspace, L, stream, 0, true, cu_seqlens);
   if (s != KDA_OK) return s;
   return do_stage34(p, nullptr, nullptr, M, workspace, L, stream, 1);
 }
