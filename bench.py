@@ -180,6 +180,45 @@ def bench_affine(args, torch, kda, WORKLOADS, workload):
     }), flush=True)
 
 
+def bench_gated(args, torch, kda, WORKLOADS, workload):
+    """The forward with the gate activation inside stage 1+2 (lower-bound
+    sigmoid, bound -5, or softplus with --gate softplus) on a core workload's
+    shape: g holds raw gate values (N(0,1) clipped to [-3, 2]) and A_log, dt_bias
+    are per head / per (head, channel). Same bytes as the plain forward (the raw
+    gate replaces the log decay) plus A_log and dt_bias; the roofline entry is
+    the whole step's algorithmic bytes over the step time."""
+    from kimi_delta_attention_03_amd.synthetic import gate_inputs
+    x = workload(args.workload)
+    dev = "cuda:0"
+    dt = torch.bfloat16 if x.dtype == "bf16" else torch.float32
+    to = lambda a, d: torch.from_numpy(np.ascontiguousarray(a)).to(d).to(dev)
+    B, T, H, K = x.q.shape
+    raw, A_log, dt_bias = gate_inputs(B, T, H, K, seed=WORKLOADS[args.workload]["seed"] + 70, dtype=x.dtype)
+    q, k, v, graw, beta = (to(a, dt) for a in (x.q, x.k, x.v, raw, x.beta))
+    init = None if x.initial_state is None else to(x.initial_state, torch.float32)
+    cu = None if x.cu_seqlens is None else torch.from_numpy(x.cu_seqlens.astype(np.int32)).to(dev)
+    mode = "softplus" if args.gate == "softplus" else "lower_bound_sigmoid"
+    fwd = kda.KdaForward(q, k, v, graw, beta, scale=x.scale, initial_state=init, cu_seqlens=cu, gate_mode=mode,
+                         A_log=to(A_log, torch.float32), dt_bias=to(dt_bias, torch.float32), gate_lower_bound=-5.0)
+    for _ in range(args.warmup):
+        fwd()
+    ms = time_loop(fwd, args.steps, torch)
+    elem = 2 if x.dtype == "bf16" else 4
+    b12, b34 = alg_bytes_per_token_head(K, K, elem, elem, elem)
+    nbytes = B * T * H * (b12 + b34) + 4 * H * (K + 1)
+    gbps = nbytes / (ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": f"KDA chunk-fwd with in-kernel gate activation ({mode}) tokens/s", "value": B * T / (ms / 1e3),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "dtype": x.dtype, "data": "synthetic (seeded numpy generators)",
+        "config": {"workload": WORKLOADS[args.workload]["name"] + "_gated", "B": B, "T": T, "H": H, "K": K,
+                   "V": K, "gate": mode},
+        "roofline": {"kernel": "stage12 (gate inside) + stage34, whole step", "bound": "hbm", "achieved": gbps,
+                     "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbps * 1e9 / PEAK_HBM, "traffic": None,
+                     "alg_bytes_per_launch": nbytes},
+    }), flush=True)
+
+
 def bwd_flops_per_chunk_head(C, K, V):
     """Algorithmic FLOPs of each backward launch per (chunk, head), causal
     triangles counted as triangles (tri = C(C+1)/2 pairs):
@@ -328,10 +367,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=2)
-    ap.add_argument("--mode", choices=["forward", "decode", "affine", "backward"], default="forward",
+    ap.add_argument("--mode", choices=["forward", "decode", "affine", "backward", "gated"], default="forward",
                     help="decode: one kda_decode_step over B=256 sequences x H=32 (K=V=128, bf16); "
                          "affine: stage 1+2 plus the affine summaries on the workload's shape; "
-                         "backward: kda_chunk_bwd on the workload's shape")
+                         "backward: kda_chunk_bwd on the workload's shape; "
+                         "gated: the forward with the gate activation inside stage 1+2")
+    ap.add_argument("--gate", choices=["lower_bound_sigmoid", "softplus"], default="lower_bound_sigmoid")
     ap.add_argument("--kernel-reps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -362,6 +403,8 @@ def main():
         return bench_affine(args, torch, kda, WORKLOADS, workload)
     if args.mode == "backward":
         return bench_backward(args, torch, kda, WORKLOADS, workload)
+    if args.mode == "gated":
+        return bench_gated(args, torch, kda, WORKLOADS, workload)
 
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()

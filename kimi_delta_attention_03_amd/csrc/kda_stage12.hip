@@ -281,7 +281,7 @@ void stage12_kernel(Stage12Args a) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) run[c] = 0.f;
       float lam = 0.f;
-      if constexpr (GATE) lam = expf(R.alog);
+      if constexpr (GATE) lam = __expf(R.alog);
 #pragma unroll
       for (int rr = 0; rr < RPS; ++rr) {
 #pragma unroll
@@ -292,11 +292,13 @@ void stage12_kernel(Stage12Args a) {
                             : __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] << 16);
           if constexpr (GATE) {
             const float x = gv + R.gbias[c];
+            // hardware exp2 / log2 based exp and log: the activations only need
+            // fp32 relative accuracy where the decay is not ~1 anyway
             if (a.gate_mode == 1) {
-              const float sp = x > 20.f ? x : log1pf(expf(x));  // softplus
+              const float sp = fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));  // softplus, stable form
               gv = -lam * sp;
             } else {
-              gv = a.gate_lb / (1.f + expf(-lam * x));            // lower_bound * sigmoid
+              gv = a.gate_lb / (1.f + __expf(-lam * x));  // lower_bound * sigmoid
             }
             if (seg * RPS + rr >= it.len) gv = 0.f;
           }
