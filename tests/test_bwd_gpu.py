@@ -97,6 +97,15 @@ def test_bwd_bf16_qkv_fp32_gates_no_final_grad():
     check(errs, TOL["bf16"])
 
 
+def test_bwd_bf16_k64_varlen_l2norm():
+    """bf16, K=V=64, packed ragged sequences and the L2 flag on raw q, k together."""
+    _say("bwd bf16 K=V=64 varlen [65, 3, 190] + l2norm")
+    x = core_inputs(1, None, 2, 64, 64, dtype="bf16", seed=37, init_std=0.1, lengths=[65, 3, 190],
+                    normalize=False)
+    errs, _ = run_case(x, seed=13, l2=True)
+    check(errs, TOL["bf16"])
+
+
 def test_bwd_deterministic():
     """Two calls give bitwise-equal gradients."""
     import torch
