@@ -51,6 +51,27 @@ struct ItemB {
   int64_t tok0;
 };
 
+// NE elements per thread of a [C, W] row block of tensor x at (chunk it, head h):
+// element e = threadIdx.x + NT m is row e / W, column e % W. Rows past the chunk
+// end read row 0's address (always valid: a chunk holds at least one token) and
+// become 0. All loads are issued before any result is used.
+template <typename TX, int NE, int NT, int W>
+__device__ __forceinline__ void load_rows(const void* x, const ItemB& it, int H, float* out) {
+  const TX* p = reinterpret_cast<const TX*>(x);
+  TX raw[NE];
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = (int)threadIdx.x + NT * m, r = e / W, d = e % W;
+    const int rr = r < it.len ? r : 0;
+    raw[m] = p[((size_t)(it.tok0 + rr) * H + it.h) * W + d];
+  }
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int r = ((int)threadIdx.x + NT * m) / W;
+    out[m] = r < it.len ? to_f32(raw[m]) : 0.f;
+  }
+}
+
 __device__ __forceinline__ int items_in_use(const BwdArgs& a) {
   return (a.varlen ? *reinterpret_cast<const int*>(a.ws) : (int)a.ncp) * a.H;
 }
@@ -176,21 +197,30 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
   const int H = a.H;
   const int qf32 = !a.bf16_qkv;
 
-  // rows of q, k, g (rows past the chunk end are zero tokens)
-  for (int e = tid; e < C * K; e += kBW) {
-    const int r = e / K, d = e % K;
-    float qv = 0.f, kv = 0.f, gv = 0.f;
-    if (r < it.len) {
-      const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
-      qv = ldx(a.q, idx, qf32);
-      kv = ldx(a.k, idx, qf32);
-      gv = ldx(a.g, idx, a.g_f32);
-    }
-    sQ[r * KP + d] = qv;
-    sK[r * KP + d] = kv;
-    sG[r * KP + d] = gv;
+  // rows of q, k, g, v (rows past the chunk end are zero tokens), all loads in
+  // flight together: no store is issued in between, since every memory-counter
+  // wait would also wait for earlier stores
+  constexpr int NE = C * K / kBW;
+  float qv[NE], kv[NE], gv[NE], vv[NE];
+  if (qf32) {
+    load_rows<float, NE, kBW, K>(a.q, it, H, qv);
+    load_rows<float, NE, kBW, K>(a.k, it, H, kv);
+    load_rows<float, NE, kBW, V>(a.v, it, H, vv);
+  } else {
+    load_rows<bf16, NE, kBW, K>(a.q, it, H, qv);
+    load_rows<bf16, NE, kBW, K>(a.k, it, H, kv);
+    load_rows<bf16, NE, kBW, V>(a.v, it, H, vv);
   }
+  if (a.g_f32) load_rows<float, NE, kBW, K>(a.g, it, H, gv);
+  else load_rows<bf16, NE, kBW, K>(a.g, it, H, gv);
   if (tid < C) sB[tid] = tid < it.len ? ldx(a.beta, (size_t)(it.tok0 + tid) * H + it.h, a.beta_f32) : 0.f;
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + kBW * m, r = e / K, d = e % K;
+    sQ[r * KP + d] = qv[m];
+    sK[r * KP + d] = kv[m];
+    sG[r * KP + d] = gv[m];
+  }
   __syncthreads();
 
   // row norms (kept for the backward of the optional L2 norm); gate cumsum
@@ -228,10 +258,10 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     sl[o.kg + e] = kn * __expf(Gl - G);
     sl[o.kb + e] = sB[r] * kn * eg;
   }
-  for (int e = tid; e < C * V; e += kBW) {
-    const int r = e / V, d = e % V;
-    const float vv = r < it.len ? ldx(a.v, ((size_t)(it.tok0 + r) * H + it.h) * V + d, qf32) : 0.f;
-    sl[o.vb + e] = sB[r] * vv;
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + kBW * m;
+    sl[o.vb + e] = sB[e / V] * vv[m];
   }
   if (tid < K) sl[o.gam + tid] = __expf(sG[(C - 1) * KP + tid]);
   if (tid < C) sl[o.beta + tid] = sB[tid];
@@ -650,6 +680,7 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   // gradient of the last row's cumulative gate through KG and gamma
   if (tid < K) {
     float acc = P.DGAM[tid] * P.GAM[tid];
+#pragma unroll 16
     for (int r = 0; r < C; ++r) acc += P.DKG[r * K + tid] * P.KG[r * K + tid];
     sDGl[tid] = acc;
   }
@@ -725,15 +756,36 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     const int i = tid / TPR, part = tid % TPR;
     float db = 0.f;
     if (i < it.len) {
+      constexpr int NV = V / TPR, NK = K / TPR, NJ = C / TPR;
       const size_t vrow = ((size_t)(it.tok0 + i) * H + it.h) * V;
-      for (int v = part * (V / TPR); v < (part + 1) * (V / TPR); ++v) {
-        const float dvb = P.DVB[i * V + v];
-        db += dvb * ldx(a.v, vrow + v, qf32);
-        a.dv[vrow + v] = sBeta[i] * dvb;
+      const int v0 = part * NV, d0 = part * NK;
+      // loads first (no store in between), then the sums, then the dv stores
+      float dvb[NV], vv[NV], dkb[NK], dl[NJ], mm[NJ];
+#pragma unroll
+      for (int c = 0; c < NV; ++c) dvb[c] = P.DVB[i * V + v0 + c];
+      if (qf32) {
+#pragma unroll
+        for (int c = 0; c < NV; ++c) vv[c] = reinterpret_cast<const float*>(a.v)[vrow + v0 + c];
+      } else {
+#pragma unroll
+        for (int c = 0; c < NV; ++c) vv[c] = to_f32(reinterpret_cast<const bf16*>(a.v)[vrow + v0 + c]);
       }
-      for (int d = part * (K / TPR); d < (part + 1) * (K / TPR); ++d)
-        db += P.DKB[i * K + d] * sKN[i * K + d] * __expf(sG[i * K + d]);
-      for (int j = part; j < i; j += TPR) db += P.DL[i * C + j] * P.Mm[i * C + j];
+#pragma unroll
+      for (int c = 0; c < NK; ++c) dkb[c] = P.DKB[i * K + d0 + c];
+#pragma unroll
+      for (int c = 0; c < NJ; ++c) {
+        const int j = part + TPR * c;
+        dl[c] = P.DL[i * C + j];
+        mm[c] = P.Mm[i * C + j];
+      }
+#pragma unroll
+      for (int c = 0; c < NV; ++c) db += dvb[c] * vv[c];
+#pragma unroll
+      for (int c = 0; c < NK; ++c) db += dkb[c] * sKN[i * K + d0 + c] * __expf(sG[i * K + d0 + c]);
+#pragma unroll
+      for (int c = 0; c < NJ; ++c) db += (part + TPR * c < i) ? dl[c] * mm[c] : 0.f;
+#pragma unroll
+      for (int c = 0; c < NV; ++c) a.dv[vrow + v0 + c] = sBeta[i] * dvb[c];
     }
 #pragma unroll
     for (int off = 1; off < TPR; off <<= 1) db += __shfl_xor(db, off, 64);
@@ -746,15 +798,24 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     const float* X = tid < C ? sQN : sKN;
     const float* D = tid < C ? P.DQN : P.DKN;
     float acc = 0.f;
+#pragma unroll 16
     for (int d = 0; d < K; ++d) acc += X[r * K + d] * D[r * K + d];
     sDot[tid] = acc;
   }
   __syncthreads();
-  for (int e = tid; e < C * K; e += kBW) {
-    const int r = e / K, d = e % K;
+  constexpr int NE = C * K / kBW;
+  float gqv[NE], gkv[NE];
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    gqv[m] = P.DQN[tid + kBW * m];
+    gkv[m] = P.DKN[tid + kBW * m];
+  }
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + kBW * m, r = e / K, d = e % K;
     if (r >= it.len) continue;
     const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
-    float gradq = P.DQN[e], gradk = P.DKN[e];
+    float gradq = gqv[m], gradk = gkv[m];
     if (a.l2norm) {
       const float nq = sl[o.nq + r], nk = sl[o.nk + r];
       gradq = nq > a.l2eps ? (gradq - sQN[e] * sDot[r]) / nq : gradq / a.l2eps;
@@ -767,9 +828,17 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   if (tid < K) {
     const int d = tid;
     float run = 0.f;
-    for (int r = C - 1; r >= 0; --r) {
-      run += P.DG[r * K + d];
-      if (r < it.len) a.dg[((size_t)(it.tok0 + r) * H + it.h) * K + d] = run;
+#pragma unroll
+    for (int half = 1; half >= 0; --half) {  // rows 32..63, then 0..31: loads before stores
+      float col[C / 2];
+#pragma unroll
+      for (int r = 0; r < C / 2; ++r) col[r] = P.DG[(half * (C / 2) + r) * K + d];
+#pragma unroll
+      for (int r = C / 2 - 1; r >= 0; --r) {
+        const int row = half * (C / 2) + r;
+        run += col[r];
+        if (row < it.len) a.dg[((size_t)(it.tok0 + row) * H + it.h) * K + d] = run;
+      }
     }
   }
 }
