@@ -115,9 +115,10 @@ __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
 
 // out(i, j) = sum_kk A(i, kk) B(kk, j) for an M x N result over KD (a multiple
 // of 16), with A(i, kk) = A[i * lda + kk] (TA: A[kk * lda + i]) and B(kk, j) =
-// B[kk * ldb + j] (TB: B[j * ldb + kk]). 16-deep slices of both operands are
-// staged in LDS (smem: 16 (M + 4) + 16 (N + 4) floats) with loads that run
-// along the contiguous index; each thread accumulates 4 rows x M N / 1024
+// B[kk * ldb + j] (TB: B[j * ldb + kk]). 16-deep slices of both operands pass
+// through registers into LDS (smem: 16 (M + 4) + 16 (N + 4) floats), loaded
+// along the contiguous index; the next slice's loads are in flight while the
+// current slice is multiplied. Each thread accumulates 4 rows x M N / 1024
 // columns. Ends with a barrier, before the epilogue calls.
 template <int M, int N, bool TA, bool TB, typename FO>
 __device__ __forceinline__ void lds_mm(int KD, const float* A, int lda, const float* B, int ldb, float* smem,
@@ -126,7 +127,9 @@ __device__ __forceinline__ void lds_mm(int KD, const float* A, int lda, const fl
   constexpr int NC = M * N / (kBT * 4);
   constexpr int NCG = N / NC;
   constexpr int SA = M + 4, SB = N + 4;
+  constexpr int LA = M * KS / kBT, LB = N * KS / kBT;  // slice elements per thread
   static_assert(NC % 4 == 0 && (M / 4) * NCG == kBT, "thread tiling");
+  static_assert(LA * kBT == M * KS && LB * kBT == N * KS, "slice split");
   float* sa = smem;
   float* sb = smem + KS * SA;
   const int tid = threadIdx.x;
@@ -136,28 +139,35 @@ __device__ __forceinline__ void lds_mm(int KD, const float* A, int lda, const fl
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[r][c] = 0.f;
+  float ra[LA], rb[LB];
+  auto fetch = [&](int k0) {
+#pragma unroll
+    for (int m = 0; m < LA; ++m) {
+      const int e = tid + kBT * m;
+      ra[m] = TA ? A[(size_t)(k0 + e / M) * lda + e % M] : A[(size_t)(e / KS) * lda + k0 + e % KS];
+    }
+#pragma unroll
+    for (int m = 0; m < LB; ++m) {
+      const int e = tid + kBT * m;
+      rb[m] = TB ? B[(size_t)(e / KS) * ldb + k0 + e % KS] : B[(size_t)(k0 + e / N) * ldb + e % N];
+    }
+  };
+  fetch(0);
   for (int k0 = 0; k0 < KD; k0 += KS) {
 #pragma unroll
-    for (int e = tid; e < M * KS; e += kBT) {
-      if (TA) {
-        const int kk = e / M, i = e % M;
-        sa[kk * SA + i] = A[(size_t)(k0 + kk) * lda + i];
-      } else {
-        const int i = e / KS, kk = e % KS;
-        sa[kk * SA + i] = A[(size_t)i * lda + k0 + kk];
-      }
+    for (int m = 0; m < LA; ++m) {
+      const int e = tid + kBT * m;
+      if (TA) sa[(e / M) * SA + e % M] = ra[m];
+      else sa[(e % KS) * SA + e / KS] = ra[m];
     }
 #pragma unroll
-    for (int e = tid; e < N * KS; e += kBT) {
-      if (TB) {
-        const int j = e / KS, kk = e % KS;
-        sb[kk * SB + j] = B[(size_t)j * ldb + k0 + kk];
-      } else {
-        const int kk = e / N, j = e % N;
-        sb[kk * SB + j] = B[(size_t)(k0 + kk) * ldb + j];
-      }
+    for (int m = 0; m < LB; ++m) {
+      const int e = tid + kBT * m;
+      if (TB) sb[(e % KS) * SB + e / KS] = rb[m];
+      else sb[(e / N) * SB + e % N] = rb[m];
     }
     __syncthreads();
+    if (k0 + KS < KD) fetch(k0 + KS);  // in flight during the products below
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
       const floatx4 a4 = *reinterpret_cast<const floatx4*>(sa + kk * SA + 4 * rg);
