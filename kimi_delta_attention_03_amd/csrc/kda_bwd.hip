@@ -319,23 +319,65 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // A = (I + L)^-1 by forward substitution, lane j of wave 0 -> column j, kept
-  // in registers: x_i = delta_ij - sum_{m<i} L_im x_m, where the rows above the
-  // diagonal come out zero by themselves (right-hand side e_j)
-  if (tid < C) {
-    const int j = tid;
-    float x[C];
+  // A = (I + L)^-1, blocked: wave w < 4 inverts diagonal block w by forward
+  // substitution (lane xi -> column xi; the four lane groups compute the same
+  // values), then its block column below the diagonal on fp32 MFMA:
+  //   A_ib,w = -D_ib sum_{kb=w}^{ib-1} L_ib,kb A_kb,w,  D_ib = A_ib,ib
+  // with the reduction index of step s at lane group g taken as 4 g + s, so an
+  // accumulator tile (lane (g, i) holds rows 4 g + r) is itself the B operand.
+  {
+    const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (w < 4) {
+      float x[16];
 #pragma unroll
-    for (int i = 0; i < C; ++i) {
-      float acc = (i == j) ? 1.f : 0.f;
+      for (int i = 0; i < 16; ++i) x[i] = (i == xi) ? 1.f : 0.f;
+      const float* Lb = sL + (16 * w) * CP + 16 * w;
 #pragma unroll
-      for (int m = 0; m < i; ++m) acc -= sL[i * CP + m] * x[m];
-      x[i] = acc;
+      for (int j = 0; j < 15; ++j)
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] -= Lb[i * CP + j] * x[j];
+      if (gq == 0)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sA[(16 * w + i) * CP + 16 * w + xi] = x[i];
     }
+    for (int e = tid; e < C * C; e += kBW) {  // blocks above the diagonal are zero
+      const int i = e / C, j = e % C;
+      if (j / 16 > i / 16) sA[i * CP + j] = 0.f;
+    }
+    __syncthreads();
+    if (w < 4) {
+      floatx4 Dw, Ab[4];
 #pragma unroll
-    for (int i = 0; i < C; ++i) sA[i * CP + j] = x[i];
+      for (int q = 0; q < 4; ++q) Dw[q] = sA[(16 * w + 4 * gq + q) * CP + 16 * w + xi];
+#pragma unroll
+      for (int ib = 1; ib < 4; ++ib) {
+        Ab[ib] = zero4();
+        if (ib > w) {
+          floatx4 P = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 3; ++kb) {
+            if (kb >= w && kb < ib) {
+              floatx4 La;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) La[q] = sL[(16 * ib + xi) * CP + 16 * kb + 4 * gq + q];
+              P = mma16_f32(P, La, kb == w ? Dw : Ab[kb]);
+            }
+          }
+          floatx4 Da;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) Da[q] = sA[(16 * ib + xi) * CP + 16 * ib + 4 * gq + q];
+          Ab[ib] = -mma16_f32(zero4(), Da, P);
+        }
+      }
+#pragma unroll
+      for (int ib = 1; ib < 4; ++ib)
+        if (ib > w)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sA[(16 * ib + 4 * gq + r) * CP + 16 * w + xi] = Ab[ib][r];
+    }
+    __syncthreads();
   }
-  __syncthreads();
   for (int e = tid; e < C * C; e += kBW) sl[o.a + e] = sA[(e / C) * CP + e % C];
 
   // W = A Kb, U = A Vb on fp32 MFMA: output tile (row block ib, 16 channels ct),
