@@ -723,23 +723,46 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   const int qf32 = !a.bf16_qkv;
   const float s = a.scale;
 
-  if (tid < C) sBeta[tid] = P.BETA[tid];
-  for (int e = tid; e < C * K / 4; e += kBW) {
-    reinterpret_cast<floatx4*>(sG)[e] = reinterpret_cast<const floatx4*>(P.G)[e];
-    reinterpret_cast<floatx4*>(sKN)[e] = reinterpret_cast<const floatx4*>(P.KN)[e];
-    reinterpret_cast<floatx4*>(sQN)[e] = reinterpret_cast<const floatx4*>(P.QN)[e];
+  // staging: every load of the thread first, then the LDS stores
+  constexpr int N4 = C * K / 4 / kBW, NPP = C * C / kBW;
+  static_assert(N4 * 4 * kBW == C * K && NPP * kBW == C * C, "staging split");
+  floatx4 rg4[N4], rk4[N4], rq4[N4];
+  float rp[NPP], rl[NPP], rbeta[NPP];
+#pragma unroll
+  for (int m = 0; m < N4; ++m) {
+    const int e = tid + kBW * m;
+    rg4[m] = reinterpret_cast<const floatx4*>(P.G)[e];
+    rk4[m] = reinterpret_cast<const floatx4*>(P.KN)[e];
+    rq4[m] = reinterpret_cast<const floatx4*>(P.QN)[e];
   }
+#pragma unroll
+  for (int m = 0; m < NPP; ++m) {
+    const int e = tid + kBW * m;
+    rp[m] = P.DAQK[e];
+    rl[m] = P.DL[e];
+    rbeta[m] = P.BETA[e / C];
+  }
+  const float rb = tid < C ? P.BETA[tid] : 0.f;
+#pragma unroll
+  for (int m = 0; m < N4; ++m) {
+    const int e = tid + kBW * m;
+    reinterpret_cast<floatx4*>(sG)[e] = rg4[m];
+    reinterpret_cast<floatx4*>(sKN)[e] = rk4[m];
+    reinterpret_cast<floatx4*>(sQN)[e] = rq4[m];
+  }
+#pragma unroll
+  for (int m = 0; m < NPP; ++m) {
+    const int e = tid + kBW * m;
+    sP[(e / C) * CP + e % C] = rp[m];
+    sDM[(e / C) * CP + e % C] = rbeta[m] * rl[m];
+  }
+  if (tid < C) sBeta[tid] = rb;
   // gradient of the last row's cumulative gate through KG and gamma
   if (tid < K) {
     float acc = P.DGAM[tid] * P.GAM[tid];
 #pragma unroll 16
     for (int r = 0; r < C; ++r) acc += P.DKG[r * K + tid] * P.KG[r * K + tid];
     sDGl[tid] = acc;
-  }
-  __syncthreads();
-  for (int e = tid; e < C * C; e += kBW) {
-    sP[(e / C) * CP + e % C] = P.DAQK[e];
-    sDM[(e / C) * CP + e % C] = sBeta[e / C] * P.DL[e];
   }
   __syncthreads();
 
