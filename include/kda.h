@@ -197,7 +197,8 @@ kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k
  * keeping them from the forward).
  *   p, q, k, v, g, beta, initial_state, cu_seqlens: exactly as passed to kda_chunk_fwd
  *     (g is the log decay: the gate activation of kda_chunk_fwd_gated has no backward here).
- *   d_o:           [B, T, H, V] in qkv_dtype, the gradient of o (rows of every token used).
+ *   d_o:           [B, T, H, V] in qkv_dtype, the gradient of o (rows of every token used),
+ *                  16-byte aligned; q, k, v, g, beta aligned to their element size.
  *   d_final_state: [N, H, K, V] fp32 or NULL (zero).
  *   dq, dk, dg:    [B, T, H, K] fp32;  dv: [B, T, H, V] fp32;  dbeta: [B, T, H] fp32.
  *     With use_qk_l2norm, dq and dk are the gradients of the un-normalised q and k.

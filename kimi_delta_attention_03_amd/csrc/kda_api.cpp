@@ -308,8 +308,9 @@ kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const v
     if (!dq || !dk || !dv || !dg || !dbeta)
       return fail(KDA_ERR_INVALID_ARG, "dq, dk, dv, dg and dbeta must be non-NULL");
     const size_t ea = p->qkv_dtype == KDA_DTYPE_BF16 ? 2 : 4;
-    for (const void* t : {q, k, v, d_o})
+    for (const void* t : {q, k, v})
       if (!aligned(t, ea)) return fail(KDA_ERR_INVALID_ARG, "q, k, v and d_o must be aligned to their element size");
+    if (!aligned(d_o, 16)) return fail(KDA_ERR_INVALID_ARG, "d_o must be 16-byte aligned");
     if (!aligned(g, p->g_dtype == KDA_DTYPE_BF16 ? 2 : 4) || !aligned(beta, p->beta_dtype == KDA_DTYPE_BF16 ? 2 : 4))
       return fail(KDA_ERR_INVALID_ARG, "g and beta must be aligned to their element size");
     for (const float* t : {dq, dk, dv, dg, dbeta})

@@ -543,7 +543,13 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
     }
   floatx4 rKG[NF], rQG[NF], rW[NF], rA[NA];
-  float rO[4];
+  // dO block of the chunk as raw bits (fp32: four words; bf16: two words), kept
+  // unconverted until it is staged so that the prefetch never waits for it
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x4 rO32 = {0u, 0u, 0u, 0u};
+  u32x2 rO16 = {0u, 0u};
+  bool rOk = false;
   float rG = 0.f;
   auto fetch = [&](int cc) {
     const float* sl = slab_of(a, p0 + cc, h);
@@ -557,9 +563,10 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
     for (int m = 0; m < NA; ++m) rA[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (tid + kBT * m));
     const ItemB it = chunk_of(a, p0 + cc, h);
     const int r = tid >> 2, c0 = 16 * vb + 4 * (tid & 3);
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      rO[c] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * a.H + h) * V + c0 + c, qf32) : 0.f;
+    rOk = r < it.len;
+    const size_t at = ((size_t)(it.tok0 + (rOk ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
+    if (qf32) rO32 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.d_o) + at);
+    else rO16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
     if (tid < K) rG = sl[o.gam + tid];
   };
   if (nch > 0) fetch(nch - 1);
@@ -577,8 +584,20 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       const int e = 4 * (tid + kBT * m);
       *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = rA[m];
     }
+    {
+      float dov[4];
+      if (qf32) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sdO[(tid >> 2) * 17 + 4 * (tid & 3) + c] = rO[c];
+        for (int c = 0; c < 4; ++c) dov[c] = __uint_as_float(rO32[c]);
+      } else {
+        dov[0] = __uint_as_float(rO16[0] << 16);
+        dov[1] = __uint_as_float(rO16[0] & 0xffff0000u);
+        dov[2] = __uint_as_float(rO16[1] << 16);
+        dov[3] = __uint_as_float(rO16[1] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sdO[(tid >> 2) * 17 + 4 * (tid & 3) + c] = rOk ? dov[c] : 0.f;
+    }
     if (tid < K) sGam[tid] = rG;
     float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
