@@ -675,12 +675,18 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
   const SlabPtrs P = slab_ptrs(slab_of(a, it.p, it.h), a.sl);
   const int qf32 = !a.bf16_qkv;
 
-  for (int e = tid; e < C * V; e += kBT) {
-    const int r = e / V, d = e % V;
-    P.DO[e] = r < it.len ? ldx(a.d_o, ((size_t)(it.tok0 + r) * a.H + it.h) * V + d, qf32) : 0.f;
+  {
+    // dO of the chunk into the slab: all loads first (typed), then the stores
+    constexpr int NE = C * V / kBT;
+    float dov[NE];
+    if (qf32) load_rows<float, NE, kBT, V>(a.d_o, it, a.H, dov);
+    else load_rows<bf16, NE, kBT, V>(a.d_o, it, a.H, dov);
+#pragma unroll
+    for (int m = 0; m < NE; ++m) P.DO[tid + kBT * m] = dov[m];
   }
   if (tid < K) {
     float acc = 0.f;
+#pragma unroll 16
     for (int v = 0; v < V; ++v) acc += P.S[tid * V + v] * P.DS[tid * V + v];
     P.DGAM[tid] = acc;
   }
