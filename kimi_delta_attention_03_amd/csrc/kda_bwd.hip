@@ -29,8 +29,11 @@
 //   chunk       per (chunk, head): every other gradient, as two launches (the
 //               matrix products, then the elementwise and gated-sum rules)
 // Every intermediate lives in a per-(chunk, head) fp32 slab of the workspace.
-// The per-chunk kernels are latency-bound chains of phases and run 16 waves
-// per workgroup; the two state passes are bound by their per-chunk chain.
+// prep and the elementwise kernel are latency-bound chains of phases and run
+// 16 waves per workgroup (one workgroup per CU by LDS); the product kernel runs
+// 4 waves with its operand slices double-buffered; the two state passes are
+// bound by their per-chunk chain. Loads are issued before stores throughout: on
+// this GPU a memory-counter wait also waits for every earlier store.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -791,7 +794,7 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   }
   __syncthreads();
 
-  // output tiles (row block ib, channel tile ct): wave w takes every 4th
+  // output tiles (row block ib, channel tile ct): wave w takes tiles w, w + 16, ...
   for (int tile = w; tile < 4 * NCT; tile += kNWW) {
     const int ib = tile / NCT, ct = tile % NCT;
     const int d = 16 * ct + xi;
