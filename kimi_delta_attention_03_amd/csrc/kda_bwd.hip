@@ -322,6 +322,12 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
   }
   __syncthreads();
 
+  // the q rows are no longer needed: their LDS holds Vb for the U product below
+#pragma unroll
+  for (int m = 0; m < NE; ++m) {
+    const int e = tid + kBW * m;
+    sQ[(e / V) * KP + e % V] = sB[e / V] * vv[m];
+  }
   // A = (I + L)^-1, blocked: wave w < 4 inverts diagonal block w by forward
   // substitution (lane xi -> column xi; the four lane groups compute the same
   // values), then its block column below the diagonal on fp32 MFMA:
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         const int j = k0 + gq;
         const float aij = sA[(16 * ib + xi) * CP + j];
         accW = mfma4(aij, sB[j] * sK[j * KP + d] * __expf(sG[j * KP + d]), accW);
-        accU = mfma4(aij, sl[o.vb + j * V + d], accU);
+        accU = mfma4(aij, sQ[j * KP + d], accU);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -795,7 +801,25 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   __syncthreads();
 
   // output tiles (row block ib, channel tile ct): wave w takes tiles w, w + 16, ...
-  for (int tile = w; tile < 4 * NCT; tile += kNWW) {
+  // The per-element gradients each tile's epilogue needs are loaded up front, so
+  // that no load waits behind an earlier tile's stores.
+  constexpr int TPWE = 4 * NCT / kNWW;
+  static_assert(TPWE >= 1 && TPWE * kNWW == 4 * NCT, "tile split");
+  float pdqg[TPWE][4], pdkb[TPWE][4], pdkg[TPWE][4];
+#pragma unroll
+  for (int t = 0; t < TPWE; ++t) {
+    const int tile = w + kNWW * t, ib = tile / NCT, d = 16 * (tile % NCT) + xi;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * ib + 4 * gq + r;
+      pdqg[t][r] = P.DQG[i * K + d];
+      pdkb[t][r] = P.DKB[i * K + d];
+      pdkg[t][r] = P.DKG[i * K + d];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < TPWE; ++t) {
+    const int tile = w + kNWW * t;
     const int ib = tile / NCT, ct = tile % NCT;
     const int d = 16 * ct + xi;
     floatx4 qa = zero4(), qm = zero4(), ka = zero4(), km = zero4();
@@ -842,7 +866,7 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
       const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
       const float Gl = sG[(C - 1) * K + d];
       const float eg = __expf(Gi), egl = __expf(Gl - Gi);
-      const float dqg = P.DQG[i * K + d], dkb = P.DKB[i * K + d], dkg = P.DKG[i * K + d];
+      const float dqg = pdqg[t][r], dkb = pdkb[t][r], dkg = pdkg[t][r];
       P.DQN[i * K + d] = s * eg * dqg + s * qa[r];
       P.DKN[i * K + d] = dkb * bi * eg + dkg * egl + s * ka[r] + qm[r] + km[r];
       // Qg = s q e^G, Kb = beta k e^G and KG = k e^(Gl - G) rebuilt from the staged rows
