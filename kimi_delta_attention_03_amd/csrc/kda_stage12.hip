@@ -274,44 +274,88 @@ void stage12_kernel(Stage12Args a) {
       sKn[tid] = 1.f;
     }
     // inclusive cumsum over rows: thread (cg, seg) sums its CPT channels over the
-    // RPS rows of segment seg into sG, then adds the totals of all earlier
-    // segments (in segment order) and converts to log2 units
+    // RPS rows of segment seg. The four segments of a wave sit in its four
+    // 16-lane rows (seg % 4 == gq), so their exclusive prefix is a scan across
+    // lane rows (permlane swaps); the rows go to sG with that prefix included
+    // and the wave's total to sA. After the barrier, the totals of the earlier
+    // waves are added and the result is converted to log2 units.
     {
+      float lam = 0.f;
+      if constexpr (GATE) lam = __expf(R.alog);
+      auto gate = [&](int rr, int c) {
+        float gv;
+        if constexpr (GF32) gv = __uint_as_float(R.g[rr][c / 4][c % 4]);
+        else gv = (c & 1) ? __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] & 0xffff0000u)
+                          : __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] << 16);
+        if constexpr (GATE) {
+          const float x = gv + R.gbias[c];
+          // hardware exp2 / log2 based exp and log: the activations only need
+          // fp32 relative accuracy where the decay is not ~1 anyway
+          if (a.gate_mode == 1) {
+            const float sp = fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));  // softplus, stable form
+            gv = -lam * sp;
+          } else {
+            gv = a.gate_lb / (1.f + __expf(-lam * x));  // lower_bound * sigmoid
+          }
+          if (seg * RPS + rr >= it.len) gv = 0.f;
+        }
+        return gv;
+      };
+      auto put_row = [&](int rr, int c, floatx4 x) {
+        *reinterpret_cast<floatx4*>(sG + (seg * RPS + rr) * GS + cg * CPT + c) = x;
+      };
+      // segment totals; with the activation the rows (without the prefix) are
+      // stored on the way, so that it is evaluated once
       float run[CPT];
 #pragma unroll
       for (int c = 0; c < CPT; ++c) run[c] = 0.f;
-      float lam = 0.f;
-      if constexpr (GATE) lam = __expf(R.alog);
 #pragma unroll
       for (int rr = 0; rr < RPS; ++rr) {
 #pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          float gv;
-          if constexpr (GF32) gv = __uint_as_float(R.g[rr][c / 4][c % 4]);
-          else gv = (c & 1) ? __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] & 0xffff0000u)
-                            : __uint_as_float(R.g[rr][c / 8][(c % 8) / 2] << 16);
-          if constexpr (GATE) {
-            const float x = gv + R.gbias[c];
-            // hardware exp2 / log2 based exp and log: the activations only need
-            // fp32 relative accuracy where the decay is not ~1 anyway
-            if (a.gate_mode == 1) {
-              const float sp = fmaxf(x, 0.f) + __logf(1.f + __expf(-fabsf(x)));  // softplus, stable form
-              gv = -lam * sp;
-            } else {
-              gv = a.gate_lb / (1.f + __expf(-lam * x));  // lower_bound * sigmoid
-            }
-            if (seg * RPS + rr >= it.len) gv = 0.f;
-          }
-          run[c] += gv;
+        for (int c = 0; c < CPT; ++c) run[c] += gate(rr, c);
+        if constexpr (GATE) {
+#pragma unroll
+          for (int c = 0; c < CPT; c += 4) put_row(rr, c, floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]});
         }
+      }
+      // exclusive prefix over lane rows r = 0..3 of the totals x_r:
+      // permlane16_swap(x, x) gives {x0, x0, x2, x2} and {x1, x1, x3, x3} by row,
+      // permlane32_swap(P, P) of the pair sums P gives {P01 x4} and {P23 x4}
+      float pre[CPT];
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const unsigned xu = __float_as_uint(run[c]);
+        const auto a16 = __builtin_amdgcn_permlane16_swap(xu, xu, false, false);
+        const float lo = __uint_as_float(a16[0]), hi = __uint_as_float(a16[1]);
+        const unsigned Pu = __float_as_uint(lo + hi);
+        const auto a32 = __builtin_amdgcn_permlane32_swap(Pu, Pu, false, false);
+        const float P01 = __uint_as_float(a32[0]), P23 = __uint_as_float(a32[1]);
+        pre[c] = ((gq & 1) ? lo : 0.f) + ((gq & 2) ? P01 : 0.f);
+        run[c] = P01 + P23;  // this wave's total
+      }
+      if (gq == 0) {
 #pragma unroll
         for (int c = 0; c < CPT; c += 4)
-          *reinterpret_cast<floatx4*>(sG + (seg * RPS + rr) * GS + cg * CPT + c) =
-              floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
+          *reinterpret_cast<floatx4*>(sA + w * K + cg * CPT + c) = floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
       }
+      if constexpr (GATE) {
 #pragma unroll
-      for (int c = 0; c < CPT; c += 4)
-        *reinterpret_cast<floatx4*>(sA + seg * K + cg * CPT + c) = floatx4{run[c], run[c + 1], run[c + 2], run[c + 3]};
+        for (int rr = 0; rr < RPS; ++rr) {
+#pragma unroll
+          for (int c = 0; c < CPT; c += 4) {
+            const floatx4 p4{pre[c], pre[c + 1], pre[c + 2], pre[c + 3]};
+            put_row(rr, c, ldsf4(sG + (seg * RPS + rr) * GS + cg * CPT + c) + p4);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < RPS; ++rr) {
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) pre[c] += gate(rr, c);
+#pragma unroll
+          for (int c = 0; c < CPT; c += 4) put_row(rr, c, floatx4{pre[c], pre[c + 1], pre[c + 2], pre[c + 3]});
+        }
+      }
     }
     // k, g and beta of this item are consumed: start loading the next item's
     if constexpr (kPrefetch) issue_kgb(R, nx);
@@ -321,10 +365,8 @@ void stage12_kernel(Stage12Args a) {
       for (int c = 0; c < CPT; c += 4) {
         floatx4 carry = zero4();
 #pragma unroll
-        for (int s = 0; s < SEG - 1; ++s) {
-          const floatx4 t4 = ldsf4(sA + s * K + cg * CPT + c);
-          if (s < seg) carry += t4;
-        }
+        for (int s = 0; s < 3; ++s)
+          if (s < w) carry += ldsf4(sA + s * K + cg * CPT + c);
 #pragma unroll
         for (int rr = 0; rr < RPS; ++rr) {
           float* gp = sG + (seg * RPS + rr) * GS + cg * CPT + c;
