@@ -416,19 +416,25 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------- chunk-start states
-// One workgroup per (sequence, head, 16-column block) walks the chunks in order.
-// Wave w keeps state rows [16 TPW w, 16 TPW (w + 1)) of the block as fp32 MFMA
-// accumulators (16x16x4: lane (g, i) = (l / 16, l % 16) holds rows 4 g + r,
-// column i of a 16 x 16 tile; an A operand lane holds row i, reduction index g of
-// a 4-deep slice, a B operand lane reduction index g, column i). The next
-// chunk's operands are loaded into registers while the current chunk computes.
+// One workgroup (8 waves) per (sequence, head, 16-column block) walks the
+// chunks in order. Compute wave w (0..3) keeps state rows [16 TPW w,
+// 16 TPW (w + 1)) of the block as fp32 MFMA accumulators (16x16x4: lane (g, i) =
+// (l / 16, l % 16) holds rows 4 g + r, column i of a 16 x 16 tile; an A operand
+// lane holds row i, reduction index g of a 4-deep slice, a B operand lane
+// reduction index g, column i). Loader waves 4..7 bring the next chunk's
+// operands into the other of two LDS buffers and copy the chunk-start state to
+// the slab, so the compute waves only run the two products of each chunk. Two
+// barriers per chunk: A (operands and start state published) and B (V_new
+// published, start state read).
 
 template <int K>
-__global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
   constexpr int V = K, KP = K + 4, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
-  __shared__ __attribute__((aligned(16))) float sW[C * KP], sKG[C * KP];
-  __shared__ __attribute__((aligned(16))) float sU[C * 20];
-  __shared__ float sVn[C * 17], sS[K * 17], sGam[K];
+  // two LDS buffers of the chunk operands: loader waves fill one while the
+  // compute waves multiply from the other
+  __shared__ __attribute__((aligned(16))) float sW[2][C * KP], sKG[2][C * KP];
+  __shared__ __attribute__((aligned(16))) float sU[2][C * 20];
+  __shared__ float sVn[C * 17], sS[K * 17], sGam[2][K];
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -443,78 +449,98 @@ __global__ __launch_bounds__(kBT) void bwd_states_fwd_kernel(BwdArgs a) {
   seq_chunks(a, seq, p0, nch);
   const int col = 16 * vb + xi;
 
-  floatx4 S[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * (TPW * w + t) + 4 * gq + r;
-      S[t][r] = a.init ? a.init[((size_t)u * K + row) * V + col] : 0.f;
-    }
-  // prefetch registers: W and KG as float4 (chunk-row-major), the U block, gamma
-  floatx4 rW[NF], rKG[NF], rU;
-  float rG = 0.f;
-  auto fetch = [&](int cc) {
-    const float* sl = slab_of(a, p0 + cc, h);
-#pragma unroll
-    for (int m = 0; m < NF; ++m) {
-      rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (tid + kBT * m));
-      rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (tid + kBT * m));
-    }
-    rU = *reinterpret_cast<const floatx4*>(sl + o.u + (tid >> 2) * V + 16 * vb + 4 * (tid & 3));
-    if (tid < K) rG = sl[o.gam + tid];
-  };
-  if (nch > 0) fetch(0);
-  for (int cc = 0; cc < nch; ++cc) {
-    __syncthreads();  // the previous chunk's operands are no longer read
-#pragma unroll
-    for (int m = 0; m < NF; ++m) {
-      const int e = 4 * (tid + kBT * m), r = e / K, d = e % K;
-      *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
-      *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
-    }
-    *reinterpret_cast<floatx4*>(sU + (tid >> 2) * 20 + 4 * (tid & 3)) = rU;
-    if (tid < K) sGam[tid] = rG;
-    float* sl = slab_of(a, p0 + cc, h);
+  if (w < 4) {
+    // ---------------------------------------------------------- compute waves
+    // wave w: V_new rows 16 w .. 16 w + 15, state rows 16 (TPW w + t) ..
+    floatx4 S[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * (TPW * w + t) + 4 * gq + r;
-        sl[o.S + row * V + col] = S[t][r];  // chunk-start state
+        S[t][r] = a.init ? a.init[((size_t)u * K + row) * V + col] : 0.f;
         sS[row * 17 + xi] = S[t][r];
       }
-    if (cc + 1 < nch) fetch(cc + 1);
-    __syncthreads();
-    // Vn rows 16 w .. 16 w + 15 = U - W S (four independent accumulator chains)
-    {
-      floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int cc = 0; cc < nch; ++cc) {
+      const int b = cc & 1;
+      __syncthreads();  // A: operands of chunk cc and its start state published
+      // Vn = U - W S (four independent accumulator chains)
+      {
+        floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-      for (int k0 = 0; k0 < K; k0 += 16)
+        for (int k0 = 0; k0 < K; k0 += 16)
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          acc[c] = mfma4(sW[(16 * w + xi) * KP + k0 + 4 * c + gq], sS[(k0 + 4 * c + gq) * 17 + xi], acc[c]);
-      const floatx4 ws = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+          for (int c = 0; c < 4; ++c)
+            acc[c] = mfma4(sW[b][(16 * w + xi) * KP + k0 + 4 * c + gq], sS[(k0 + 4 * c + gq) * 17 + xi], acc[c]);
+        const floatx4 ws = (acc[0] + acc[1]) + (acc[2] + acc[3]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * w + 4 * gq + r;
-        sVn[i * 17 + xi] = sU[i * 20 + xi] - ws[r];
+        for (int r = 0; r < 4; ++r) {
+          const int i = 16 * w + 4 * gq + r;
+          sVn[i * 17 + xi] = sU[b][i * 20 + xi] - ws[r];
+        }
+      }
+      __syncthreads();  // B: Vn published; the start state has been read
+      // S = Diag(gamma) S + KG^T Vn (two accumulator chains per tile)
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int rt = TPW * w + t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[t][r] *= sGam[b][16 * rt + 4 * gq + r];
+        floatx4 acc2 = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < C; k0 += 8) {
+          S[t] = mfma4(sKG[b][(k0 + gq) * KP + 16 * rt + xi], sVn[(k0 + gq) * 17 + xi], S[t]);
+          acc2 = mfma4(sKG[b][(k0 + 4 + gq) * KP + 16 * rt + xi], sVn[(k0 + 4 + gq) * 17 + xi], acc2);
+        }
+        S[t] += acc2;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sS[(16 * rt + 4 * gq + r) * 17 + xi] = S[t][r];
       }
     }
-    __syncthreads();
-    // S = Diag(gamma) S + KG^T Vn (two accumulator chains per tile)
+  } else {
+    // ----------------------------------------------------------- loader waves
+    // thread lt loads W and KG as float4 (chunk-row-major), one float4 of the
+    // U block and one gamma, and copies K / 16 entries of the chunk-start
+    // state (column lt % 16) to the checkpoint
+    const int lt = tid - kBT;
+    constexpr int NSC = K / 16;
+    floatx4 rW[NF], rKG[NF], rU;
+    float rG = 0.f;
+    auto fetch = [&](int cc) {
+      const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int rt = TPW * w + t;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) S[t][r] *= sGam[16 * rt + 4 * gq + r];
-      floatx4 acc2 = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < C; k0 += 8) {
-        S[t] = mfma4(sKG[(k0 + gq) * KP + 16 * rt + xi], sVn[(k0 + gq) * 17 + xi], S[t]);
-        acc2 = mfma4(sKG[(k0 + 4 + gq) * KP + 16 * rt + xi], sVn[(k0 + 4 + gq) * 17 + xi], acc2);
+      for (int m = 0; m < NF; ++m) {
+        rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
+        rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
       }
-      S[t] += acc2;
+      rU = *reinterpret_cast<const floatx4*>(sl + o.u + (lt >> 2) * V + 16 * vb + 4 * (lt & 3));
+      if (lt < K) rG = sl[o.gam + lt];
+    };
+    auto stage = [&](int b) {
+#pragma unroll
+      for (int m = 0; m < NF; ++m) {
+        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
+        *reinterpret_cast<floatx4*>(&sW[b][r * KP + d]) = rW[m];
+        *reinterpret_cast<floatx4*>(&sKG[b][r * KP + d]) = rKG[m];
+      }
+      *reinterpret_cast<floatx4*>(&sU[b][(lt >> 2) * 20 + 4 * (lt & 3)]) = rU;
+      if (lt < K) sGam[b][lt] = rG;
+    };
+    if (nch > 0) {
+      fetch(0);
+      stage(0);
+    }
+    for (int cc = 0; cc < nch; ++cc) {
+      __syncthreads();  // A
+      if (cc + 1 < nch) fetch(cc + 1);
+      float rS[NSC];
+#pragma unroll
+      for (int m = 0; m < NSC; ++m) rS[m] = sS[((lt >> 4) + 16 * m) * 17 + (lt & 15)];
+      __syncthreads();  // B
+      float* sl = slab_of(a, p0 + cc, h);
+#pragma unroll
+      for (int m = 0; m < NSC; ++m) sl[o.S + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+      if (cc + 1 < nch) stage((cc + 1) & 1);
     }
   }
 }
@@ -978,7 +1004,7 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   if ((stages & 1) && nitems > 0) hipLaunchKernelGGL(bwd_prep_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
   if (a.nunits > 0) {
     if ((stages & 2) && nitems > 0)
-      hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(sgrid), dim3(kBT), 0, s, a);
+      hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
     if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(kBT), 0, s, a);
   }
   if ((stages & 8) && nitems > 0) {
