@@ -434,7 +434,11 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
   // compute waves multiply from the other
   __shared__ __attribute__((aligned(16))) float sW[2][C * KP], sKG[2][C * KP];
   __shared__ __attribute__((aligned(16))) float sU[2][C * 20];
-  __shared__ float sVn[C * 17], sS[K * 17], sGam[2][K];
+  // the start state and V_new transposed (column-major, rows padded by 4), so
+  // that a lane reads 4 consecutive reduction indices at once
+  constexpr int SP = K + 4, VP = C + 4;
+  __shared__ __attribute__((aligned(16))) float sST[16 * SP], sVnT[16 * VP];
+  __shared__ float sGam[2][K];
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -459,42 +463,60 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * (TPW * w + t) + 4 * gq + r;
         S[t][r] = a.init ? a.init[((size_t)u * K + row) * V + col] : 0.f;
-        sS[row * 17 + xi] = S[t][r];
       }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      *reinterpret_cast<floatx4*>(sST + xi * SP + 16 * (TPW * w + t) + 4 * gq) = S[t];
+    // The reduction index of 16-deep slice k0 is ordered k0 + 4 g + s (lane group
+    // g, MFMA step s), so each lane's operands for the 4 steps are 4 consecutive
+    // floats: one 16-byte LDS read instead of four, all issued before the MFMAs.
     for (int cc = 0; cc < nch; ++cc) {
       const int b = cc & 1;
       __syncthreads();  // A: operands of chunk cc and its start state published
-      // Vn = U - W S (four independent accumulator chains)
+      // Vn = U - W S (four independent accumulator chains, one per step s)
       {
+        floatx4 Wa[K / 16], Sb[K / 16];
+#pragma unroll
+        for (int q = 0; q < K / 16; ++q) {
+          Wa[q] = *reinterpret_cast<const floatx4*>(&sW[b][(16 * w + xi) * KP + 16 * q + 4 * gq]);
+          Sb[q] = *reinterpret_cast<const floatx4*>(sST + xi * SP + 16 * q + 4 * gq);
+        }
         floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
-        for (int k0 = 0; k0 < K; k0 += 16)
+        for (int q = 0; q < K / 16; ++q)
 #pragma unroll
-          for (int c = 0; c < 4; ++c)
-            acc[c] = mfma4(sW[b][(16 * w + xi) * KP + k0 + 4 * c + gq], sS[(k0 + 4 * c + gq) * 17 + xi], acc[c]);
+          for (int st = 0; st < 4; ++st) acc[st] = mfma4(Wa[q][st], Sb[q][st], acc[st]);
         const floatx4 ws = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        floatx4 vn;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * w + 4 * gq + r;
-          sVn[i * 17 + xi] = sU[b][i * 20 + xi] - ws[r];
-        }
+        for (int r = 0; r < 4; ++r) vn[r] = sU[b][(16 * w + 4 * gq + r) * 20 + xi] - ws[r];
+        *reinterpret_cast<floatx4*>(sVnT + xi * VP + 16 * w + 4 * gq) = vn;
       }
       __syncthreads();  // B: Vn published; the start state has been read
       // S = Diag(gamma) S + KG^T Vn (two accumulator chains per tile)
+      floatx4 Vb[C / 16];
+#pragma unroll
+      for (int q = 0; q < C / 16; ++q) Vb[q] = *reinterpret_cast<const floatx4*>(sVnT + xi * VP + 16 * q + 4 * gq);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int rt = TPW * w + t;
+        float Ka[C / 16][4];
+#pragma unroll
+        for (int q = 0; q < C / 16; ++q)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) Ka[q][st] = sKG[b][(16 * q + 4 * gq + st) * KP + 16 * rt + xi];
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[t][r] *= sGam[b][16 * rt + 4 * gq + r];
         floatx4 acc2 = zero4();
 #pragma unroll
-        for (int k0 = 0; k0 < C; k0 += 8) {
-          S[t] = mfma4(sKG[b][(k0 + gq) * KP + 16 * rt + xi], sVn[(k0 + gq) * 17 + xi], S[t]);
-          acc2 = mfma4(sKG[b][(k0 + 4 + gq) * KP + 16 * rt + xi], sVn[(k0 + 4 + gq) * 17 + xi], acc2);
+        for (int q = 0; q < C / 16; ++q) {
+          S[t] = mfma4(Ka[q][0], Vb[q][0], S[t]);
+          acc2 = mfma4(Ka[q][1], Vb[q][1], acc2);
+          S[t] = mfma4(Ka[q][2], Vb[q][2], S[t]);
+          acc2 = mfma4(Ka[q][3], Vb[q][3], acc2);
         }
         S[t] += acc2;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sS[(16 * rt + 4 * gq + r) * 17 + xi] = S[t][r];
+        *reinterpret_cast<floatx4*>(sST + xi * SP + 16 * rt + 4 * gq) = S[t];
       }
     }
   } else {
@@ -504,43 +526,53 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
     // state (column lt % 16) to the checkpoint
     const int lt = tid - kBT;
     constexpr int NSC = K / 16;
-    floatx4 rW[NF], rKG[NF], rU;
-    float rG = 0.f;
-    auto fetch = [&](int cc) {
+    struct Regs { floatx4 w[NF], kg[NF], u; float g; };
+    // two register sets: the loads of chunk c + 2 are issued while chunk c
+    // computes and staged one chunk later. The chunk index is clamped, so the
+    // loads are unconditional and the memory-counter waits stay exact.
+    auto fetch = [&](Regs& r, int cc) {
+      cc = cc < nch - 1 ? cc : nch - 1;
       const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
       for (int m = 0; m < NF; ++m) {
-        rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
-        rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
+        r.w[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
+        r.kg[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
       }
-      rU = *reinterpret_cast<const floatx4*>(sl + o.u + (lt >> 2) * V + 16 * vb + 4 * (lt & 3));
-      if (lt < K) rG = sl[o.gam + lt];
+      r.u = *reinterpret_cast<const floatx4*>(sl + o.u + (lt >> 2) * V + 16 * vb + 4 * (lt & 3));
+      r.g = sl[o.gam + (lt < K ? lt : 0)];
     };
-    auto stage = [&](int b) {
+    auto stage = [&](const Regs& r, int b) {
 #pragma unroll
       for (int m = 0; m < NF; ++m) {
-        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
-        *reinterpret_cast<floatx4*>(&sW[b][r * KP + d]) = rW[m];
-        *reinterpret_cast<floatx4*>(&sKG[b][r * KP + d]) = rKG[m];
+        const int e = 4 * (lt + kBT * m), rr = e / K, d = e % K;
+        *reinterpret_cast<floatx4*>(&sW[b][rr * KP + d]) = r.w[m];
+        *reinterpret_cast<floatx4*>(&sKG[b][rr * KP + d]) = r.kg[m];
       }
-      *reinterpret_cast<floatx4*>(&sU[b][(lt >> 2) * 20 + 4 * (lt & 3)]) = rU;
-      if (lt < K) sGam[b][lt] = rG;
+      *reinterpret_cast<floatx4*>(&sU[b][(lt >> 2) * 20 + 4 * (lt & 3)]) = r.u;
+      if (lt < K) sGam[b][lt] = r.g;
     };
-    if (nch > 0) {
-      fetch(0);
-      stage(0);
-    }
-    for (int cc = 0; cc < nch; ++cc) {
+    // chunk cc: cur holds chunk cc + 1 (staged after barrier B), nxt receives chunk cc + 2
+    auto step = [&](int cc, Regs& cur, Regs& nxt) {
       __syncthreads();  // A
-      if (cc + 1 < nch) fetch(cc + 1);
+      fetch(nxt, cc + 2);
       float rS[NSC];
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) rS[m] = sS[((lt >> 4) + 16 * m) * 17 + (lt & 15)];
+      for (int m = 0; m < NSC; ++m) rS[m] = sST[(lt & 15) * SP + (lt >> 4) + 16 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
       for (int m = 0; m < NSC; ++m) sl[o.S + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
-      if (cc + 1 < nch) stage((cc + 1) & 1);
+      if (cc + 1 < nch) stage(cur, (cc + 1) & 1);
+    };
+    if (nch > 0) {
+      Regs R0, R1;
+      fetch(R0, 0);
+      fetch(R1, 1);
+      stage(R0, 0);
+      for (int cc = 0; cc < nch; cc += 2) {
+        step(cc, R1, R0);
+        if (cc + 1 < nch) step(cc + 1, R0, R1);
+      }
     }
   }
 }
