@@ -578,14 +578,19 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ state gradients
-// Same layout as above, chunks in reverse: wave w keeps rows of dS (the
-// gradient of the state at the current chunk boundary) as accumulators.
+// Same layout as above, chunks in reverse: compute wave w (0..3) keeps rows of
+// dS (the gradient of the state at the current chunk boundary) as
+// accumulators. Three barriers per chunk: A (chunk operands and dS' published),
+// B (dVn published), C (the update is done). Loader waves 4..7 copy dS' to the
+// slab and stage the previous chunk's operands in two groups: KG, Aqk, dO and
+// gamma after B (dO and gamma into the other of two buffers), Qg and W after
+// C; each group's next loads are issued as soon as it is staged.
 template <int K>
-__global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
   constexpr int V = K, KP = K + 4, CP = C + 4, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
   constexpr int NA = C * C / 4 / kBT;
   __shared__ __attribute__((aligned(16))) float sKG[C * KP], sQG[C * KP], sW[C * KP], sAq[C * CP];
-  __shared__ float sdO[C * 17], sdVn[C * 17], sdS[K * 17], sGam[K];
+  __shared__ float sdO[2][C * 17], sdVn[C * 17], sdS[K * 17], sGam[2][K];
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -599,59 +604,109 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
   int p0, nch;
   seq_chunks(a, seq, p0, nch);
   const int col = 16 * vb + xi;
-  const int qf32 = !a.bf16_qkv;
 
-  floatx4 dS[TPW];
+  if (w < 4) {
+    // ---------------------------------------------------------- compute waves
+    floatx4 dS[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = 16 * (TPW * w + t) + 4 * gq + r;
-      dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + t) + 4 * gq + r;
+        dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
+        sdS[row * 17 + xi] = dS[t][r];
+      }
+    for (int cc = nch - 1; cc >= 0; --cc) {
+      const int b = cc & 1;
+      __syncthreads();  // A
+      // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS'
+      {
+        floatx4 acc = zero4();
+#pragma unroll 8
+        for (int k0 = 0; k0 < C; k0 += 4)
+          acc = mfma4(sAq[(k0 + gq) * CP + 16 * w + xi], sdO[b][(k0 + gq) * 17 + xi], acc);
+#pragma unroll 8
+        for (int k0 = 0; k0 < K; k0 += 4)
+          acc = mfma4(sKG[(16 * w + xi) * KP + k0 + gq], sdS[(k0 + gq) * 17 + xi], acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdVn[(16 * w + 4 * gq + r) * 17 + xi] = acc[r];
+      }
+      __syncthreads();  // B
+      // dS = Diag(gamma) dS' + Qg^T dO - W^T dVn
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int rt = TPW * w + t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dS[t][r] *= sGam[b][16 * rt + 4 * gq + r];
+#pragma unroll 8
+        for (int k0 = 0; k0 < C; k0 += 4) {
+          dS[t] = mfma4(sQG[(k0 + gq) * KP + 16 * rt + xi], sdO[b][(k0 + gq) * 17 + xi], dS[t]);
+          dS[t] = mfma4(-sW[(k0 + gq) * KP + 16 * rt + xi], sdVn[(k0 + gq) * 17 + xi], dS[t]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sdS[(16 * rt + 4 * gq + r) * 17 + xi] = dS[t][r];
+      }
+      __syncthreads();  // C
     }
-  floatx4 rKG[NF], rQG[NF], rW[NF], rA[NA];
-  // dO block of the chunk as raw bits (fp32: four words; bf16: two words), kept
-  // unconverted until it is staged so that the prefetch never waits for it
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-  u32x4 rO32 = {0u, 0u, 0u, 0u};
-  u32x2 rO16 = {0u, 0u};
-  bool rOk = false;
-  float rG = 0.f;
-  auto fetch = [&](int cc) {
-    const float* sl = slab_of(a, p0 + cc, h);
+    if (a.dh0) {
 #pragma unroll
-    for (int m = 0; m < NF; ++m) {
-      rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (tid + kBT * m));
-      rQG[m] = *reinterpret_cast<const floatx4*>(sl + o.qg + 4 * (tid + kBT * m));
-      rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (tid + kBT * m));
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (TPW * w + t) + 4 * gq + r;
+          a.dh0[((size_t)u * K + row) * V + col] = dS[t][r];
+        }
     }
+  } else {
+    // ----------------------------------------------------------- loader waves
+    const int lt = tid - kBT;
+    constexpr int NSC = K / 16;
+    const int qf32 = !a.bf16_qkv;
+    // dO block of the chunk as raw bits (fp32: four words; bf16: two words),
+    // converted when it is staged
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    floatx4 rKG[NF], rA[NA], rQG[NF], rW[NF];
+    u32x4 rO32 = {0u, 0u, 0u, 0u};
+    u32x2 rO16 = {0u, 0u};
+    bool rOk = false;
+    float rG = 0.f;
+    // loads are unconditional: the chunk index is clamped to 0
+    auto fetch1 = [&](int cc) {
+      cc = cc > 0 ? cc : 0;
+      const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-    for (int m = 0; m < NA; ++m) rA[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (tid + kBT * m));
-    const ItemB it = chunk_of(a, p0 + cc, h);
-    const int r = tid >> 2, c0 = 16 * vb + 4 * (tid & 3);
-    rOk = r < it.len;
-    const size_t at = ((size_t)(it.tok0 + (rOk ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
-    if (qf32) rO32 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.d_o) + at);
-    else rO16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
-    if (tid < K) rG = sl[o.gam + tid];
-  };
-  if (nch > 0) fetch(nch - 1);
-  for (int cc = nch - 1; cc >= 0; --cc) {
-    __syncthreads();
+      for (int m = 0; m < NF; ++m) rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
 #pragma unroll
-    for (int m = 0; m < NF; ++m) {
-      const int e = 4 * (tid + kBT * m), r = e / K, d = e % K;
-      *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
-      *reinterpret_cast<floatx4*>(sQG + r * KP + d) = rQG[m];
-      *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
-    }
+      for (int m = 0; m < NA; ++m) rA[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (lt + kBT * m));
+      const ItemB it = chunk_of(a, p0 + cc, h);
+      const int r = lt >> 2, c0 = 16 * vb + 4 * (lt & 3);
+      rOk = r < it.len;
+      const size_t at = ((size_t)(it.tok0 + (rOk ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
+      if (qf32) rO32 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.d_o) + at);
+      else rO16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
+      rG = sl[o.gam + (lt < K ? lt : 0)];
+    };
+    auto fetch2 = [&](int cc) {
+      cc = cc > 0 ? cc : 0;
+      const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-    for (int m = 0; m < NA; ++m) {
-      const int e = 4 * (tid + kBT * m);
-      *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = rA[m];
-    }
-    {
+      for (int m = 0; m < NF; ++m) {
+        rQG[m] = *reinterpret_cast<const floatx4*>(sl + o.qg + 4 * (lt + kBT * m));
+        rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
+      }
+    };
+    auto stage1 = [&](int b) {
+#pragma unroll
+      for (int m = 0; m < NF; ++m) {
+        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
+        *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
+      }
+#pragma unroll
+      for (int m = 0; m < NA; ++m) {
+        const int e = 4 * (lt + kBT * m);
+        *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = rA[m];
+      }
       float dov[4];
       if (qf32) {
 #pragma unroll
@@ -663,54 +718,40 @@ __global__ __launch_bounds__(kBT) void bwd_states_bwd_kernel(BwdArgs a) {
         dov[3] = __uint_as_float(rO16[1] & 0xffff0000u);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sdO[(tid >> 2) * 17 + 4 * (tid & 3) + c] = rOk ? dov[c] : 0.f;
-    }
-    if (tid < K) sGam[tid] = rG;
-    float* sl = slab_of(a, p0 + cc, h);
+      for (int c = 0; c < 4; ++c) sdO[b][(lt >> 2) * 17 + 4 * (lt & 3) + c] = rOk ? dov[c] : 0.f;
+      if (lt < K) sGam[b][lt] = rG;
+    };
+    auto stage2 = [&]() {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (TPW * w + t) + 4 * gq + r;
-        sl[o.dS + row * V + col] = dS[t][r];  // gradient of the chunk-end state
-        sdS[row * 17 + xi] = dS[t][r];
+      for (int m = 0; m < NF; ++m) {
+        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
+        *reinterpret_cast<floatx4*>(sQG + r * KP + d) = rQG[m];
+        *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
       }
-    if (cc > 0) fetch(cc - 1);
-    __syncthreads();
-    // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS'
-    {
-      floatx4 acc = zero4();
-#pragma unroll 8
-      for (int k0 = 0; k0 < C; k0 += 4)
-        acc = mfma4(sAq[(k0 + gq) * CP + 16 * w + xi], sdO[(k0 + gq) * 17 + xi], acc);
-#pragma unroll 8
-      for (int k0 = 0; k0 < K; k0 += 4)
-        acc = mfma4(sKG[(16 * w + xi) * KP + k0 + gq], sdS[(k0 + gq) * 17 + xi], acc);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sdVn[(16 * w + 4 * gq + r) * 17 + xi] = acc[r];
+    };
+    if (nch > 0) {
+      fetch1(nch - 1);
+      fetch2(nch - 1);
+      stage1((nch - 1) & 1);
+      stage2();
+      fetch1(nch - 2);
+      fetch2(nch - 2);
     }
-    __syncthreads();
-    // dS = Diag(gamma) dS' + Qg^T dO - W^T dVn
+    for (int cc = nch - 1; cc >= 0; --cc) {
+      __syncthreads();  // A
+      float rS[NSC];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      const int rt = TPW * w + t;
+      for (int m = 0; m < NSC; ++m) rS[m] = sdS[((lt >> 4) + 16 * m) * 17 + (lt & 15)];
+      __syncthreads();  // B
+      float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dS[t][r] *= sGam[16 * rt + 4 * gq + r];
-#pragma unroll 8
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        dS[t] = mfma4(sQG[(k0 + gq) * KP + 16 * rt + xi], sdO[(k0 + gq) * 17 + xi], dS[t]);
-        dS[t] = mfma4(-sW[(k0 + gq) * KP + 16 * rt + xi], sdVn[(k0 + gq) * 17 + xi], dS[t]);
-      }
+      for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];  // gradient of the chunk-end state
+      if (cc > 0) stage1((cc - 1) & 1);
+      fetch1(cc - 2);
+      __syncthreads();  // C
+      if (cc > 0) stage2();
+      fetch2(cc - 2);
     }
-  }
-  if (a.dh0) {
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * (TPW * w + t) + 4 * gq + r;
-        a.dh0[((size_t)u * K + row) * V + col] = dS[t][r];
-      }
   }
 }
 
@@ -1037,7 +1078,7 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   if (a.nunits > 0) {
     if ((stages & 2) && nitems > 0)
       hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
-    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(kBT), 0, s, a);
+    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
   }
   if ((stages & 8) && nitems > 0) {
     hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
