@@ -590,7 +590,12 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
   constexpr int V = K, KP = K + 4, CP = C + 4, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
   constexpr int NA = C * C / 4 / kBT;
   __shared__ __attribute__((aligned(16))) float sKG[C * KP], sQG[C * KP], sW[C * KP], sAq[C * CP];
-  __shared__ float sdO[2][C * 17], sdVn[C * 17], sdS[K * 17], sGam[2][K];
+  // dO, dVn and dS' transposed (column-major, rows padded by 4): with the
+  // reduction index of 16-deep slice k0 ordered k0 + 4 g + s (lane group g,
+  // MFMA step s), a lane reads its 4 steps' operands as one 16-byte load
+  constexpr int SP = K + 4, VP = C + 4;
+  __shared__ __attribute__((aligned(16))) float sdOT[2][16 * VP], sdVnT[16 * VP], sdST[16 * SP];
+  __shared__ float sGam[2][K];
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -614,37 +619,58 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) {
         const int row = 16 * (TPW * w + t) + 4 * gq + r;
         dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
-        sdS[row * 17 + xi] = dS[t][r];
       }
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+      *reinterpret_cast<floatx4*>(sdST + xi * SP + 16 * (TPW * w + t) + 4 * gq) = dS[t];
     for (int cc = nch - 1; cc >= 0; --cc) {
       const int b = cc & 1;
       __syncthreads();  // A
-      // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS'
-      {
-        floatx4 acc = zero4();
-#pragma unroll 8
-        for (int k0 = 0; k0 < C; k0 += 4)
-          acc = mfma4(sAq[(k0 + gq) * CP + 16 * w + xi], sdO[b][(k0 + gq) * 17 + xi], acc);
-#pragma unroll 8
-        for (int k0 = 0; k0 < K; k0 += 4)
-          acc = mfma4(sKG[(16 * w + xi) * KP + k0 + gq], sdS[(k0 + gq) * 17 + xi], acc);
+      floatx4 Ob[C / 16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sdVn[(16 * w + 4 * gq + r) * 17 + xi] = acc[r];
+      for (int q = 0; q < C / 16; ++q) Ob[q] = *reinterpret_cast<const floatx4*>(&sdOT[b][xi * VP + 16 * q + 4 * gq]);
+      // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS' (one accumulator chain per step s)
+      {
+        floatx4 Ka[K / 16], Sb[K / 16];
+#pragma unroll
+        for (int q = 0; q < K / 16; ++q) {
+          Ka[q] = *reinterpret_cast<const floatx4*>(sKG + (16 * w + xi) * KP + 16 * q + 4 * gq);
+          Sb[q] = *reinterpret_cast<const floatx4*>(sdST + xi * SP + 16 * q + 4 * gq);
+        }
+        floatx4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+        for (int q = 0; q < C / 16; ++q)
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+            acc[st] = mfma4(sAq[(16 * q + 4 * gq + st) * CP + 16 * w + xi], Ob[q][st], acc[st]);
+#pragma unroll
+        for (int q = 0; q < K / 16; ++q)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) acc[st] = mfma4(Ka[q][st], Sb[q][st], acc[st]);
+        const floatx4 dv = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        *reinterpret_cast<floatx4*>(sdVnT + xi * VP + 16 * w + 4 * gq) = dv;
       }
       __syncthreads();  // B
       // dS = Diag(gamma) dS' + Qg^T dO - W^T dVn
+      floatx4 Vb[C / 16];
+#pragma unroll
+      for (int q = 0; q < C / 16; ++q) Vb[q] = *reinterpret_cast<const floatx4*>(sdVnT + xi * VP + 16 * q + 4 * gq);
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int rt = TPW * w + t;
 #pragma unroll
         for (int r = 0; r < 4; ++r) dS[t][r] *= sGam[b][16 * rt + 4 * gq + r];
-#pragma unroll 8
-        for (int k0 = 0; k0 < C; k0 += 4) {
-          dS[t] = mfma4(sQG[(k0 + gq) * KP + 16 * rt + xi], sdO[b][(k0 + gq) * 17 + xi], dS[t]);
-          dS[t] = mfma4(-sW[(k0 + gq) * KP + 16 * rt + xi], sdVn[(k0 + gq) * 17 + xi], dS[t]);
-        }
+        floatx4 acc2 = zero4();
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sdS[(16 * rt + 4 * gq + r) * 17 + xi] = dS[t][r];
+        for (int q = 0; q < C / 16; ++q)
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const int k = 16 * q + 4 * gq + st;
+            dS[t] = mfma4(sQG[k * KP + 16 * rt + xi], Ob[q][st], dS[t]);
+            acc2 = mfma4(-sW[k * KP + 16 * rt + xi], Vb[q][st], acc2);
+          }
+        dS[t] += acc2;
+        *reinterpret_cast<floatx4*>(sdST + xi * SP + 16 * rt + 4 * gq) = dS[t];
       }
       __syncthreads();  // C
     }
@@ -718,7 +744,7 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
         dov[3] = __uint_as_float(rO16[1] & 0xffff0000u);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sdO[b][(lt >> 2) * 17 + 4 * (lt & 3) + c] = rOk ? dov[c] : 0.f;
+      for (int c = 0; c < 4; ++c) sdOT[b][(4 * (lt & 3) + c) * VP + (lt >> 2)] = rOk ? dov[c] : 0.f;
       if (lt < K) sGam[b][lt] = rG;
     };
     auto stage2 = [&]() {
@@ -741,7 +767,7 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       __syncthreads();  // A
       float rS[NSC];
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) rS[m] = sdS[((lt >> 4) + 16 * m) * 17 + (lt & 15)];
+      for (int m = 0; m < NSC; ++m) rS[m] = sdST[(lt & 15) * SP + (lt >> 4) + 16 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
