@@ -692,26 +692,31 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
     // converted when it is staged
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    floatx4 rKG[NF], rA[NA], rQG[NF], rW[NF];
-    u32x4 rO32 = {0u, 0u, 0u, 0u};
-    u32x2 rO16 = {0u, 0u};
-    bool rOk = false;
-    float rG = 0.f;
+    struct G1 {
+      floatx4 kg[NF], aq[NA];
+      u32x4 o32;
+      u32x2 o16;
+      bool ok;
+      float g;
+    };
+    floatx4 rQG[NF], rW[NF];
     // loads are unconditional: the chunk index is clamped to 0
-    auto fetch1 = [&](int cc) {
+    auto fetch1 = [&](G1& r1, int cc) {
       cc = cc > 0 ? cc : 0;
       const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-      for (int m = 0; m < NF; ++m) rKG[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
+      for (int m = 0; m < NF; ++m) r1.kg[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
 #pragma unroll
-      for (int m = 0; m < NA; ++m) rA[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (lt + kBT * m));
+      for (int m = 0; m < NA; ++m) r1.aq[m] = *reinterpret_cast<const floatx4*>(sl + o.aqk + 4 * (lt + kBT * m));
       const ItemB it = chunk_of(a, p0 + cc, h);
       const int r = lt >> 2, c0 = 16 * vb + 4 * (lt & 3);
-      rOk = r < it.len;
-      const size_t at = ((size_t)(it.tok0 + (rOk ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
-      if (qf32) rO32 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.d_o) + at);
-      else rO16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
-      rG = sl[o.gam + (lt < K ? lt : 0)];
+      r1.ok = r < it.len;
+      const size_t at = ((size_t)(it.tok0 + (r1.ok ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
+      r1.o32 = u32x4{0u, 0u, 0u, 0u};
+      r1.o16 = u32x2{0u, 0u};
+      if (qf32) r1.o32 = *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(a.d_o) + at);
+      else r1.o16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
+      r1.g = sl[o.gam + (lt < K ? lt : 0)];
     };
     auto fetch2 = [&](int cc) {
       cc = cc > 0 ? cc : 0;
@@ -722,30 +727,30 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
         rW[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
       }
     };
-    auto stage1 = [&](int b) {
+    auto stage1 = [&](const G1& r1, int b) {
 #pragma unroll
       for (int m = 0; m < NF; ++m) {
         const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
-        *reinterpret_cast<floatx4*>(sKG + r * KP + d) = rKG[m];
+        *reinterpret_cast<floatx4*>(sKG + r * KP + d) = r1.kg[m];
       }
 #pragma unroll
       for (int m = 0; m < NA; ++m) {
         const int e = 4 * (lt + kBT * m);
-        *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = rA[m];
+        *reinterpret_cast<floatx4*>(sAq + (e / C) * CP + e % C) = r1.aq[m];
       }
       float dov[4];
       if (qf32) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) dov[c] = __uint_as_float(rO32[c]);
+        for (int c = 0; c < 4; ++c) dov[c] = __uint_as_float(r1.o32[c]);
       } else {
-        dov[0] = __uint_as_float(rO16[0] << 16);
-        dov[1] = __uint_as_float(rO16[0] & 0xffff0000u);
-        dov[2] = __uint_as_float(rO16[1] << 16);
-        dov[3] = __uint_as_float(rO16[1] & 0xffff0000u);
+        dov[0] = __uint_as_float(r1.o16[0] << 16);
+        dov[1] = __uint_as_float(r1.o16[0] & 0xffff0000u);
+        dov[2] = __uint_as_float(r1.o16[1] << 16);
+        dov[3] = __uint_as_float(r1.o16[1] & 0xffff0000u);
       }
 #pragma unroll
-      for (int c = 0; c < 4; ++c) sdOT[b][(4 * (lt & 3) + c) * VP + (lt >> 2)] = rOk ? dov[c] : 0.f;
-      if (lt < K) sGam[b][lt] = rG;
+      for (int c = 0; c < 4; ++c) sdOT[b][(4 * (lt & 3) + c) * VP + (lt >> 2)] = r1.ok ? dov[c] : 0.f;
+      if (lt < K) sGam[b][lt] = r1.g;
     };
     auto stage2 = [&]() {
 #pragma unroll
@@ -755,15 +760,9 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
         *reinterpret_cast<floatx4*>(sW + r * KP + d) = rW[m];
       }
     };
-    if (nch > 0) {
-      fetch1(nch - 1);
-      fetch2(nch - 1);
-      stage1((nch - 1) & 1);
-      stage2();
-      fetch1(nch - 2);
-      fetch2(nch - 2);
-    }
-    for (int cc = nch - 1; cc >= 0; --cc) {
+    // group 1 has two register sets: set cur holds chunk cc - 1 at step cc and
+    // is refilled with chunk cc - 3 once staged (two chunks of latency)
+    auto step = [&](int cc, G1& cur) {
       __syncthreads();  // A
       float rS[NSC];
 #pragma unroll
@@ -772,11 +771,26 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
       for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];  // gradient of the chunk-end state
-      if (cc > 0) stage1((cc - 1) & 1);
-      fetch1(cc - 2);
+      if (cc > 0) stage1(cur, (cc - 1) & 1);
+      fetch1(cur, cc - 3);
       __syncthreads();  // C
       if (cc > 0) stage2();
       fetch2(cc - 2);
+    };
+    if (nch > 0) {
+      G1 X, Y;  // X: chunks of the parity of nch - 1, Y: the other parity
+      fetch1(X, nch - 1);
+      fetch2(nch - 1);
+      fetch1(Y, nch - 2);
+      stage1(X, (nch - 1) & 1);
+      stage2();
+      fetch1(X, nch - 3);
+      fetch2(nch - 2);
+      // step cc stages chunk cc - 1: from Y when cc = nch - 1, nch - 3, ..., from X otherwise
+      for (int cc = nch - 1; cc >= 0; cc -= 2) {
+        step(cc, Y);
+        if (cc - 1 >= 0) step(cc - 1, X);
+      }
     }
   }
 }
