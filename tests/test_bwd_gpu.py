@@ -81,6 +81,16 @@ def test_bwd_varlen_ragged_fp32():
     check(errs, TOL["fp32"])
 
 
+def test_bwd_varlen_fp32_k128_chunk_counts():
+    """fp32, K=V=128, packed sequences of 5, 6 and 3 chunks (the last one short):
+    the state passes walk odd and even chunk counts, which alternate their
+    operand buffers and register sets."""
+    _say("bwd varlen fp32 K=V=128 lengths [300, 383, 129]")
+    x = core_inputs(1, None, 2, 128, 128, dtype="fp32", seed=38, init_std=0.1, lengths=[300, 383, 129])
+    errs, _ = run_case(x, seed=14)
+    check(errs, TOL["fp32"])
+
+
 def test_bwd_l2norm_unnormalised_inputs():
     """use_qk_l2norm on raw N(0,1) q, k: gradients of the un-normalised inputs."""
     _say("bwd l2norm fp32 B=1 H=2 T=128 K=V=64")
