@@ -31,16 +31,17 @@
 // Every intermediate lives in a per-(chunk, head) fp32 slab of the workspace.
 // prep and the elementwise kernel are latency-bound chains of phases and run
 // 16 waves per workgroup (one workgroup per CU by LDS); the product kernel runs
-// 4 waves with its operand slices double-buffered; the two state passes are
-// bound by their per-chunk chain. Loads are issued before stores throughout: on
-// this GPU a memory-counter wait also waits for every earlier store.
+// 4 waves with its operand slices double-buffered; the two state passes run 8
+// waves, 4 on the per-chunk MFMA chain and 4 that load and stage the chunk
+// operands ahead of it. Loads are issued before stores throughout: on this GPU
+// a memory-counter wait also waits for every earlier store.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
 namespace kda {
 namespace {
 
-constexpr int kBT = 256;  // threads per workgroup
+constexpr int kBT = 256;  // threads per workgroup (the state passes run 2 kBT)
 constexpr int kBW = 1024;  // threads of the per-chunk rebuild and elementwise kernels
 constexpr int kNWW = kBW / 64;
 constexpr int C = kChunk;
