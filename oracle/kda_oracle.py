@@ -37,11 +37,13 @@ Parity status:
   kda_recurrent_vjp        -> pinned (central finite differences of
                               kda_recurrent, the beta = 0 closed form and
                               the varlen / l2norm cases in tests/).
-  kda_layer_ref            -> partly pinned: its convolution is pinned against
-                              numpy.convolve, its norm and gate by their
-                              defining properties, and causality end to end;
-                              the layer as a whole has no printed values to
-                              match ("parity unpinned" for the composition).
+  kda_layer_ref            -> pinned: its steps (conv against numpy.convolve,
+                              RMSNorm by closed forms with eps != 0, the gate
+                              by closed forms) and their composition (a
+                              single-token closed form worked by hand, a
+                              reduced-weight case composed from the pinned
+                              token recurrence, per-head RMS, causality), with
+                              planted mistakes in each step caught in tests/.
 """
 from __future__ import annotations
 
@@ -62,6 +64,11 @@ __all__ = [
     "silu",
     "sigmoid",
     "rms_norm",
+    "short_conv_silu",
+    "qk_features",
+    "head_rms_norm",
+    "output_gate",
+    "decay_gate",
     "gate_activation",
     "kda_recurrent_vjp",
 ]
@@ -453,27 +460,66 @@ def depthwise_causal_conv(x, w):
 
 
 def rms_norm(x, weight, eps):
-    """x / sqrt(mean(x^2) + eps) * weight over the last axis."""
+    """x / sqrt(mean(x^2) + eps) * weight over the last axis (eps inside the root)."""
     x = _f64(x)
     return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f64(weight)
 
 
+def short_conv_silu(p, conv_w):
+    """One feature stream of the layer: causal depthwise conv, then SiLU
+    ([K3] "From the hidden states to causal Q, K, and V": the projection is
+    convolved along time first and the activation follows)."""
+    return silu(depthwise_causal_conv(p, conv_w))
+
+
+def qk_features(p, conv_w, num_heads, head_dim, eps):
+    """q or k of the layer: conv -> SiLU, then split into heads and
+    L2-normalised over the head dimension ([K3] "FP32 core and log-space
+    decay": the normalisation acts on the activated features)."""
+    B, T, _ = p.shape
+    return l2norm(short_conv_silu(p, conv_w).reshape(B, T, num_heads, head_dim), eps)
+
+
+def head_rms_norm(o, weight, eps):
+    """RMSNorm of the core output per (token, head) over the head dimension
+    ([K3] "Returning to the model dimension": the norm is per head, with a
+    weight of length D shared by the heads). o: [B, T, H, D]."""
+    return rms_norm(o, weight, eps)
+
+
+def output_gate(x, Wgd, Wgu, num_heads, head_dim):
+    """Low-rank output gate sigmoid(x Wgd^T Wgu^T), split into heads
+    ([K3] "Returning to the model dimension")."""
+    B, T, _ = x.shape
+    return sigmoid((_f64(x) @ _f64(Wgd).T) @ _f64(Wgu).T).reshape(B, T, num_heads, head_dim)
+
+
+def decay_gate(x, w, num_heads, head_dim, lower_bound):
+    """Log decay of the layer, the lower-bound sigmoid form of [Tokamax]
+    9.1.3: g = a * sigmoid(exp(A_log_h) * (x Wad^T Wau^T + dt_bias))."""
+    B, T, _ = x.shape
+    raw = (_f64(x) @ _f64(w["Wad"]).T) @ _f64(w["Wau"]).T
+    return gate_activation(raw.reshape(B, T, num_heads, head_dim), w["A_log"],
+                           _f64(w["dt_bias"]).reshape(num_heads, head_dim), "lower_bound_sigmoid",
+                           lower_bound)
+
+
 def kda_layer_ref(x, w, num_heads, head_dim, chunk_size=64, gate_lower_bound=-5.0,
-                  norm_eps=1e-6, l2_eps=1e-6):
+                  norm_eps=1e-6, l2_eps=1e-6, heads=None):
     """KDA layer forward with the low-rank output gate, float64.
 
     x: [B, T, M]. `w` maps names to arrays (Linear weights are [out, in]):
       Wqkv [3*H*D, M]; conv_q, conv_k, conv_v [H*D, 4]; Wb [H, M];
       Wad [r, M]; Wau [H*D, r]; A_log [H]; dt_bias [H*D];
       Wgd [D, M]; Wgu [H*D, D]; norm_w [D]; Wo [M, H*D].
-    Steps ([K3]):
-      QKV projection -> per-stream causal depthwise conv -> SiLU ->
-      q, k L2-normalised over D -> beta = sigmoid(x Wb^T) ->
-      log decay g = a * sigmoid(exp(A_log_h) * (x Wad^T Wau^T + dt_bias)),
-      a = gate_lower_bound ([Tokamax] 9.1.3 lower-bound variant) ->
-      chunkwise core with scale D^-1/2 and zero state ->
-      per-head RMSNorm -> * sigmoid(x Wgd^T Wgu^T) -> Wo.
-    Returns (x_new [B, T, M], dict of intermediates).
+    Steps ([K3]), each a function of this module:
+      QKV projection -> short_conv_silu per stream (q and k through
+      qk_features, L2-normalised over D) -> beta = sigmoid(x Wb^T) ->
+      decay_gate -> chunkwise core with scale D^-1/2 and zero state ->
+      head_rms_norm -> * output_gate -> Wo.
+    `heads` restricts the core to a subset of heads (then x_new is not
+    formed and is returned as None; the intermediates carry those heads).
+    Returns (x_new [B, T, M], dict of intermediates q, k, v, g, beta, o).
     """
     x = _f64(x)
     B, T, M = x.shape
@@ -481,18 +527,18 @@ def kda_layer_ref(x, w, num_heads, head_dim, chunk_size=64, gate_lower_bound=-5.
     HD = H * D
     qkv = x @ _f64(w["Wqkv"]).T
     qp, kp, vp = qkv[..., :HD], qkv[..., HD:2 * HD], qkv[..., 2 * HD:]
-    q = silu(depthwise_causal_conv(qp, w["conv_q"])).reshape(B, T, H, D)
-    k = silu(depthwise_causal_conv(kp, w["conv_k"])).reshape(B, T, H, D)
-    v = silu(depthwise_causal_conv(vp, w["conv_v"])).reshape(B, T, H, D)
-    q, k = l2norm(q, l2_eps), l2norm(k, l2_eps)
+    q = qk_features(qp, w["conv_q"], H, D, l2_eps)
+    k = qk_features(kp, w["conv_k"], H, D, l2_eps)
+    v = short_conv_silu(vp, w["conv_v"]).reshape(B, T, H, D)
     beta = sigmoid(x @ _f64(w["Wb"]).T)
-    a = (x @ _f64(w["Wad"]).T) @ _f64(w["Wau"]).T
-    lam = np.exp(_f64(w["A_log"]))                       # [H]
-    pre = (a + _f64(w["dt_bias"])).reshape(B, T, H, D) * lam[None, None, :, None]
-    g = gate_lower_bound * sigmoid(pre)
+    g = decay_gate(x, w, H, D, gate_lower_bound)
+    if heads is not None:
+        hs = list(heads)
+        q, k, v, g, beta = q[:, :, hs], k[:, :, hs], v[:, :, hs], g[:, :, hs], beta[:, :, hs]
     o, _ = kda_chunkwise(q, k, v, g, beta, D ** -0.5, chunk_size)
-    on = rms_norm(o, w["norm_w"], norm_eps)
-    gate = sigmoid((x @ _f64(w["Wgd"]).T) @ _f64(w["Wgu"]).T).reshape(B, T, H, D)
-    y = (on * gate).reshape(B, T, HD)
-    x_new = y @ _f64(w["Wo"]).T
-    return x_new, {"q": q, "k": k, "v": v, "g": g, "beta": beta, "o": o}
+    inter = {"q": q, "k": k, "v": v, "g": g, "beta": beta, "o": o}
+    if heads is not None:
+        return None, inter
+    y = head_rms_norm(o, w["norm_w"], norm_eps) * output_gate(x, w["Wgd"], w["Wgu"], H, D)
+    x_new = y.reshape(B, T, HD) @ _f64(w["Wo"]).T
+    return x_new, inter
