@@ -26,6 +26,7 @@
  *    (the lower bound of the pages; it keeps the rebased operands inside the
  *    fp32 range), beta in [0, 1], cu_seqlens non-decreasing from 0 to T.
  *    Values outside give undefined numbers but never an out-of-bounds access.
+ *    kda_validate_inputs checks them on request (it synchronises).
  *
  * Layouts (row-major, contiguous, token-major like the layer projections):
  *   q, k, g : [B, T, H, K]     v, o : [B, T, H, V]     beta : [B, T, H]
@@ -230,6 +231,41 @@ kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const v
                                 const void* d_o, const float* d_final_state, float* dq, float* dk,
                                 float* dv, float* dg, float* dbeta, float* d_initial_state,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Value preconditions of the fast path, checked on the GPU (Tokamax
+ * "chunk_kda_fwd design doc", section 5.3 "Required Runtime Invariants": the
+ * log decay inside the lower bound [-5, 0] and beta in [0, 1]; section 3.5:
+ * cu_seqlens[0] == 0, non-decreasing, cu_seqlens[num_seqs] == T). The lower
+ * bound matters: below g = -5 the rebased in-chunk key factors leave the fp32
+ * range ("KDA Doesn't Care About the Future", section "What's the catch?").
+ *   p          : as for kda_chunk_fwd (B, T, H, K, g_dtype, beta_dtype and
+ *                num_seqs are used)
+ *   g          : [B, T, H, K] log decay (dtype g_dtype), device
+ *   beta       : [B, T, H] (dtype beta_dtype), device
+ *   cu_seqlens : [num_seqs + 1] int32, device, or NULL when num_seqs == 0
+ *   scratch    : device buffer of >= KDA_VALIDATE_SCRATCH_BYTES, 16-byte
+ *                aligned, owned by the caller (contents overwritten)
+ *   report     : host struct; report->failed is -1 until the check has run
+ * SYNCHRONISES `stream` (it copies the reduction back to the host). Returns
+ * KDA_OK when every precondition holds, KDA_ERR_INVALID_ARG naming the first
+ * failed one (non-finite g, g range, non-finite beta, beta range, cu_seqlens)
+ * in kda_last_error(), or the usual argument / HIP errors. Reads only the
+ * elements of the three inputs; any values, however malformed, are safe. */
+#define KDA_VALIDATE_SCRATCH_BYTES 16384
+typedef struct {
+  float g_min, g_max;          /* over the finite entries of g (+inf / -inf if there are none) */
+  float beta_min, beta_max;    /* over the finite entries of beta */
+  int64_t g_nonfinite;         /* NaN or infinite entries of g */
+  int64_t beta_nonfinite;      /* NaN or infinite entries of beta */
+  int64_t cu_first_bad;        /* -1, or the first index of cu_seqlens that breaks the conditions */
+  int32_t failed;              /* -1: not run (argument error); 0: every precondition holds;
+                                  1: non-finite g, 2: g outside [-5, 0], 3: non-finite beta,
+                                  4: beta outside [0, 1], 5: cu_seqlens (the first that fails) */
+} kda_input_report;
+
+kda_status kda_validate_inputs(const kda_fwd_params* p, const void* g, const void* beta,
+                               const int32_t* cu_seqlens, void* scratch, size_t scratch_bytes,
+                               hipStream_t stream, kda_input_report* report);
 
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status s);

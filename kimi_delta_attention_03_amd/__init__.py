@@ -21,7 +21,7 @@ from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
 __all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
            "KdaLayer", "layer_fwd", "decode_step", "affine_summary", "affine_apply",
-           "chunk_bwd", "KdaBackward"]
+           "chunk_bwd", "KdaBackward", "validate_inputs"]
 
 
 def _torch():
@@ -98,6 +98,40 @@ def _core_params(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
     params = make_params(B, T, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale,
                          chunk_size, use_qk_l2norm, l2norm_eps, num_seqs)
     return params, N
+
+
+def validate_inputs(g, beta, cu_seqlens=None, scratch=None):
+    """Check the fast path's value preconditions on the GPU (kda_validate_inputs):
+    g in [-5, 0], beta in [0, 1] (all finite), cu_seqlens[0] == 0, non-decreasing,
+    cu_seqlens[-1] == T. g: [B, T, H, K], beta: [B, T, H]. Synchronises the
+    current stream. Returns (ok, message, report dict); report["failed"] names
+    the first failed precondition (0: none, 1: non-finite g, 2: g range,
+    3: non-finite beta, 4: beta range, 5: cu_seqlens)."""
+    torch = _torch()
+    lib = _lib.load()
+    if g.dim() != 4 or beta.dim() != 3 or tuple(beta.shape) != tuple(g.shape[:3]):
+        raise KdaValueError(1, "g must be [B, T, H, K] and beta [B, T, H]")
+    for t in (g, beta) + (() if cu_seqlens is None else (cu_seqlens,)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise KdaValueError(1, "g, beta and cu_seqlens must be contiguous GPU tensors")
+    num_seqs = 0
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+            raise KdaValueError(1, "cu_seqlens must be a 1-D int32 tensor with at least 2 entries")
+        num_seqs = cu_seqlens.numel() - 1
+    B, T, H, K = g.shape
+    p = make_params(B, T, H, K, K, _lib.KDA_DTYPE_F32, _dtype_code(g), _dtype_code(beta), 1.0, num_seqs=num_seqs)
+    if scratch is None:
+        scratch = torch.empty(_lib.KDA_VALIDATE_SCRATCH_BYTES, dtype=torch.uint8, device=g.device)
+    rep = _lib.KdaInputReport()
+    st = lib.kda_validate_inputs(ctypes.byref(p), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(scratch),
+                                 scratch.numel(), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream),
+                                 ctypes.byref(rep))
+    if rep.failed < 0:          # an argument error: the check did not run
+        _lib.check(st)
+    msg = lib.kda_last_error().decode(errors="replace")
+    report = {n: getattr(rep, n) for n, _ in _lib.KdaInputReport._fields_}
+    return st == 0, msg, report
 
 
 class KdaForward:

@@ -44,6 +44,16 @@ class KdaWorkspaceInfo(ctypes.Structure):
     ]
 
 
+class KdaInputReport(ctypes.Structure):
+    _fields_ = [("g_min", ctypes.c_float), ("g_max", ctypes.c_float),
+                ("beta_min", ctypes.c_float), ("beta_max", ctypes.c_float),
+                ("g_nonfinite", ctypes.c_int64), ("beta_nonfinite", ctypes.c_int64),
+                ("cu_first_bad", ctypes.c_int64), ("failed", ctypes.c_int32)]
+
+
+KDA_VALIDATE_SCRATCH_BYTES = 16384
+
+
 class KdaGateParams(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("lower_bound", ctypes.c_float),
                 ("A_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p)]
@@ -90,6 +100,8 @@ SIGNATURES = {
                                      _vp, _vp, ctypes.c_size_t, _vp]),
     "kda_chunk_bwd_stages": (ctypes.c_int, [_P, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_validate_inputs": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                           ctypes.POINTER(KdaInputReport)]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }

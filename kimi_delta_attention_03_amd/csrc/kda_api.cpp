@@ -87,15 +87,37 @@ kda_status check_gate(const kda_gate_params* gp) {
   return KDA_OK;
 }
 
-kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
-                      const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream,
-                      const kda_gate_params* gp = nullptr) {
+// Host-only checks of the stage 1+2 inputs. Every entry point runs them (and
+// check_stage34 for its outputs) before its first launch, so that a failed
+// check launches nothing.
+kda_status check_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                         const void* beta, const kda::Layout& L) {
   if (p->T > 0 && p->B > 0) {
     if (!q || !k || !v || !g || !beta) return fail(KDA_ERR_INVALID_ARG, "q, k, v, g and beta must be non-NULL");
     for (const void* t : {q, k, v, g})
       if (!aligned(t, 16)) return fail(KDA_ERR_INVALID_ARG, "q, k, v and g must be 16-byte aligned");
     if (!aligned(beta, 4)) return fail(KDA_ERR_INVALID_ARG, "beta must be 4-byte aligned");
   }
+  if (L.ncp * (size_t)p->H > (size_t)INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "grid too large");
+  return KDA_OK;
+}
+
+// Host-only checks of the stage 3+4 outputs and states; need_o: the call
+// writes o (every forward entry point; not the affine summaries).
+kda_status check_stage34(const kda_fwd_params* p, const void* o, bool need_o, const float* init, const float* fin) {
+  const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
+  if (need_o && p->T > 0 && p->B > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  if (o && !aligned(o, 16)) return fail(KDA_ERR_INVALID_ARG, "o must be 16-byte aligned");
+  if ((init && !aligned(init, 16)) || (fin && !aligned(fin, 16)))
+    return fail(KDA_ERR_INVALID_ARG, "initial_state and final_state must be 16-byte aligned");
+  if (nseq * p->H > INT32_MAX / 16) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
+  return KDA_OK;
+}
+
+// Launches only: the arguments have passed check_common and check_stage12.
+kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                      const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream,
+                      const kda_gate_params* gp = nullptr) {
   char* w = static_cast<char*>(ws);
   const int varlen = p->num_seqs > 0;
   if (varlen) {
@@ -125,12 +147,12 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
   a.off_w = L.off_w; a.off_qg = L.off_qg; a.off_kg = L.off_kg; a.off_aq = L.off_aq; a.off_u = L.off_u;
   a.off_gam = L.off_gam;
   const size_t nblocks = L.ncp * (size_t)p->H;
-  if (nblocks > (size_t)INT32_MAX) return fail(KDA_ERR_UNSUPPORTED, "grid too large");
   hipError_t e = kda::launch_stage12(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, (int)nblocks, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "stage 1+2 launch: %s", hipGetErrorString(e));
   return KDA_OK;
 }
 
+// Launches only: the arguments have passed check_common and check_stage34.
 // build_map: (re)build the variable-length chunk map first. The entry points that
 // run stage 3+4 on its own do, so that a workspace not prepared by stage 1+2 still
 // holds valid tables and every access stays in bounds.
@@ -144,10 +166,6 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
                                           L.off_seq_tab, L.off_order, stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "varlen map launch: %s", hipGetErrorString(e));
   }
-  if (p->T > 0 && !o && !fin) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
-  if (o && !aligned(o, 16)) return fail(KDA_ERR_INVALID_ARG, "o must be 16-byte aligned");
-  if ((init && !aligned(init, 16)) || (fin && !aligned(fin, 16)))
-    return fail(KDA_ERR_INVALID_ARG, "states must be 16-byte aligned");
   kda::Stage34Args a{};
   a.init = init;
   a.final_state = fin;
@@ -155,9 +173,7 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   a.init_identity = affine_linear;
   a.zero_u = affine_linear;
   a.H = (int)p->H;
-  const int64_t nunits = nseq * p->H;
-  if (nunits > INT32_MAX / 16) return fail(KDA_ERR_UNSUPPORTED, "too many (sequence, head) pairs");
-  a.nunits = (int)nunits;
+  a.nunits = (int)(nseq * p->H);
   a.nt = p->num_seqs > 0 ? 0 : (int)(p->T / 64);
   a.varlen = p->num_seqs > 0;
   a.ws = static_cast<const char*>(ws);
@@ -222,6 +238,8 @@ kda_status kda_chunk_fwd_stage12(const kda_fwd_params* p, const void* q, const v
   kda::Layout L;
   kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
   if (s != KDA_OK) return s;
+  s = check_stage12(p, q, k, v, g, beta, L);
+  if (s != KDA_OK) return s;
   return do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream);
 }
 
@@ -230,6 +248,8 @@ kda_status kda_chunk_fwd_stage34(const kda_fwd_params* p, const float* initial_s
                                  hipStream_t stream) {
   kda::Layout L;
   kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
+  if (s != KDA_OK) return s;
+  s = check_stage34(p, o, true, initial_state, final_state);
   if (s != KDA_OK) return s;
   return do_stage34(p, initial_state, o, final_state, workspace, L, stream, 0, true, cu_seqlens);
 }
@@ -240,7 +260,10 @@ kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, 
   kda::Layout L;
   kda_status s = check_common(p, cu_seqlens, workspace, workspace_bytes, &L);
   if (s != KDA_OK) return s;
-  if (p->T > 0 && p->B > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  s = check_stage12(p, q, k, v, g, beta, L);
+  if (s != KDA_OK) return s;
+  s = check_stage34(p, o, true, initial_state, final_state);
+  if (s != KDA_OK) return s;
   s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream);
   if (s != KDA_OK) return s;
   return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
@@ -290,6 +313,7 @@ kda_status kda_chunk_bwd_stages(const kda_fwd_params* p, int32_t stages, const v
                                 const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, float* dq,
                                 float* dk, float* dv, float* dg, float* dbeta, float* d_initial_state,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_msg[0] = 0;
   if (stages < 1 || stages > 15) return fail(KDA_ERR_INVALID_ARG, "stages must be a mask in [1, 15] (got %d)", stages);
   kda_status s = check_params(p);
   if (s != KDA_OK) return s;
@@ -373,7 +397,10 @@ kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* g
   if (s != KDA_OK) return s;
   s = check_gate(gate);
   if (s != KDA_OK) return s;
-  if (p->T > 0 && p->B > 0 && !o) return fail(KDA_ERR_INVALID_ARG, "o must be non-NULL");
+  s = check_stage12(p, q, k, v, g, beta, L);
+  if (s != KDA_OK) return s;
+  s = check_stage34(p, o, true, initial_state, final_state);
+  if (s != KDA_OK) return s;
   s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream, gate);
   if (s != KDA_OK) return s;
   return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
@@ -386,6 +413,9 @@ kda_status kda_chunk_affine_summary(const kda_fwd_params* p, const int32_t* cu_s
   if (s != KDA_OK) return s;
   if (!M || !N) return fail(KDA_ERR_INVALID_ARG, "M and N must be non-NULL");
   if (!aligned(M, 16) || !aligned(N, 16)) return fail(KDA_ERR_INVALID_ARG, "M and N must be 16-byte aligned");
+  if (M == N) return fail(KDA_ERR_INVALID_ARG, "M and N must not alias");
+  s = check_stage34(p, nullptr, false, nullptr, N);
+  if (s != KDA_OK) return s;
   // N: the state reached from a zero start; M: the recurrence run on an identity
   // start with U taken as zero (the linear part). No output is written.
   s = do_stage34(p, nullptr, nullptr, N, workspace, L, stream, 0, true, cu_seqlens);

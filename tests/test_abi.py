@@ -244,3 +244,114 @@ def test_backward_rejects_before_launch(lib):
     pv = P(num_seqs=2, T=100)                      # varlen without cu_seqlens
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(pv), ctypes.byref(n)) == 0
     assert lib.kda_chunk_bwd(ctypes.byref(pv), *ins, *outs, fake, n.value, null) == 1
+
+
+# ------------------------------------------- output / state checks before any launch
+# These pass fake device addresses: they run only where no GPU is visible, so that
+# an address can never reach a device even if a check were missing (on a machine
+# without a GPU a launch fails with KDA_ERR_HIP, so status 1 also shows that the
+# check ran before the first launch).
+
+def _gpu_visible():
+    import torch
+    return torch.cuda.is_available()
+
+
+no_gpu = pytest.mark.skipif(_gpu_visible(), reason="fake device addresses must never reach a real device")
+
+
+@no_gpu
+@pytest.mark.parametrize("which", ["o", "initial_state", "final_state"])
+@pytest.mark.parametrize("entry", ["fwd", "gated", "stage34", "stage34_varlen"])
+def test_misaligned_output_or_state_rejected_before_launch(lib, which, entry):
+    """kda_chunk_fwd, kda_chunk_fwd_gated and kda_chunk_fwd_stage34 with aligned
+    inputs and one misaligned o, initial_state or final_state: KDA_ERR_INVALID_ARG,
+    nothing launched (the varlen stage 3+4 used to launch its chunk map first)."""
+    p = P(num_seqs=2, T=100) if entry == "stage34_varlen" else P()
+    _, n = ws_bytes(lib, p)
+    ok = ctypes.c_void_p(1 << 24)
+    mis = ctypes.c_void_p((1 << 24) + 8)          # 8-byte aligned, not 16
+    ws = ctypes.c_void_p(1 << 30)
+    o, h0, hf = ok, ok, ok
+    if which == "o":
+        o = mis
+    elif which == "initial_state":
+        h0 = mis
+    else:
+        hf = mis
+    cu = ok if entry == "stage34_varlen" else None
+    if entry == "fwd":
+        st = lib.kda_chunk_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, h0, None, o, hf, ws, n, None)
+    elif entry == "gated":
+        st = lib.kda_chunk_fwd_gated(ctypes.byref(p), None, ok, ok, ok, ok, ok, h0, None, o, hf, ws, n, None)
+    else:
+        st = lib.kda_chunk_fwd_stage34(ctypes.byref(p), h0, cu, o, hf, ws, n, None)
+    assert st == 1, lib.kda_last_error()
+    assert b"aligned" in lib.kda_last_error()
+
+
+@no_gpu
+def test_forward_needs_o_before_launch(lib):
+    p = P()
+    _, n = ws_bytes(lib, p)
+    ok = ctypes.c_void_p(1 << 24)
+    st = lib.kda_chunk_fwd(ctypes.byref(p), ok, ok, ok, ok, ok, None, None, None, None, ctypes.c_void_p(1 << 30), n,
+                           None)
+    assert st == 1 and b"o must be non-NULL" in lib.kda_last_error()
+
+
+@no_gpu
+def test_affine_summary_rejects_aliased_outputs(lib):
+    p = P()
+    _, n = ws_bytes(lib, p)
+    m = ctypes.c_void_p(1 << 24)
+    assert lib.kda_chunk_affine_summary(ctypes.byref(p), None, m, m, ctypes.c_void_p(1 << 30), n, None) == 1
+    assert b"alias" in lib.kda_last_error()
+
+
+def test_backward_stage_mask_message(lib):
+    """A bad stage mask is reported with its own message, not a stale one."""
+    lib.kda_chunk_fwd_workspace_bytes(None, None)            # leaves "params is NULL"
+    p = P()
+    args = [None] * 15
+    assert lib.kda_chunk_bwd_stages(ctypes.byref(p), 0, *args, None, 0, None) == 1
+    assert b"stages" in lib.kda_last_error()
+
+
+# ------------------------------------------------------------- kda_validate_inputs
+
+def _report():
+    return _lib.KdaInputReport()
+
+
+def test_validate_rejects_bad_arguments_before_launch(lib):
+    """Argument errors are reported without a launch; report.failed stays -1."""
+    vp = ctypes.c_void_p(1 << 24)
+    p = P()
+    r = _report()
+    assert lib.kda_validate_inputs(ctypes.byref(p), vp, vp, None, vp, 16384, None, None) == 1
+    assert lib.kda_validate_inputs(ctypes.byref(p), vp, vp, None, None, 16384, None, ctypes.byref(r)) == 3
+    assert r.failed == -1
+    assert lib.kda_validate_inputs(ctypes.byref(p), vp, vp, None, vp, 1024, None, ctypes.byref(r)) == 3
+    assert b"scratch" in lib.kda_last_error()
+    odd = ctypes.c_void_p((1 << 24) + 1)
+    assert lib.kda_validate_inputs(ctypes.byref(p), odd, vp, None, vp, 16384, None, ctypes.byref(r)) == 1
+    assert b"aligned" in lib.kda_last_error() and r.failed == -1
+    assert lib.kda_validate_inputs(ctypes.byref(p), vp, vp, vp, vp, 16384, None, ctypes.byref(r)) == 1
+    assert b"num_seqs == 0" in lib.kda_last_error()
+    pv = P(num_seqs=3, T=100)
+    assert lib.kda_validate_inputs(ctypes.byref(pv), vp, vp, None, vp, 16384, None, ctypes.byref(r)) == 1
+    assert b"needs cu_seqlens" in lib.kda_last_error()
+    assert lib.kda_validate_inputs(ctypes.byref(P()), None, None, None, vp, 16384, None, ctypes.byref(r)) == 1
+
+
+def test_validate_report_layout_matches_header():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    body = text[:text.index("} kda_input_report;")]
+    body = body[body.rindex("typedef struct {") + len("typedef struct {"):]
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    names = re.findall(r"(\w+)\s*[,;]", body)
+    assert names == [n for n, _ in _lib.KdaInputReport._fields_]
+    assert ctypes.sizeof(_lib.KdaInputReport) == 48
+    assert int(re.search(r"#define KDA_VALIDATE_SCRATCH_BYTES (\d+)", text).group(1)) == \
+        _lib.KDA_VALIDATE_SCRATCH_BYTES
