@@ -72,6 +72,19 @@ typedef struct {
 /* Device workspace bytes kda_layer_fwd needs (pure host computation). */
 kda_status kda_layer_fwd_workspace_bytes(const kda_layer_params* p, size_t* bytes);
 
+/* Where kda_layer_fwd leaves the core's fp32 inputs in its workspace (byte
+ * offsets): q, k, v [B, T, H, D] (after conv, SiLU and, for q and k, the L2
+ * norm), the raw decay gate x Wad^T Wau^T [B, T, H, D] (before dt_bias and the
+ * activation, which run inside the core), beta [B, T, H], and the core output
+ * o [B, T, H, D] (used when core_out is NULL). They hold the last call's
+ * values until the workspace is reused. Pure host computation. */
+typedef struct {
+  size_t total_bytes;
+  size_t off_q, off_k, off_v, off_g_raw, off_beta, off_o;
+} kda_layer_workspace_info;
+
+kda_status kda_layer_workspace_layout(const kda_layer_params* p, kda_layer_workspace_info* info);
+
 /* x: bf16 [B, T, M]; x_new: bf16 [B, T, M] (must not alias x).
  * If core_out is not NULL it receives the fp32 core output o [B, T, H, D]
  * (before the norm), for inspection. */

@@ -398,6 +398,28 @@ class KdaLayer:
         self.cw = _lib.KdaLayerWeights(*[t.data_ptr() for t in (weights[n] for n in _lib.LAYER_WEIGHT_NAMES)])
         self._lib = lib
 
+    def core_inputs(self):
+        """Views into the workspace of the last call's fp32 core inputs and
+        output (kda_layer_workspace_layout): q, k, v [B, T, H, D], the raw
+        decay gate g_raw [B, T, H, D] (before dt_bias and the activation),
+        beta [B, T, H] and the core output o [B, T, H, D] (when no core_out)."""
+        torch = _torch()
+        p = self.params
+        info = _lib.KdaLayerWorkspaceInfo()
+        _lib.check(self._lib.kda_layer_workspace_layout(ctypes.byref(p), ctypes.byref(info)))
+        B, T, H, D = p.B, p.T, p.H, p.D
+
+        def view(off, shape):
+            n = 1
+            for d in shape:
+                n *= d
+            return self.workspace[off:off + 4 * n].view(torch.float32).view(shape)
+
+        full = (B, T, H, D)
+        return {"q": view(info.off_q, full), "k": view(info.off_k, full), "v": view(info.off_v, full),
+                "g_raw": view(info.off_g_raw, full), "beta": view(info.off_beta, (B, T, H)),
+                "o": self.core_out if self.core_out is not None else view(info.off_o, full)}
+
     def __call__(self, x):
         torch = _torch()
         p = self.params

@@ -71,6 +71,11 @@ class KdaLayerParams(ctypes.Structure):
     ]
 
 
+class KdaLayerWorkspaceInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in ("total_bytes", "off_q", "off_k", "off_v", "off_g_raw", "off_beta",
+                                               "off_o")]
+
+
 LAYER_WEIGHT_NAMES = ["Wqkv", "conv_q", "conv_k", "conv_v", "Wb", "Wad", "Wau", "A_log", "dt_bias",
                       "Wgd", "Wgu", "norm_w", "Wo"]
 
@@ -103,6 +108,7 @@ SIGNATURES = {
     "kda_validate_inputs": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
                                            ctypes.POINTER(KdaInputReport)]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
+    "kda_layer_workspace_layout": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWorkspaceInfo)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }
 

@@ -13,8 +13,8 @@
 //   5. core: the two-kernel chunkwise forward on fp32 q, k, v, beta with the
 //      decay g = lb * sigmoid(exp(A_log_h) (g_raw + dt_bias)) applied inside
 //      stage 1+2 (no separate pass over g)
-//   6. Gu   = P_g Wgu^T                    rocBLAS -> fp32 [BT, HD] (in k's space)
-//   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in q's space)
+//   6. Gu   = P_g Wgu^T                    rocBLAS -> fp32 [BT, HD]
+//   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in P's space)
 //   8. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
 // The plain projections are library GEMMs; every other step is a kernel of
 // this file or of the core. The elementwise kernels are HBM-bound: each reads
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kLayerThreads) void layer_norm_gate_kernel(const fl
 struct LayerLayout {
   int64_t BT;
   int HD, NP;
-  size_t off_wcat, off_P, off_q, off_k, off_v, off_g, off_beta, off_o, off_core, total;
+  size_t off_wcat, off_P, off_q, off_k, off_v, off_g, off_beta, off_o, off_gu, off_core, total;
   size_t core_bytes;
 };
 
@@ -216,12 +216,15 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
   auto take = [&](size_t bytes) { const size_t o = off; off = up256(off + bytes); return o; };
   L->off_wcat = take((size_t)L->NP * p->M * 2);
   L->off_P = take(BT * L->NP * 2);        // bf16
-  L->off_q = take(BT * HD * 4);           // later y (bf16)
-  L->off_k = take(BT * HD * 4);           // later the output-gate projection [BT, HD] fp32
+  // q, k, v, the raw gate and beta are the core's inputs; nothing later overwrites
+  // them, so they can be inspected after the call (kda_layer_workspace_layout)
+  L->off_q = take(BT * HD * 4);
+  L->off_k = take(BT * HD * 4);
   L->off_v = take(BT * HD * 4);
   L->off_g = take(BT * HD * 4);
   L->off_beta = take(BT * p->H * 4);
   L->off_o = take(BT * HD * 4);
+  L->off_gu = take(BT * HD * 4);          // output-gate projection [BT, HD] fp32
   L->off_core = take(cb);
   L->total = off;
   return KDA_OK;
@@ -269,6 +272,21 @@ kda_status kda_layer_fwd_workspace_bytes(const kda_layer_params* p, size_t* byte
   if (s != KDA_OK) return s;
   if (!bytes) return kda::fail_msg(KDA_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = L.total;
+  return KDA_OK;
+}
+
+kda_status kda_layer_workspace_layout(const kda_layer_params* p, kda_layer_workspace_info* info) {
+  kda::LayerLayout L;
+  kda_status s = kda::check_layer(p, &L);
+  if (s != KDA_OK) return s;
+  if (!info) return kda::fail_msg(KDA_ERR_INVALID_ARG, "info is NULL");
+  info->total_bytes = L.total;
+  info->off_q = L.off_q;
+  info->off_k = L.off_k;
+  info->off_v = L.off_v;
+  info->off_g_raw = L.off_g;
+  info->off_beta = L.off_beta;
+  info->off_o = L.off_o;
   return KDA_OK;
 }
 
@@ -359,12 +377,12 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
                             stream);
     if (s != KDA_OK) return s;
   }
-  // 6. output-gate up projection into k's space (k is dead after the core),
-  // 7. RMSNorm * gate -> y (bf16, in q's space)
-  float* gu = k;
+  // 6. output-gate up projection,
+  // 7. RMSNorm * gate -> y (bf16, in P's space: P is dead once both up projections have read it)
+  float* gu = reinterpret_cast<float*>(ws + L.off_gu);
   s = gemm_nt(hb, w->Wgu, rg, P + off_r + r, NP, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
   if (s != KDA_OK) return s;
-  uint16_t* y = reinterpret_cast<uint16_t*>(q);
+  uint16_t* y = P;
   {
     const int64_t nw = (int64_t)BT * H;
     const int wpb = kLayerThreads / kWave;

@@ -3,9 +3,11 @@ layer oracle, through the C ABI.
 
 Metric: max|gpu - oracle| / max|oracle| per tensor. The layer output x_new is
 bf16 and is held to 2e-2, the bound used for bf16 outputs throughout the parity
-tests; the fp32 core output o (before the norm) is held to the same bound,
-since its inputs come from bf16-operand projections and bf16-rounded low-rank
-gate activations.
+tests; the fp32 core output o (before the norm) is held to the same bound when
+the oracle runs the whole layer, since its inputs then come from bf16-operand
+projections and bf16-rounded activations on the GPU side only. The fp32 core
+itself is held to 1e-4 on the GPU's own core inputs (read back from the layer's
+workspace), which isolates it from the projections' rounding.
 """
 import sys
 
@@ -75,23 +77,46 @@ def test_layer_deterministic_and_causal():
     assert not torch.equal(y1[:, n + 1:], y3[:, n + 1:])
 
 
-def test_layer_workload4_full_size_prefix():
-    """Workload 4 at full size (B=4, T=8192, M=2048, H=16, D=128, rank 128): the
-    whole batch runs on the GPU; the oracle, which is causal, recomputes the
-    first 256 tokens of batch rows 0 and 3 and they must agree."""
+@pytest.fixture(scope="module")
+def workload4():
+    """Workload 4 at full size (B=4, T=8192, M=2048, H=16, D=128, rank 128): one GPU
+    run of the whole layer; x_new, the fp32 core output and the core's own fp32
+    inputs (left in the workspace) are copied to the host."""
     _say("layer workload 4: generating inputs")
     x, w = layer_inputs()
-    B, T, M = x.shape
     H, D = 16, 128
     _say("layer workload 4: GPU run")
     layer, y = run_layer(x, w, H, D)
-    yh = host(y)
-    oh = host(layer.core_out)
-    assert np.isfinite(yh).all() and np.isfinite(oh).all()
-    n = 256
-    for b in (0, 3):
-        ref, inter = orc.kda_layer_ref(x[b:b + 1, :n], w, H, D)
-        eo = rel_err(oh[b:b + 1, :n], inter["o"])
-        ey = rel_err(yh[b:b + 1, :n], ref)
-        _say(f"  batch row {b}, first {n} tokens: rel err core o={eo:.2e} x_new={ey:.2e}")
-        assert eo <= TOL_LAYER and ey <= TOL_LAYER
+    ci = layer.core_inputs()
+    got = {"x_new": host(y), "o": host(layer.core_out)}
+    for n in ("q", "k", "v", "g_raw", "beta"):
+        got[n] = host(ci[n])
+    return x, w, H, D, got
+
+
+def test_layer_workload4_core_fp32_own_inputs(workload4):
+    """The fp32 core of the layer at its stated tolerance (1e-4): oracle C run on
+    the GPU's own fp32 core inputs (q, k, v, beta, and the decay from the GPU's raw
+    gate through the oracle's gate activation), two heads of batch row 1 over all
+    8192 tokens (128 chunks), against the GPU's core output."""
+    x, w, H, D, got = workload4
+    b, heads = 1, [3, 12]
+    sl = lambda a: a[b:b + 1][:, :, heads]
+    g = orc.gate_activation(sl(got["g_raw"]), np.asarray(w["A_log"])[heads],
+                            np.asarray(w["dt_bias"]).reshape(H, D)[heads], "lower_bound_sigmoid", -5.0)
+    o_ref, _ = orc.kda_chunkwise(sl(got["q"]), sl(got["k"]), sl(got["v"]), g, sl(got["beta"]), D ** -0.5, 64)
+    err = rel_err(sl(got["o"]), o_ref)
+    _say(f"  core o (row {b}, heads {heads}, 8192 tokens) on the GPU's own inputs: rel err {err:.2e}")
+    assert err <= 1e-4
+
+
+@pytest.mark.parametrize("b", [0, 1, 2, 3])
+def test_layer_workload4_full_row(workload4, b):
+    """x_new and the core output of one whole batch row (8192 tokens, every head)
+    against the float64 layer oracle at the bf16 output tolerance."""
+    x, w, H, D, got = workload4
+    ref, inter = orc.kda_layer_ref(x[b:b + 1], w, H, D)
+    eo = rel_err(got["o"][b:b + 1], inter["o"])
+    ey = rel_err(got["x_new"][b:b + 1], ref)
+    _say(f"  batch row {b}, all 8192 tokens: rel err core o={eo:.2e} x_new={ey:.2e}")
+    assert eo <= TOL_LAYER and ey <= TOL_LAYER
