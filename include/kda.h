@@ -267,6 +267,23 @@ kda_status kda_validate_inputs(const kda_fwd_params* p, const void* g, const voi
                                const int32_t* cu_seqlens, void* scratch, size_t scratch_bytes,
                                hipStream_t stream, kda_input_report* report);
 
+/* kda_chunk_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same forward, with the workspace taken from a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. Arguments, results, stream and error rules as
+ * kda_chunk_fwd, without the workspace arguments. Problems whose
+ * kda_chunk_fwd_workspace_bytes exceeds KDA_NOALLOC_SCRATCH_BYTES return
+ * KDA_ERR_WORKSPACE (128 MiB holds e.g. 1850 bf16 chunk-heads at K = V = 128,
+ * 118k token-heads). Nothing is allocated or freed. Every call on one GPU uses
+ * that GPU's single array: calls that overlap on one GPU (several streams or
+ * threads) race and must be serialised by the caller. */
+#define KDA_NOALLOC_SCRATCH_BYTES (128u << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_fwd_params* p, const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta, const float* initial_state,
+                                 const int32_t* cu_seqlens, void* o, float* final_state,
+                                 hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* kda_status_string(kda_status s);
 

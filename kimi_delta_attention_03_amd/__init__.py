@@ -21,7 +21,7 @@ from ._lib import KdaError, KdaValueError, KdaFwdParams, KdaWorkspaceInfo
 
 __all__ = ["chunk_fwd", "KdaForward", "KdaError", "KdaValueError", "make_params", "workspace_layout",
            "KdaLayer", "layer_fwd", "decode_step", "affine_summary", "affine_apply",
-           "chunk_bwd", "KdaBackward", "validate_inputs"]
+           "chunk_bwd", "KdaBackward", "validate_inputs", "chunk_fwd_noalloc"]
 
 
 def _torch():
@@ -98,6 +98,23 @@ def _core_params(q, k, v, g, beta, scale, chunk_size, initial_state, cu_seqlens,
     params = make_params(B, T, H, K, V, _dtype_code(q), _dtype_code(g), _dtype_code(beta), scale,
                          chunk_size, use_qk_l2norm, l2norm_eps, num_seqs)
     return params, N
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, scale=None, initial_state=None, cu_seqlens=None, out=None,
+                      final_state=None, use_qk_l2norm=False, l2norm_eps=1e-6):
+    """kda_chunk_fwd_noalloc: the forward with the library's static device
+    workspace (no workspace allocation; the problem must fit
+    KDA_NOALLOC_SCRATCH_BYTES). `out` and `final_state` may be preallocated
+    (final_state None: not written). Returns (o, final_state)."""
+    torch = _torch()
+    lib = _lib.load()
+    params, N = _core_params(q, k, v, g, beta, scale, 64, initial_state, cu_seqlens, use_qk_l2norm, l2norm_eps)
+    B, T, H, K = q.shape
+    o = out if out is not None else torch.empty((B, T, H, v.shape[3]), dtype=q.dtype, device=q.device)
+    _lib.check(lib.kda_chunk_fwd_noalloc(
+        ctypes.byref(params), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), _ptr(o), _ptr(final_state), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)))
+    return o, final_state
 
 
 def validate_inputs(g, beta, cu_seqlens=None, scratch=None):

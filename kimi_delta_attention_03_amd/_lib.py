@@ -52,6 +52,7 @@ class KdaInputReport(ctypes.Structure):
 
 
 KDA_VALIDATE_SCRATCH_BYTES = 16384
+KDA_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class KdaGateParams(ctypes.Structure):
@@ -105,6 +106,7 @@ SIGNATURES = {
                                      _vp, _vp, ctypes.c_size_t, _vp]),
     "kda_chunk_bwd_stages": (ctypes.c_int, [_P, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                             _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
+    "kda_chunk_fwd_noalloc": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "kda_validate_inputs": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
                                            ctypes.POINTER(KdaInputReport)]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
