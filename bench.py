@@ -89,6 +89,53 @@ def time_loop(fn, reps, torch):
     return s.elapsed_time(e) / reps
 
 
+def host_info():
+    """CPU model, usable cores and the BLAS numpy calls (for the CPU baseline record)."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = f"{b.get('name')} {b.get('version')}".strip()
+    except Exception:
+        pass
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    return {"cpu_model": model, "usable_cores": len(os.sched_getaffinity(0)), "blas": blas, "blas_threads": threads}
+
+
+def build_info():
+    """Provenance of the loaded library (written next to it at build time)."""
+    p = os.path.join(ROOT, "kimi_delta_attention_03_amd", "_build_info.json")
+    try:
+        return json.load(open(p))
+    except (OSError, ValueError):
+        return None
+
+
+def copy_rate(torch, nbytes=1 << 30, reps=5):
+    """Measured device-to-device copy rate (read + write bytes per second)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    ms = time_loop(lambda: dst.copy_(src), reps, torch)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms / 1e3)
+
+
 def cpu_baseline(x, target_s=15.0):
     """Time the float64 chunkwise oracle on a bounded sample of the workload."""
     import oracle.kda_oracle as orc
@@ -111,11 +158,13 @@ def cpu_baseline(x, target_s=15.0):
         tok = max(64, tok // 64 * 64)
     token_heads = tok * len(heads)
     tps = token_heads / wall / H       # tokens/s of the full-H workload
+    hi = host_info()
     return {
-        "value": tps, "unit": "tokens/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "value": tps, "unit": "tokens/s", "cores": hi["blas_threads"] or hi["usable_cores"], "kind": "oracle",
         "sample": f"float64 chunkwise oracle on heads {heads} of {H}, first {tok} of {T} tokens "
-                  f"({token_heads} token-heads, {wall:.1f} s wall, {cpu:.1f} s CPU); tokens/s scaled "
-                  f"to all {H} heads; host has {len(os.sched_getaffinity(0))} usable cores",
+                  f"({token_heads} token-heads, {wall:.1f} s wall, {cpu:.1f} s CPU, "
+                  f"{cpu / wall:.1f} cores busy on average); tokens/s scaled to all {H} heads",
+        **hi,
     }
 
 
@@ -321,11 +370,14 @@ def cpu_baseline_bwd(x, d_o, d_f, target_s=10.0):
         if wall * 2 >= target_s or tok * 2 > T:
             break
         tok = min(T, tok * max(2, int(target_s / max(wall, 1e-3) / 2)))
+    hi = host_info()
+    import torch
     return {
-        "value": tok / wall / H, "unit": "tokens/s", "cores": round(cpu / wall, 2), "kind": "oracle",
+        "value": tok / wall / H, "unit": "tokens/s", "cores": torch.get_num_threads(), "kind": "oracle",
         "sample": f"float64 backward oracle (torch autograd over the token recurrence) on head 0 of {H}, "
-                  f"first {tok} of {T} tokens ({wall:.1f} s wall, {cpu:.1f} s CPU); tokens/s scaled to all "
-                  f"{H} heads; host has {len(os.sched_getaffinity(0))} usable cores",
+                  f"first {tok} of {T} tokens ({wall:.1f} s wall, {cpu:.1f} s CPU, {cpu / wall:.1f} cores busy "
+                  f"on average); tokens/s scaled to all {H} heads",
+        **hi,
     }
 
 
@@ -425,9 +477,43 @@ def main():
     torch.cuda.synchronize()
     ms_step = time_loop(fwd, args.steps, torch)
 
-    # per-kernel durations on the launch stream
-    ms12 = time_loop(fwd.stage12, args.kernel_reps, torch)
-    ms34 = time_loop(fwd.stage34, args.kernel_reps, torch)
+    # per-kernel durations on the launch stream. kda_chunk_fwd runs long
+    # fixed-length inputs in segments along T (stage 1+2 then stage 3+4 of each
+    # segment, the state handed over in fp32); the same launches are replayed
+    # here segment by segment (B = 1: each segment is a contiguous view) with
+    # HIP events around each, giving the average duration of one launch.
+    info = kda.workspace_layout(fwd.params)
+    nseg = int(info.segments)
+    if nseg > 1 and B == 1:
+        ts = int(info.segment_chunks) * 64
+        seg_calls, states = [], [init] + [torch.empty((1, H, K, V), dtype=torch.float32, device=dev)
+                                          for _ in range(nseg)]
+        seg_ws = None
+        for i in range(nseg):
+            sl = slice(i * ts, min(T, (i + 1) * ts))
+            c = kda.KdaForward(q[:, sl], k[:, sl], v[:, sl], g[:, sl], beta[:, sl], scale=x.scale,
+                               initial_state=states[i], out=fwd.o[:, sl], workspace=seg_ws)
+            c.final_state = states[i + 1]
+            seg_ws = c.workspace
+            seg_calls.append(c)
+        t12 = t34 = 0.0
+        reps = max(1, args.kernel_reps)
+        for _ in range(reps):
+            for c in seg_calls:
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                e0.record(); c.stage12(); e1.record(); c.stage34(); e2.record()
+                torch.cuda.synchronize()
+                t12 += e0.elapsed_time(e1)
+                t34 += e1.elapsed_time(e2)
+        ms12, ms34 = t12 / (reps * nseg), t34 / (reps * nseg)     # per launch
+        launches = nseg
+        seg_token_heads = [min(T, (i + 1) * ts) - i * ts for i in range(nseg)]
+        del seg_calls, states
+    else:
+        ms12 = time_loop(fwd.stage12, args.kernel_reps, torch)
+        ms34 = time_loop(fwd.stage34, args.kernel_reps, torch)
+        launches = 1
+        seg_token_heads = [T]
 
     tokens = B * T
     token_heads = tokens * H
@@ -442,11 +528,21 @@ def main():
     peak_mma = PEAK_BF16 if x.dtype == "bf16" else PEAK_FP32
     s_step = ms_step / 1e3
     dom = "stage12" if ms12 >= ms34 else "stage34"
-    dom_bytes = (b12 if dom == "stage12" else b34) * token_heads
+    # algorithmic bytes of one launch (the average segment)
+    dom_bytes = (b12 if dom == "stage12" else b34) * token_heads / launches
     dom_ms = ms12 if dom == "stage12" else ms34
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
 
     cfg = WORKLOADS[args.workload]
+    copy_Bps = copy_rate(torch)
+    if cu is not None:
+        lens = np.diff(x.cu_seqlens).astype(np.int64)
+        seg = {"num_seqs": int(len(lens)), "min": int(lens.min()), "median": float(np.median(lens)),
+               "max": int(lens.max()), "mean": float(lens.mean())}
+        aligned = int(sum(-(-int(L) // 64) * 64 for L in lens))
+    else:
+        seg = None
+        aligned = tokens
     result = {
         "metric": METRIC,
         "value": tokens / s_step,
@@ -466,16 +562,25 @@ def main():
         "mfma_frac": flops / s_step / peak_mma,
         "hbm_alg_GBps": bytes_total / s_step / 1e9,
         "hbm_alg_frac": bytes_total / s_step / PEAK_HBM,
-        "kernels_ms": {"stage12": ms12, "stage34": ms34},
+        "kernels_ms": {"stage12": ms12, "stage34": ms34, "launches_per_step": launches,
+                       "per": "one launch (one segment along T)" if launches > 1 else "one launch"},
+        "hbm_alg_frac_of_copy": bytes_total / s_step / copy_Bps,
+        "copy_GBps_measured": copy_Bps / 1e9,
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM / 1e9,
                      "unit": "GB/s", "frac": achieved * 1e9 / PEAK_HBM,
                      "traffic": measured_traffic(cfg["name"], dom),
-                     "alg_bytes_per_launch": dom_bytes},
-        "record": {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+                     "alg_bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
+        "record": {"library": build_info(),
+                   "tokens_logical": tokens, "tokens_chunk_aligned": aligned, "segments": seg,
+                   "flags": {"use_qk_l2norm": False, "gate": "log_decay (g given)",
+                             "initial_state": init is not None, "final_state": True, "chunk_size": 64},
+                   "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
                    "device": torch.cuda.get_device_name(0),
                    "cus": torch.cuda.get_device_properties(0).multi_processor_count,
                    "sync": "torch.cuda.synchronize + HIP events on the launch stream",
-                   "timed": "kernel launches only (inputs resident, workspace preallocated)",
+                   "timed": "end to end per step: one kda_chunk_fwd call (chunk map if varlen, stage 1+2, "
+                            "stage 3+4) per step, inputs resident, workspace preallocated; kernels_ms times "
+                            "each stage alone",
                    "input_gen_s": round(t_gen, 1)},
     }
     if not args.no_cpu_baseline:

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum { KDA_DTYPE_F32 = 0, KDA_DTYPE_BF16 = 1 } kda_dtype;
 
@@ -157,6 +157,9 @@ typedef struct {
   size_t off_chunk_table;  /* varlen: int32 pairs (first token, valid length) per chunk slot */
   size_t off_seq_table;    /* varlen: int32 pairs (first chunk slot, chunk count) per sequence */
   size_t off_order;        /* varlen: sequences ordered longest first */
+  int32_t segments;        /* kda_chunk_fwd runs fixed-length inputs in this many segments along T */
+  int32_t segment_chunks;  /* chunks per row in each segment (the last may be shorter); the records
+                              of one segment fill the chunk slots from 0 */
 } kda_workspace_info;
 
 kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* info);

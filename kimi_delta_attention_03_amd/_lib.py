@@ -41,6 +41,7 @@ class KdaWorkspaceInfo(ctypes.Structure):
         ("elem_bytes", ctypes.c_int32),
         ("off_chunk_table", ctypes.c_size_t), ("off_seq_table", ctypes.c_size_t),
         ("off_order", ctypes.c_size_t),
+        ("segments", ctypes.c_int32), ("segment_chunks", ctypes.c_int32),
     ]
 
 

@@ -57,6 +57,36 @@ def _compile(src: str) -> str:
     return obj
 
 
+def _write_build_info():
+    """Record which sources the library was built from (commit, dirty flag, source hash)
+    next to it, so that measurements made from a copy of the tree without git can
+    name their provenance."""
+    import hashlib
+    import json
+    import time
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        h.update(name.encode())
+        h.update(open(os.path.join(CSRC, name), "rb").read())
+    for name in sorted(os.listdir(INCLUDE)):
+        h.update(open(os.path.join(INCLUDE, name), "rb").read())
+    commit, dirty = None, None
+    try:
+        root = os.path.dirname(HERE)
+        r = subprocess.run(["git", "-C", root, "rev-parse", "--short=12", "HEAD"], capture_output=True, text=True,
+                           timeout=10)
+        commit = r.stdout.strip() or None
+        r = subprocess.run(["git", "-C", root, "status", "--porcelain", "--", "kimi_delta_attention_03_amd/csrc",
+                            "include"], capture_output=True, text=True, timeout=10)
+        dirty = bool(r.stdout.strip())
+    except Exception:
+        pass
+    info = {"commit": commit, "sources_dirty": dirty, "sources_sha256_16": h.hexdigest()[:16],
+            "built_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime()), "arch": ARCH}
+    with open(os.path.join(HERE, "_build_info.json"), "w") as f:
+        json.dump(info, f)
+
+
 def build(jobs: int | None = None, verbose: bool = False) -> str:
     """Compile every source and link the library; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
@@ -69,6 +99,7 @@ def build(jobs: int | None = None, verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB_PATH)
+    _write_build_info()
     if verbose:
         print(f"built {LIB_PATH}")
     return LIB_PATH

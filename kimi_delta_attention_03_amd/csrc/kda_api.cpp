@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -114,10 +115,20 @@ kda_status check_stage34(const kda_fwd_params* p, const void* o, bool need_o, co
   return KDA_OK;
 }
 
+// A fixed-length segment: chunks [c0, c0 + nc) of every batch row. Its records
+// occupy chunk slots 0 .. B nc - 1 of the workspace (slot b nc + c).
+struct Segment {
+  int64_t c0;
+  int nc;
+};
+
+Segment whole(const kda_fwd_params* p) { return {0, p->num_seqs > 0 ? 1 : (int)(p->T / 64)}; }
+
 // Launches only: the arguments have passed check_common and check_stage12.
 kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
                       const void* beta, const int32_t* cu, void* ws, const kda::Layout& L, hipStream_t stream,
-                      const kda_gate_params* gp = nullptr) {
+                      const kda_gate_params* gp = nullptr, Segment sg = {-1, 0}) {
+  if (sg.c0 < 0) sg = whole(p);
   char* w = static_cast<char*>(ws);
   const int varlen = p->num_seqs > 0;
   if (varlen) {
@@ -146,7 +157,11 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
   a.off_chunk_tab = L.off_chunk_tab;
   a.off_w = L.off_w; a.off_qg = L.off_qg; a.off_kg = L.off_kg; a.off_aq = L.off_aq; a.off_u = L.off_u;
   a.off_gam = L.off_gam;
-  const size_t nblocks = L.ncp * (size_t)p->H;
+  a.row_T = p->T;
+  a.seg_t0 = sg.c0 * 64;
+  a.nt_seg = sg.nc;
+  if (!varlen) a.ncp = (size_t)p->B * sg.nc;
+  const size_t nblocks = a.ncp * (size_t)p->H;
   hipError_t e = kda::launch_stage12(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, (int)nblocks, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "stage 1+2 launch: %s", hipGetErrorString(e));
   return KDA_OK;
@@ -158,7 +173,8 @@ kda_status do_stage12(const kda_fwd_params* p, const void* q, const void* k, con
 // holds valid tables and every access stays in bounds.
 kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float* fin, void* ws,
                       const kda::Layout& L, hipStream_t stream, int affine_linear = 0, bool build_map = false,
-                      const int32_t* cu = nullptr) {
+                      const int32_t* cu = nullptr, Segment sg = {-1, 0}) {
+  if (sg.c0 < 0) sg = whole(p);
   const int64_t nseq = p->num_seqs > 0 ? p->num_seqs : p->B;
   if (nseq == 0) return KDA_OK;
   if (build_map && p->num_seqs > 0) {
@@ -174,7 +190,9 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   a.zero_u = affine_linear;
   a.H = (int)p->H;
   a.nunits = (int)(nseq * p->H);
-  a.nt = p->num_seqs > 0 ? 0 : (int)(p->T / 64);
+  a.nt = p->num_seqs > 0 ? 0 : sg.nc;
+  a.row_T = p->T;
+  a.seg_t0 = p->num_seqs > 0 ? 0 : sg.c0 * 64;
   a.varlen = p->num_seqs > 0;
   a.ws = static_cast<const char*>(ws);
   a.meta_bytes = L.meta_bytes; a.rec_bytes = L.rec_bytes; a.ncp = L.ncp;
@@ -184,6 +202,70 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   a.off_gam = L.off_gam;
   hipError_t e = kda::launch_stage34(a, p->K, p->qkv_dtype == KDA_DTYPE_BF16, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "stage 3+4 launch: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
+
+// Fixed-length inputs are processed in segments of whole chunks along T: stage
+// 1+2 of a segment, then stage 3+4 of it, the fp32 state handed from one
+// segment to the next through two buffers in the workspace (an exact hand-off:
+// stage 3+4 keeps the state in fp32 throughout). A segment's records (about
+// kSegmentRecordBytes) are read back by stage 3+4 while they still sit in the
+// 256 MB memory-side cache, instead of from HBM after the whole problem's
+// records have streamed through it. The result is bitwise the same for any
+// segmentation, since every chunk's arithmetic is unchanged.
+constexpr size_t kSegmentRecordBytes = (size_t)144 << 20;
+
+struct SegmentPlan {
+  int nseg;          // 1: one pass over the whole problem
+  int nc;            // chunks per segment (the last may be shorter)
+  size_t off_state;  // two state buffers at off_state and off_state + state_bytes
+  size_t state_bytes;
+};
+
+SegmentPlan plan_segments(const kda_fwd_params* p, const kda::Layout& L) {
+  SegmentPlan sp{1, 0, 0, 0};
+  if (p->num_seqs > 0 || p->B == 0 || p->T == 0) return sp;
+  const int64_t nt = p->T / 64;
+  sp.nc = (int)nt;
+  const size_t per_chunk = (size_t)p->B * (size_t)p->H * L.rec_bytes;  // records of one chunk index
+  const int64_t nc_max = std::max<int64_t>(1, (int64_t)(kSegmentRecordBytes / per_chunk));
+  const int64_t nseg = (nt + nc_max - 1) / nc_max;
+  if (nseg <= 1) return sp;
+  const int64_t nc = (nt + nseg - 1) / nseg;
+  const size_t state_bytes = kda::round_up((size_t)p->B * p->H * p->K * p->V * sizeof(float), 256);
+  const size_t off_state = L.meta_bytes + kda::round_up(per_chunk * nc, 256);
+  if (off_state + 2 * state_bytes > L.total_bytes) return sp;
+  sp.nseg = (int)((nt + nc - 1) / nc);
+  sp.nc = (int)nc;
+  sp.off_state = off_state;
+  sp.state_bytes = state_bytes;
+  return sp;
+}
+
+// Both stages over the whole problem (segmented for long fixed-length inputs).
+// The arguments have passed every check.
+kda_status run_forward(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
+                       const void* beta, const float* init, const int32_t* cu, void* o, float* fin, void* ws,
+                       const kda::Layout& L, hipStream_t stream, const kda_gate_params* gp) {
+  const SegmentPlan sp = plan_segments(p, L);
+  if (sp.nseg <= 1) {
+    kda_status s = do_stage12(p, q, k, v, g, beta, cu, ws, L, stream, gp);
+    if (s != KDA_OK) return s;
+    return do_stage34(p, init, o, fin, ws, L, stream);
+  }
+  char* w = static_cast<char*>(ws);
+  float* st[2] = {reinterpret_cast<float*>(w + sp.off_state),
+                  reinterpret_cast<float*>(w + sp.off_state + sp.state_bytes)};
+  const int64_t nt = p->T / 64;
+  for (int i = 0; i < sp.nseg; ++i) {
+    const Segment sg{(int64_t)i * sp.nc, (int)std::min<int64_t>(sp.nc, nt - (int64_t)i * sp.nc)};
+    const float* si = i == 0 ? init : st[(i - 1) & 1];
+    float* so = i == sp.nseg - 1 ? fin : st[i & 1];
+    kda_status s = do_stage12(p, q, k, v, g, beta, cu, ws, L, stream, gp, sg);
+    if (s != KDA_OK) return s;
+    s = do_stage34(p, si, o, so, ws, L, stream, 0, false, nullptr, sg);
+    if (s != KDA_OK) return s;
+  }
   return KDA_OK;
 }
 
@@ -229,6 +311,9 @@ kda_status kda_workspace_layout(const kda_fwd_params* p, kda_workspace_info* inf
   info->off_chunk_table = L.off_chunk_tab;
   info->off_seq_table = L.off_seq_tab;
   info->off_order = L.off_order;
+  const SegmentPlan sp = plan_segments(p, L);
+  info->segments = sp.nseg;
+  info->segment_chunks = sp.nc;
   return KDA_OK;
 }
 
@@ -264,9 +349,7 @@ kda_status kda_chunk_fwd(const kda_fwd_params* p, const void* q, const void* k, 
   if (s != KDA_OK) return s;
   s = check_stage34(p, o, true, initial_state, final_state);
   if (s != KDA_OK) return s;
-  s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream);
-  if (s != KDA_OK) return s;
-  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+  return run_forward(p, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace, L, stream, nullptr);
 }
 
 kda_status kda_decode_step(const kda_fwd_params* p, const void* q, const void* k, const void* v, const void* g,
@@ -401,9 +484,7 @@ kda_status kda_chunk_fwd_gated(const kda_fwd_params* p, const kda_gate_params* g
   if (s != KDA_OK) return s;
   s = check_stage34(p, o, true, initial_state, final_state);
   if (s != KDA_OK) return s;
-  s = do_stage12(p, q, k, v, g, beta, cu_seqlens, workspace, L, stream, gate);
-  if (s != KDA_OK) return s;
-  return do_stage34(p, initial_state, o, final_state, workspace, L, stream);
+  return run_forward(p, q, k, v, g, beta, initial_state, cu_seqlens, o, final_state, workspace, L, stream, gate);
 }
 
 kda_status kda_chunk_affine_summary(const kda_fwd_params* p, const int32_t* cu_seqlens, float* M, float* N,

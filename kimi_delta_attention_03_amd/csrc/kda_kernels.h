@@ -30,6 +30,10 @@ struct Stage12Args {
   size_t meta_bytes, rec_bytes, ncp;
   size_t off_chunk_tab;
   size_t off_w, off_qg, off_kg, off_aq, off_u, off_gam;
+  // fixed length: chunk slot p holds chunk p % nt_seg of batch row p / nt_seg of
+  // the segment starting at token seg_t0 of every row (rows are row_T tokens long)
+  int64_t row_T, seg_t0;
+  int nt_seg;
 };
 
 struct Stage34Args {
@@ -40,7 +44,9 @@ struct Stage34Args {
   int zero_u;          // 1: U is taken as zero (the linear part of the affine map)
   int H;
   int nunits;          // N * H
-  int nt;              // fixed length: chunks per batch row
+  int nt;              // fixed length: chunks per batch row in this segment
+  int64_t row_T;       // fixed length: tokens per batch row of the tensors
+  int64_t seg_t0;      // fixed length: first token of the segment in every row
   int varlen;
   const char* ws;
   size_t meta_bytes, rec_bytes, ncp;

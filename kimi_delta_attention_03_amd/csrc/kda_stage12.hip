@@ -176,7 +176,8 @@ void stage12_kernel(Stage12Args a) {
       r.tok0 = ct.x;
       r.len = ct.y;
     } else {
-      r.tok0 = (int64_t)r.p * C;
+      const int row = r.p / a.nt_seg;
+      r.tok0 = (int64_t)row * a.row_T + a.seg_t0 + (int64_t)(r.p - row * a.nt_seg) * C;
       r.len = C;
     }
     return r;

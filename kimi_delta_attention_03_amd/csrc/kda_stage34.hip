@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kThreads34) void stage34_kernel(Stage34Args a) {
   } else {
     p0 = (size_t)seq * a.nt;
     nch = a.nt;
-    tfirst = (int64_t)p0 * kChunk;
+    tfirst = (int64_t)seq * a.row_T + a.seg_t0;
   }
   const int last = nch - 1;
   const size_t state_base = ((size_t)seq * H + h) * K * V + 16 * vb + xi;

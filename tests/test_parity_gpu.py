@@ -225,3 +225,36 @@ def test_varlen_many_sequences_unsorted_path():
         assert eo <= TOL["bf16"] and ef <= TOL["bf16"]
     # zero-length sequences return their initial state exactly
     assert np.array_equal(fs[[3, 4000]], x.initial_state[[3, 4000]])
+
+
+@pytest.mark.parametrize("dtype,B,T,H", [("bf16", 3, 67 * 64, 16), ("fp32", 2, 66 * 64, 16)])
+def test_segmented_forward_bitwise_equals_one_pass(dtype, B, T, H):
+    """Long fixed-length inputs run in segments along T with the fp32 state handed
+    over in the workspace (kda_chunk_fwd); stage 1+2 and stage 3+4 called once each
+    over the whole problem (kda_chunk_fwd_stage12 / _stage34) compute the same chunks.
+    The two must agree bitwise, with and without final_state; the shapes give 2
+    (uneven) and 3 segments."""
+    import kimi_delta_attention_03_amd as kda
+    import torch
+    _say(f"segmented vs one pass {dtype} B={B} T={T} H={H}")
+    x = core_inputs(B, T, H, 128, 128, dtype=dtype, seed=16, init_std=0.1)
+    d = dev_inputs(x)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
+    fwd = kda.KdaForward(*args, scale=x.scale, initial_state=d["initial_state"])
+    o1, f1 = fwd()
+    o1, f1 = o1.clone(), f1.clone()
+    fwd.o.zero_()
+    fwd.final_state.zero_()
+    fwd.stage12()
+    fwd.stage34()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, fwd.o) and torch.equal(f1, fwd.final_state)
+    o3, f3 = kda.chunk_fwd(*args, scale=x.scale, initial_state=d["initial_state"], output_final_state=False)
+    torch.cuda.synchronize()
+    assert f3 is None and torch.equal(o3, o1)
+    # and the oracle on one head over the whole length
+    h = H - 1
+    o_ref, f_ref = orc.kda_chunkwise(x.q, x.k, x.v, x.g, x.beta, x.scale, 64, x.initial_state, heads=[h])
+    eo, ef = rel_err(host(o1)[:, :, [h]], o_ref), rel_err(host(f1)[:, [h]], f_ref)
+    _say(f"  head {h}: rel err o={eo:.3e} final={ef:.3e}")
+    assert eo <= TOL[dtype] and ef <= TOL[dtype]
