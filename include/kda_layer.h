@@ -16,18 +16,19 @@
  *   y      = RMSNorm_D(o) * norm_w * sigmoid(x Wgd^T Wgu^T)
  *   x_new  = y Wo^T                                 [B, T, M]
  *
- * Implementation: the plain projections run on rocBLAS (bf16 operands, fp32
- * accumulation); conv + SiLU + L2 norm, the gate and beta activations and
- * the RMSNorm / output gate are HIP kernels of this library; the core is the
- * same two-kernel path as kda_chunk_fwd with fp32 q, k, v, g and beta.
+ * Implementation: every step runs in this library's HIP kernels: the
+ * projections on its bf16 MFMA GEMM (fp32 accumulation, kda_gemm_bf16_nt),
+ * conv + SiLU + L2 norm, the gate and beta activations and the RMSNorm /
+ * output gate in elementwise kernels, and the core on the same two-kernel
+ * path as kda_chunk_fwd with fp32 q, k, v, g and beta.
  *
  * Conventions:
  *  - Every tensor pointer is a DEVICE pointer; row-major and contiguous.
  *    Linear weights are [out, in]. The caller owns every buffer.
- *  - Work is enqueued on `stream`; the call does not synchronise. The first
- *    call on a device creates that device's rocBLAS handle (rocBLAS may then
- *    allocate its own workspace); the layer entry point is therefore not
- *    meant for HIP graph capture. The core entry points are unaffected.
+ *  - Work is enqueued on `stream`; the call does not synchronise and
+ *    allocates nothing (the caller's workspace holds every intermediate), so
+ *    it can be captured in a HIP graph. It keeps no state between calls and
+ *    may be called from several threads at once on different workspaces.
  *  - Shapes and sizes are checked on the host before any launch; a failed
  *    check returns a non-zero kda_status and launches nothing.
  *  - Value preconditions are not checked (finite inputs are assumed).
@@ -68,6 +69,17 @@ typedef struct {
   const float* norm_w;     /* fp32 [D] */
   const void* Wo;          /* bf16 [M, H D] */
 } kda_layer_weights;
+
+/* The layer's projection GEMM on its own (bf16 operands, fp32 accumulation,
+ * hand-written MFMA kernel): C[m, n] = sum_k A[m, k] B[n, k] for A [M, K] and
+ * B [N, K], both row-major with K contiguous (activations [tokens, features]
+ * and Linear weights [out, in], as in the "KDAChunkwise" docs' projections),
+ * row strides lda, ldb, ldc in elements. c_dtype is KDA_DTYPE_BF16 (rounded to
+ * nearest even) or KDA_DTYPE_F32. Device pointers; A and B 16-byte aligned with
+ * K, lda and ldb multiples of 8; C must not overlap A or B. Asynchronous on
+ * `stream`, no allocation; errors as for the other entry points. */
+kda_status kda_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, void* C, int64_t ldc, int32_t c_dtype, hipStream_t stream);
 
 /* Device workspace bytes kda_layer_fwd needs (pure host computation). */
 kda_status kda_layer_fwd_workspace_bytes(const kda_layer_params* p, size_t* bytes);

@@ -111,6 +111,8 @@ SIGNATURES = {
     "kda_validate_inputs": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
                                            ctypes.POINTER(KdaInputReport)]),
     "kda_layer_fwd_workspace_bytes": (ctypes.c_int, [_LP, ctypes.POINTER(ctypes.c_size_t)]),
+    "kda_gemm_bf16_nt": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp, ctypes.c_int64, _vp,
+                                        ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int32, _vp]),
     "kda_layer_workspace_layout": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWorkspaceInfo)]),
     "kda_layer_fwd": (ctypes.c_int, [_LP, ctypes.POINTER(KdaLayerWeights), _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
 }

@@ -23,9 +23,8 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["kda_api.cpp", "kda_stage12.hip", "kda_stage34.hip", "kda_varlen.hip", "kda_layer.hip",
            "kda_decode.hip", "kda_bwd.hip", "kda_validate.hip",
-           "kda_noalloc.hip"]
-# the layer's plain projections run on rocBLAS
-LIBS = ["-L/opt/rocm/lib", "-lrocblas", "-Wl,-rpath,/opt/rocm/lib"]
+           "kda_noalloc.hip", "kda_gemm.hip"]
+LIBS = ["-L/opt/rocm/lib", "-Wl,-rpath,/opt/rocm/lib"]
 
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,259 @@
+// bf16 GEMM with fp32 accumulation on gfx950 MFMA, for the plain projections
+// of the KDA layer ("KDAChunkwise" docs, sections "From the hidden states to
+// causal Q, K, and V" and "Returning to the model dimension": the input
+// projections of the hidden states and the output projection back to the
+// model dimension).
+//
+//   C[m, n] = sum_k A[m, k] B[n, k]      A [M, K] (row stride lda), B [N, K]
+//                                         (row stride ldb), C [M, N] (ldc)
+//
+// Both operands are K-contiguous, as the layer stores them (activations
+// [tokens, features], Linear weights [out, in]), so every lane loads 16
+// contiguous bytes of one row for an MFMA operand.
+//
+// Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C; wave (wm, wn)
+// owns the 128 x 128 quadrant and keeps it in 16 accumulators of
+// v_mfma_f32_32x32x16_bf16 (4 x 4 tiles of 32 x 32). K advances in steps of
+// 64: while one step's A and B slices (32 KB each) are multiplied out of LDS,
+// the next step's slices are loaded into registers, then written to the other
+// half of a double-buffered LDS stage (128 KB).
+//
+// LDS layout: a slice is [256 rows][8 chunks of 8 bf16] with the chunk index
+// XOR-ed with (row / 2) % 8, so the 16-byte operand reads of consecutive rows
+// at one k offset spread over all banks.
+//
+// Workgroup-to-tile mapping: the workgroups of one XCD (ids congruent mod 8)
+// take blocks of 8 x 4 tiles, so each A slice is read by 4 and each B slice by
+// 8 workgroups sharing that XCD's L2.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda_device.h"
+#include "kda_kernels.h"
+#include "kda_gemm.h"
+
+namespace kda {
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kGemmThreads = 256;
+constexpr int kGroupM = 8, kGroupN = 4;   // tiles per XCD block
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx16 zero16() {
+  floatx16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// byte offset of (row, chunk) in a swizzled [256][64] bf16 slice. LDS has 64
+// banks of 4 bytes and serves a 16-byte access for 16 lanes at a time: row r
+// starts in bank 32 (r % 2), and the chunk index is XOR-ed with (r / 2) % 8,
+// so the 16 rows read by 16 lanes at one k offset (and the 2 rows x 8 chunks
+// written by 16 lanes) fall in 16 distinct 4-bank groups.
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+
+template <typename TC>
+__device__ __forceinline__ void store_out(TC* p, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
+template <>
+__device__ __forceinline__ void store_out<bf16>(bf16* p, float v) { *p = (bf16)v; }
+
+// KTAIL: K is not a multiple of 64 and the chunks past K are zeroed by selects
+// (without it the loop carries no select between a load and its LDS write)
+template <typename TC, bool KTAIL>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char sA[2][kBM * kBK * 2];
+  __shared__ __attribute__((aligned(16))) char sB[2][kBN * kBK * 2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = w >> 1, wn = w & 1;
+
+  // tile of this workgroup (XCD-aware blocks of kGroupM x kGroupN tiles)
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int slot = bid >> 3;
+  const int blk = (slot / (kGroupM * kGroupN)) * 8 + xcd;
+  const int j = slot % (kGroupM * kGroupN);
+  const int nbn = (a.ntn + kGroupN - 1) / kGroupN;
+  const int tm = (blk / nbn) * kGroupM + j % kGroupM;
+  const int tn = (blk % nbn) * kGroupN + j / kGroupM;
+  if (tm >= a.ntm || tn >= a.ntn) return;
+  const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+
+  const bf16* A = static_cast<const bf16*>(a.A);
+  const bf16* B = static_cast<const bf16*>(a.B);
+
+  // Loads of one K slice go through buffer resources over the tile's rows of A
+  // and B (rows past M or N lie outside the resource and read as zero, with no
+  // branch): thread tid loads row tid / 8 + 32 i, 16-byte chunk tid % 8, of
+  // both slices. K past the end is zeroed by a select.
+  const int64_t rowsA = a.M - m0 < kBM ? a.M - m0 : kBM, rowsB = a.N - n0 < kBN ? a.N - n0 : kBN;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(A + m0 * a.lda), (short)0, (int)(rowsA * a.lda * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(B + n0 * a.ldb), (short)0, (int)(rowsB * a.ldb * 2), 0x00020000);
+  const int lrow = tid >> 3, lch = tid & 7;
+  const int voffA = (int)((lrow * a.lda + lch * 8) * 2), voffB = (int)((lrow * a.ldb + lch * 8) * 2);
+  const int strA = (int)(32 * a.lda * 2), strB = (int)(32 * a.ldb * 2);
+  u32x4 ra[8], rb[8];
+  auto load_slice = [&](int64_t k0) {
+    const int ko = (int)(k0 * 2);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voffA, ko + i * strA, 0));
+      rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, ko + i * strB, 0));
+    }
+    if constexpr (KTAIL) {
+      const bool kin = k0 + lch * 8 < a.K;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ra[i] = kin ? ra[i] : u32x4{0, 0, 0, 0};
+        rb[i] = kin ? rb[i] : u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  // LDS byte offsets of this thread's chunks (row lrow + 32 i): the XOR key
+  // (row / 2) % 8 is the same for every i
+  const int soff = lrow * 128 + ((lch ^ ((lrow >> 1) & 7)) << 4);
+  auto store_slice = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<u32x4*>(sA[buf] + soff + i * 32 * 128) = ra[i];
+      *reinterpret_cast<u32x4*>(sB[buf] + soff + i * 32 * 128) = rb[i];
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = zero16();
+
+  // operand reads: lane l supplies row (l % 32) of a 32-row tile and the 8
+  // k values 8 (l / 32) .. + 7 of the current 16-wide k step. The fragments
+  // of k step s + 1 are read while the MFMAs of step s run.
+  const int orow = lane & 31, og = lane >> 5;
+  auto read_frags = [&](int buf, int s, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+      fa[x] = *reinterpret_cast<const bf16x8*>(sA[buf] + swz(wm * 128 + x * 32 + orow, 2 * s + og));
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+      fb[y] = *reinterpret_cast<const bf16x8*>(sB[buf] + swz(wn * 128 + y * 32 + orow, 2 * s + og));
+  };
+  auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+  };
+
+  const int nk = (int)((a.K + kBK - 1) / kBK);
+  load_slice(0);
+  store_slice(0);
+  __syncthreads();
+  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  // One K step, straight-line code: the next slice's global loads go out first,
+  // the fragments of k step s + 1 are read from LDS between the MFMAs of step s
+  // and the next slice's LDS writes sit between the MFMAs of the last step. The
+  // scheduling-group barriers pin that interleaving (the default schedule reuses
+  // one fragment register and waits for each read before its MFMAs).
+  constexpr int MFMA = 0x008, VMEM_RD = 0x020, DS_RD = 0x100, DS_WR = 0x200;
+  int kt = 0;
+  for (; kt + 1 < nk; ++kt) {
+    const int buf = kt & 1;
+    read_frags(buf, 0, f0a, f0b);
+    load_slice((int64_t)(kt + 1) * kBK);
+    read_frags(buf, 1, f1a, f1b);
+    mma(f0a, f0b);
+    read_frags(buf, 2, f0a, f0b);
+    mma(f1a, f1b);
+    read_frags(buf, 3, f1a, f1b);
+    mma(f0a, f0b);
+    store_slice(buf ^ 1);
+    mma(f1a, f1b);
+    __builtin_amdgcn_sched_group_barrier(DS_RD, 8, 0);
+    // k step 0: the global loads spread over its MFMAs (a burst of 16 would
+    // hold the wave at a full memory queue with the MFMA pipe idle)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(VMEM_RD, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(VMEM_RD, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+    }
+#pragma unroll
+    for (int st = 1; st < 3; ++st) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+    }
+    __syncthreads();
+  }
+  {
+    const int buf = kt & 1;
+    read_frags(buf, 0, f0a, f0b);
+    read_frags(buf, 1, f1a, f1b);
+    mma(f0a, f0b);
+    read_frags(buf, 2, f0a, f0b);
+    mma(f1a, f1b);
+    read_frags(buf, 3, f1a, f1b);
+    mma(f0a, f0b);
+    mma(f1a, f1b);
+  }
+
+  // accumulator element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  TC* C = static_cast<TC*>(a.C);
+  const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;   // uniform
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int64_t col = n0 + wn * 128 + y * 32 + orow;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + x * 32 + 8 * (r >> 2) + 4 * og + (r & 3);
+        if (full || (row < a.M && col < a.N)) store_out<TC>(C + row * a.ldc + col, acc[x][y][r]);
+      }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16(const GemmArgs& a0, int out_f32, hipStream_t s) {
+  GemmArgs a = a0;
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  a.ntm = (int)((a.M + kBM - 1) / kBM);
+  a.ntn = (int)((a.N + kBN - 1) / kBN);
+  const int nbm = (a.ntm + kGroupM - 1) / kGroupM, nbn = (a.ntn + kGroupN - 1) / kGroupN;
+  const int nblk8 = (nbm * nbn + 7) / 8 * 8;   // blocks, padded to whole rounds of 8 XCDs
+  const dim3 grid((unsigned)(nblk8 * kGroupM * kGroupN)), block(kGemmThreads);
+  const bool ktail = a.K % kBK != 0;
+  if (out_f32) {
+    if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<float, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_bf16_nt_kernel<float, false>), grid, block, 0, s, a);
+  } else {
+    if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kda

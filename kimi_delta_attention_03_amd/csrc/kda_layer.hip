@@ -6,30 +6,29 @@
 // Order of work on the caller's stream (BT = B * T tokens, HD = H * D):
 //   1. Wcat = [Wqkv; Wad; Wgd; Wb] (device copies, rows of width M): the
 //      low-rank slices of P start at 16-byte aligned columns
-//   2. P    = x Wcat^T                     rocBLAS, bf16 x bf16 (fp32 accumulation) -> bf16 [BT, NP]
+//   2. P    = x Wcat^T                     GEMM, bf16 x bf16 (fp32 accumulation) -> bf16 [BT, NP]
 //   3. prologue kernel: q, k, v = SiLU(conv4(P_qkv)) (+ L2 norm for q, k) in
 //      fp32, beta = sigmoid(P_b)
-//   4. g    = P_a Wau^T                    rocBLAS -> fp32 [BT, HD] (raw gate; P_a read in place)
+//   4. g    = P_a Wau^T                    GEMM -> fp32 [BT, HD] (raw gate; P_a read in place)
 //   5. core: the two-kernel chunkwise forward on fp32 q, k, v, beta with the
 //      decay g = lb * sigmoid(exp(A_log_h) (g_raw + dt_bias)) applied inside
 //      stage 1+2 (no separate pass over g)
-//   6. Gu   = P_g Wgu^T                    rocBLAS -> fp32 [BT, HD]
+//   6. Gu   = P_g Wgu^T                    GEMM -> fp32 [BT, HD]
 //   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in P's space)
-//   8. x_new = y Wo^T                      rocBLAS, bf16 x bf16 -> bf16 [BT, M]
-// The plain projections are library GEMMs; every other step is a kernel of
-// this file or of the core. The elementwise kernels are HBM-bound: each reads
+//   8. x_new = y Wo^T                      GEMM, bf16 x bf16 -> bf16 [BT, M]
+// The projections run on this library's MFMA GEMM (kda_gemm.hip); every other
+// step is a kernel of this file or of the core. The elementwise kernels are HBM-bound: each reads
 // its inputs once with coalesced vector loads and writes its outputs once.
 #include <hip/hip_runtime.h>
-#include <rocblas/rocblas.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
-#include <mutex>
 
 #include "kda.h"
 #include "kda_layer.h"
 #include "kda_kernels.h"
+#include "kda_gemm.h"
 
 namespace kda {
 namespace {
@@ -230,34 +229,16 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
   return KDA_OK;
 }
 
-std::mutex g_handle_mu;
-rocblas_handle g_handles[64] = {};
-
-kda_status handle_for_device(rocblas_handle* out) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
-    return fail_msg(KDA_ERR_HIP, "no current HIP device");
-  std::lock_guard<std::mutex> lk(g_handle_mu);
-  if (!g_handles[dev]) {
-    rocblas_handle h = nullptr;
-    if (rocblas_create_handle(&h) != rocblas_status_success)
-      return fail_msg(KDA_ERR_HIP, "rocblas_create_handle failed");
-    g_handles[dev] = h;
-  }
-  *out = g_handles[dev];
-  return KDA_OK;
-}
-
-// Y[n_rows, N] = X[n_rows, Kd] W[N, Kd]^T, row-major; X has leading dim ldx
-kda_status gemm_nt(rocblas_handle hb, const void* W, int ldw, const void* X, int ldx, void* Y, int ldy,
-                   rocblas_datatype ytype, int N, int n_rows, int Kd, const char* what) {
-  const float one = 1.f, zero = 0.f;
-  const rocblas_status st =
-      rocblas_gemm_ex(hb, rocblas_operation_transpose, rocblas_operation_none, N, n_rows, Kd, &one, W,
-                      rocblas_datatype_bf16_r, ldw, X, rocblas_datatype_bf16_r, ldx, &zero, Y, ytype, ldy, Y, ytype,
-                      ldy, rocblas_datatype_f32_r, rocblas_gemm_algo_standard, 0, 0);
-  if (st != rocblas_status_success)
-    return fail_msg(KDA_ERR_HIP, "rocblas_gemm_ex (%s) failed: %s", what, rocblas_status_to_string(st));
+// Y[n_rows, N] = X[n_rows, Kd] W[N, Kd]^T, row-major, on this library's MFMA GEMM
+kda_status gemm_nt(const void* W, int64_t ldw, const void* X, int64_t ldx, void* Y, int64_t ldy, bool y_f32,
+                   int64_t N, int64_t n_rows, int64_t Kd, hipStream_t stream, const char* what) {
+  GemmArgs g{};
+  g.A = X; g.lda = ldx;
+  g.B = W; g.ldb = ldw;
+  g.C = Y; g.ldc = ldy;
+  g.M = n_rows; g.N = N; g.K = Kd;
+  const hipError_t e = launch_gemm_bf16(g, y_f32 ? 1 : 0, stream);
+  if (e != hipSuccess) return fail_msg(KDA_ERR_HIP, "GEMM (%s) launch: %s", what, hipGetErrorString(e));
   return KDA_OK;
 }
 
@@ -272,6 +253,28 @@ kda_status kda_layer_fwd_workspace_bytes(const kda_layer_params* p, size_t* byte
   if (s != KDA_OK) return s;
   if (!bytes) return kda::fail_msg(KDA_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = L.total;
+  return KDA_OK;
+}
+
+kda_status kda_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                            int64_t ldb, void* C, int64_t ldc, int32_t c_dtype, hipStream_t stream) {
+  using namespace kda;
+  clear_msg();
+  if (M < 0 || N < 0 || K < 0) return fail_msg(KDA_ERR_INVALID_ARG, "need M, N, K >= 0");
+  if (c_dtype != KDA_DTYPE_BF16 && c_dtype != KDA_DTYPE_F32) return fail_msg(KDA_ERR_INVALID_ARG, "unknown c_dtype");
+  if (M == 0 || N == 0) return KDA_OK;
+  if (K % 8 || lda % 8 || ldb % 8 || lda < K || ldb < K || ldc < N)
+    return fail_msg(KDA_ERR_INVALID_ARG, "K, lda, ldb must be multiples of 8 with lda, ldb >= K and ldc >= N");
+  if (!A || !B || !C) return fail_msg(KDA_ERR_INVALID_ARG, "A, B and C must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
+      reinterpret_cast<uintptr_t>(C) % (c_dtype == KDA_DTYPE_F32 ? 4 : 2))
+    return fail_msg(KDA_ERR_INVALID_ARG, "A and B must be 16-byte aligned, C aligned to its element size");
+  if ((M + 255) / 256 * ((N + 255) / 256) > (int64_t)1 << 26) return fail_msg(KDA_ERR_UNSUPPORTED, "GEMM too large");
+  GemmArgs g{};
+  g.A = A; g.B = B; g.C = C;
+  g.M = M; g.N = N; g.K = K; g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+  const hipError_t e = launch_gemm_bf16(g, c_dtype == KDA_DTYPE_F32, stream);
+  if (e != hipSuccess) return fail_msg(KDA_ERR_HIP, "GEMM launch: %s", hipGetErrorString(e));
   return KDA_OK;
 }
 
@@ -311,11 +314,6 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     return fail_msg(KDA_ERR_WORKSPACE, "workspace must be non-NULL and 256-byte aligned");
   if (workspace_bytes < L.total)
     return fail_msg(KDA_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", workspace_bytes, L.total);
-  rocblas_handle hb;
-  s = handle_for_device(&hb);
-  if (s != KDA_OK) return s;
-  if (rocblas_set_stream(hb, stream) != rocblas_status_success) return fail_msg(KDA_ERR_HIP, "rocblas_set_stream failed");
-
   char* ws = static_cast<char*>(workspace);
   const int M = p->M, H = p->H, D = p->D, HD = L.HD, NP = L.NP;
   const int BT = (int)L.BT;
@@ -343,7 +341,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
   }
   // 2. P = x Wcat^T
   const int NW = 3 * HD + r + rg + H;  // rows of Wcat (columns of P in use)
-  s = gemm_nt(hb, wcat, M, x, M, P, NP, rocblas_datatype_bf16_r, NW, BT, M, "input projections");
+  s = gemm_nt(wcat, M, x, M, P, NP, false, NW, BT, M, stream, "input projections");
   if (s != KDA_OK) return s;
   // 3. prologue
   {
@@ -363,7 +361,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "prologue launch failed");
   }
   // 4. decay-gate up projection (raw gate)
-  s = gemm_nt(hb, w->Wau, r, P + off_r, NP, g, HD, rocblas_datatype_f32_r, HD, BT, r, "decay gate");
+  s = gemm_nt(w->Wau, r, P + off_r, NP, g, HD, true, HD, BT, r, stream, "decay gate");
   if (s != KDA_OK) return s;
   // 5. the chunkwise core in fp32, gate activation inside stage 1+2
   {
@@ -380,7 +378,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
   // 6. output-gate up projection,
   // 7. RMSNorm * gate -> y (bf16, in P's space: P is dead once both up projections have read it)
   float* gu = reinterpret_cast<float*>(ws + L.off_gu);
-  s = gemm_nt(hb, w->Wgu, rg, P + off_r + r, NP, gu, HD, rocblas_datatype_f32_r, HD, BT, rg, "output gate");
+  s = gemm_nt(w->Wgu, rg, P + off_r + r, NP, gu, HD, true, HD, BT, rg, stream, "output gate");
   if (s != KDA_OK) return s;
   uint16_t* y = P;
   {
@@ -396,7 +394,7 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
     if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "norm launch failed");
   }
   // 8. x_new = y Wo^T
-  return gemm_nt(hb, w->Wo, HD, y, HD, x_new, M, rocblas_datatype_bf16_r, M, BT, HD, "output projection");
+  return gemm_nt(w->Wo, HD, y, HD, x_new, M, false, M, BT, HD, stream, "output projection");
 }
 
 }  // extern "C"
