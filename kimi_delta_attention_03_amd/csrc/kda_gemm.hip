@@ -13,14 +13,20 @@
 //
 // Tiling: a workgroup of 4 waves computes a 256 x 256 tile of C; wave (wm, wn)
 // owns the 128 x 128 quadrant and keeps it in 16 accumulators of
-// v_mfma_f32_32x32x16_bf16 (4 x 4 tiles of 32 x 32). K advances in steps of
-// 64: while one step's A and B slices (32 KB each) are multiplied out of LDS,
-// the next step's slices are loaded into registers, then written to the other
-// half of a double-buffered LDS stage (128 KB).
+// v_mfma_f32_32x32x16_bf16 (4 x 4 tiles of 32 x 32). K advances in slices of
+// 64 through a double-buffered LDS stage (2 x 64 KB): while slice kt is
+// multiplied out of one buffer, slice kt + 1 (already in registers) is written
+// to the other and slice kt + 2 is loaded from global memory into the freed
+// registers, so every load has a whole slice of MFMAs to arrive. One barrier
+// per slice, placed so that the next slice's first fragments are read while
+// the current slice's last MFMAs run.
 //
 // LDS layout: a slice is [256 rows][8 chunks of 8 bf16] with the chunk index
 // XOR-ed with (row / 2) % 8, so the 16-byte operand reads of consecutive rows
-// at one k offset spread over all banks.
+// at one k offset spread over all banks. LDS has 64 banks of 4 bytes and
+// serves a 16-byte access for 16 lanes at a time: row r starts in bank
+// 32 (r % 2), so the 16 rows read by 16 lanes at one k offset (and the 2 rows
+// x 8 chunks written by 16 lanes) fall in 16 distinct 4-bank groups.
 //
 // Workgroup-to-tile mapping: the workgroups of one XCD (ids congruent mod 8)
 // take blocks of 8 x 4 tiles, so each A slice is read by 4 and each B slice by
@@ -50,13 +56,6 @@ __device__ __forceinline__ floatx16 zero16() {
   return z;
 }
 
-// byte offset of (row, chunk) in a swizzled [256][64] bf16 slice. LDS has 64
-// banks of 4 bytes and serves a 16-byte access for 16 lanes at a time: row r
-// starts in bank 32 (r % 2), and the chunk index is XOR-ed with (r / 2) % 8,
-// so the 16 rows read by 16 lanes at one k offset (and the 2 rows x 8 chunks
-// written by 16 lanes) fall in 16 distinct 4-bank groups.
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
-
 template <typename TC>
 __device__ __forceinline__ void store_out(TC* p, float v);
 template <>
@@ -68,8 +67,8 @@ __device__ __forceinline__ void store_out<bf16>(bf16* p, float v) { *p = (bf16)v
 // (without it the loop carries no select between a load and its LDS write)
 template <typename TC, bool KTAIL>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) char sA[2][kBM * kBK * 2];
-  __shared__ __attribute__((aligned(16))) char sB[2][kBN * kBK * 2];
+  // LDS buffer b: A slice at smem[b][0, 32 KB), B slice at smem[b][32 KB, 64 KB)
+  __shared__ __attribute__((aligned(16))) char smem[2][(kBM + kBN) * kBK * 2];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -104,17 +103,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
   const int voffA = (int)((lrow * a.lda + lch * 8) * 2), voffB = (int)((lrow * a.ldb + lch * 8) * 2);
   const int strA = (int)(32 * a.lda * 2), strB = (int)(32 * a.ldb * 2);
   u32x4 ra[8], rb[8];
-  auto load_slice = [&](int64_t k0) {
+  // half h of a slice: rows lrow + 32 i for i in [4 h, 4 h + 4)
+  auto load_half = [&](int64_t k0, int h) {
     const int ko = (int)(k0 * 2);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 4 * h; i < 4 * h + 4; ++i) {
       ra[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsA, voffA, ko + i * strA, 0));
       rb[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsB, voffB, ko + i * strB, 0));
     }
     if constexpr (KTAIL) {
       const bool kin = k0 + lch * 8 < a.K;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 4 * h; i < 4 * h + 4; ++i) {
         ra[i] = kin ? ra[i] : u32x4{0, 0, 0, 0};
         rb[i] = kin ? rb[i] : u32x4{0, 0, 0, 0};
       }
@@ -123,11 +123,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
   // LDS byte offsets of this thread's chunks (row lrow + 32 i): the XOR key
   // (row / 2) % 8 is the same for every i
   const int soff = lrow * 128 + ((lch ^ ((lrow >> 1) & 7)) << 4);
-  auto store_slice = [&](int buf) {
+  auto store_half = [&](int buf, int h) {
+    char* base = smem[buf] + soff;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<u32x4*>(sA[buf] + soff + i * 32 * 128) = ra[i];
-      *reinterpret_cast<u32x4*>(sB[buf] + soff + i * 32 * 128) = rb[i];
+    for (int i = 4 * h; i < 4 * h + 4; ++i) {
+      *reinterpret_cast<u32x4*>(base + i * 32 * 128) = ra[i];
+      *reinterpret_cast<u32x4*>(base + kBM * kBK * 2 + i * 32 * 128) = rb[i];
     }
   };
 
@@ -138,16 +139,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
     for (int y = 0; y < 4; ++y) acc[x][y] = zero16();
 
   // operand reads: lane l supplies row (l % 32) of a 32-row tile and the 8
-  // k values 8 (l / 32) .. + 7 of the current 16-wide k step. The fragments
-  // of k step s + 1 are read while the MFMAs of step s run.
+  // k values 8 (l / 32) .. + 7 of the current 16-wide k step. The XOR key of
+  // rows wm 128 + 32 x + orow is (orow / 2) % 8 for every x, and chunk 2 s + og
+  // XOR-ed with it is 2 s XOR (og ^ key): a lane's fragment addresses differ
+  // across x, y and buffers only by constants.
   const int orow = lane & 31, og = lane >> 5;
+  const int kx = og ^ ((orow >> 1) & 7);
+  int ofa[4], ofb[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    ofa[st] = (wm * 128 + orow) * 128 + (((2 * st) ^ kx) << 4);
+    ofb[st] = kBM * kBK * 2 + (wn * 128 + orow) * 128 + (((2 * st) ^ kx) << 4);
+  }
   auto read_frags = [&](int buf, int s, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+    const char* base = smem[buf];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
-      fa[x] = *reinterpret_cast<const bf16x8*>(sA[buf] + swz(wm * 128 + x * 32 + orow, 2 * s + og));
+    for (int x = 0; x < 4; ++x) fa[x] = *reinterpret_cast<const bf16x8*>(base + ofa[s] + x * 32 * 128);
 #pragma unroll
-    for (int y = 0; y < 4; ++y)
-      fb[y] = *reinterpret_cast<const bf16x8*>(sB[buf] + swz(wn * 128 + y * 32 + orow, 2 * s + og));
+    for (int y = 0; y < 4; ++y) fb[y] = *reinterpret_cast<const bf16x8*>(base + ofb[s] + y * 32 * 128);
   };
   auto mma = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
 #pragma unroll
@@ -157,59 +166,78 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
         acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
   };
 
-  const int nk = (int)((a.K + kBK - 1) / kBK);
-  load_slice(0);
-  store_slice(0);
-  __syncthreads();
-  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
-  // One K step, straight-line code: the next slice's global loads go out first,
-  // the fragments of k step s + 1 are read from LDS between the MFMAs of step s
-  // and the next slice's LDS writes sit between the MFMAs of the last step. The
-  // scheduling-group barriers pin that interleaving (the default schedule reuses
-  // one fragment register and waits for each read before its MFMAs).
+  // Pipeline over K slices of 64: slice kt is multiplied out of LDS buffer
+  // kt % 2. At the start of that, slice kt + 1 (loaded into registers during
+  // slice kt - 1) is written to the other buffer, each register being reloaded
+  // with slice kt + 2 right after its write, so a load has a whole slice of
+  // MFMAs to arrive. The one barrier of a slice sits before the MFMAs of its
+  // last 16-wide k step: by then every wave has read all of this slice's
+  // fragments and written the next slice, so the next slice's first fragments
+  // are read while those MFMAs run.
   constexpr int MFMA = 0x008, VMEM_RD = 0x020, DS_RD = 0x100, DS_WR = 0x200;
+  bf16x8 f0a[4], f0b[4], f1a[4], f1b[4];
+  const int nk = (int)((a.K + kBK - 1) / kBK);
+  load_half(0, 0);
+  load_half(0, 1);
+  store_half(0, 0);
+  store_half(0, 1);
+  load_half(nk > 1 ? kBK : 0, 0);
+  load_half(nk > 1 ? kBK : 0, 1);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  read_frags(0, 0, f0a, f0b);
   int kt = 0;
   for (; kt + 1 < nk; ++kt) {
     const int buf = kt & 1;
-    read_frags(buf, 0, f0a, f0b);
-    load_slice((int64_t)(kt + 1) * kBK);
-    read_frags(buf, 1, f1a, f1b);
+    const int64_t kl = (int64_t)(kt + 2 < nk ? kt + 2 : nk - 1) * kBK;
+    // k steps 0 and 1: the fragments of the following step are read first,
+    // then half of the next slice goes to LDS, each register reloaded from
+    // global memory right after its write
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st == 0) {
+        mma(f0a, f0b);
+        read_frags(buf, 1, f1a, f1b);
+      } else {
+        mma(f1a, f1b);
+        read_frags(buf, 2, f0a, f0b);
+      }
+      store_half(buf ^ 1, st);
+      load_half(kl, st);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(VMEM_RD, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // k step 2
     mma(f0a, f0b);
-    read_frags(buf, 2, f0a, f0b);
-    mma(f1a, f1b);
     read_frags(buf, 3, f1a, f1b);
-    mma(f0a, f0b);
-    store_slice(buf ^ 1);
-    mma(f1a, f1b);
-    __builtin_amdgcn_sched_group_barrier(DS_RD, 8, 0);
-    // k step 0: the global loads spread over its MFMAs (a burst of 16 would
-    // hold the wave at a full memory queue with the MFMA pipe idle)
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(VMEM_RD, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(VMEM_RD, 1, 0);
       __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
     }
-#pragma unroll
-    for (int st = 1; st < 3; ++st) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(MFMA, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(DS_RD, 1, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(MFMA, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(DS_WR, 1, 0);
-    }
-    __syncthreads();
+    __builtin_amdgcn_sched_group_barrier(MFMA, 8, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // every wave has read this slice's fragments and written the next slice:
+    // the barrier, then the next slice's first fragments are read under the
+    // MFMAs of k step 3 (global loads stay in flight)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    read_frags(buf ^ 1, 0, f0a, f0b);
+    mma(f1a, f1b);
+    __builtin_amdgcn_sched_group_barrier(DS_RD, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(MFMA, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
   {
     const int buf = kt & 1;
-    read_frags(buf, 0, f0a, f0b);
     read_frags(buf, 1, f1a, f1b);
     mma(f0a, f0b);
     read_frags(buf, 2, f0a, f0b);
