@@ -12,6 +12,7 @@ struct GemmArgs {
   void* C;             // [M, N], row stride ldc, bf16 or fp32
   int64_t M, N, K, lda, ldb, ldc;
   int ntm, ntn;        // tiles along M and N (set by the launcher)
+  int vec_out;         // C rows 4-element aligned: full tiles use vector stores (set by the launcher)
 };
 
 // C = A B^T on MFMA (bf16 operands, fp32 accumulation); out_f32 selects fp32 C

@@ -31,6 +31,12 @@
 // Workgroup-to-tile mapping: the workgroups of one XCD (ids congruent mod 8)
 // take blocks of 8 x 4 tiles, so each A slice is read by 4 and each B slice by
 // 8 workgroups sharing that XCD's L2.
+//
+// Output: fp32 C is stored straight from the accumulators (each store
+// instruction covers 128 contiguous bytes of two rows). bf16 C is computed
+// transposed (B as the first MFMA operand, so a lane holds runs of four columns
+// of one row), staged through LDS and written back as 16-byte pieces of whole
+// rows: 32 store instructions per lane instead of 256 two-byte ones.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -62,7 +68,6 @@ template <>
 __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
 template <>
 __device__ __forceinline__ void store_out<bf16>(bf16* p, float v) { *p = (bf16)v; }
-
 // KTAIL: K is not a multiple of 64 and the chunks past K are zeroed by selects
 // (without it the loop carries no select between a load and its LDS write)
 template <typename TC, bool KTAIL>
@@ -74,6 +79,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
+  // bf16 C is computed transposed (B as the first MFMA operand) and staged
+  // through LDS for row-contiguous stores; fp32 C keeps A first (see the end)
+  constexpr bool kTr = sizeof(TC) == 2;
 
   // tile of this workgroup (XCD-aware blocks of kGroupM x kGroupN tiles)
   const int bid = blockIdx.x;
@@ -82,8 +90,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
   const int blk = (slot / (kGroupM * kGroupN)) * 8 + xcd;
   const int j = slot % (kGroupM * kGroupN);
   const int nbn = (a.ntn + kGroupN - 1) / kGroupN;
-  const int tm = (blk / nbn) * kGroupM + j % kGroupM;
-  const int tn = (blk % nbn) * kGroupN + j / kGroupM;
+  // the tile indices are uniform; the integer division runs on the vector ALU,
+  // so they are moved to scalar registers explicitly (otherwise the buffer
+  // resources built from them may be taken as per-lane values)
+  const int tm = __builtin_amdgcn_readfirstlane((blk / nbn) * kGroupM + j % kGroupM);
+  const int tn = __builtin_amdgcn_readfirstlane((blk % nbn) * kGroupN + j / kGroupM);
   if (tm >= a.ntm || tn >= a.ntn) return;
   const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
 
@@ -163,7 +174,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
     for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 4; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
+        acc[x][y] = kTr ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[y], fa[x], acc[x][y], 0, 0, 0)
+                        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[x], fb[y], acc[x][y], 0, 0, 0);
   };
 
   // Pipeline over K slices of 64: slice kt is multiplied out of LDS buffer
@@ -247,20 +259,95 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
     mma(f1a, f1b);
   }
 
-  // accumulator element r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
   TC* C = static_cast<TC*>(a.C);
-  const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;   // uniform
+  if constexpr (!kTr) {
+    // fp32 C: accumulator element r of lane l is row 8 (r / 4) + 4 (l / 32) +
+    // r % 4, column l % 32; one store instruction covers 128 contiguous bytes of
+    // each of two rows
+    const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;   // uniform
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int64_t col = n0 + wn * 128 + y * 32 + orow;
+      for (int y = 0; y < 4; ++y) {
+        const int64_t col = n0 + wn * 128 + y * 32 + orow;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + x * 32 + 8 * (r >> 2) + 4 * og + (r & 3);
-        if (full || (row < a.M && col < a.N)) store_out<TC>(C + row * a.ldc + col, acc[x][y][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 128 + x * 32 + 8 * (r >> 2) + 4 * og + (r & 3);
+          if (full || (row < a.M && col < a.N)) store_out<TC>(C + row * a.ldc + col, acc[x][y][r]);
+        }
+      }
+    return;
+  } else {
+    // bf16 C, computed transposed: element r of lane l is row l % 32, column
+    // 8 (r / 4) + 4 (l / 32) + r % 4 of the 32 x 32 tile, i.e. four consecutive
+    // columns of one row per group r / 4.
+    if (a.vec_out) {
+      // Each wave stages its 128 x 128 quadrant through its own 32 KB of LDS
+      // (rows of 256 bytes, 16-byte chunks XOR-swizzled by row) and writes it
+      // back in 16-byte pieces of whole rows: one store instruction covers four
+      // complete rows. Pieces of partial tiles that cross M or N are written
+      // element by element.
+      const bool full = m0 + kBM <= a.M && n0 + kBN <= a.N;   // uniform
+      char* q = &smem[0][0] + w * 32768;
+      // every wave has read its last operand fragments before any staging write
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int rw = x * 32 + orow;
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int byte = (32 * y + 8 * g + 4 * og) * 2;
+            const floatx16& c = acc[x][y];
+            bf16x4 o;
+            o[0] = (bf16)c[4 * g]; o[1] = (bf16)c[4 * g + 1]; o[2] = (bf16)c[4 * g + 2]; o[3] = (bf16)c[4 * g + 3];
+            *reinterpret_cast<bf16x4*>(q + rw * 256 + (((byte >> 4) ^ (rw & 15)) << 4) + (byte & 15)) = o;
+          }
+      }
+      // the quadrant region is this wave's own: an LDS wait orders the reads
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int i0 = 0; i0 < 32; i0 += 8) {
+        u32x4 rv[8];
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) {
+          const int rw = 4 * (i0 + i2) + (lane >> 4), ch = lane & 15;
+          rv[i2] = *reinterpret_cast<const u32x4*>(q + rw * 256 + ((ch ^ (rw & 15)) << 4));
+        }
+#pragma unroll
+        for (int i2 = 0; i2 < 8; ++i2) {
+          const int rw = 4 * (i0 + i2) + (lane >> 4), ch = lane & 15;
+          const int64_t row = m0 + wm * 128 + rw, col = n0 + wn * 128 + ch * 8;
+          if (full || (row < a.M && col + 8 <= a.N)) {
+            *reinterpret_cast<u32x4*>(C + row * a.ldc + col) = rv[i2];
+          } else if (row < a.M) {
+            const bf16* e = reinterpret_cast<const bf16*>(&rv[i2]);
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (col + k < a.N) C[row * a.ldc + col + k] = e[k];
+          }
+        }
+      }
+      return;
+    }
+    // C rows not 16-byte aligned: element stores
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int64_t row = m0 + wm * 128 + x * 32 + orow;
+      if (row >= a.M) continue;
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int64_t col = n0 + wn * 128 + y * 32 + 8 * g + 4 * og;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (col + e < a.N) store_out<TC>(C + row * a.ldc + col + e, acc[x][y][4 * g + e]);
+        }
       }
     }
+  }
 }
 
 }  // namespace
@@ -270,6 +357,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& a0, int out_f32, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   a.ntm = (int)((a.M + kBM - 1) / kBM);
   a.ntn = (int)((a.N + kBN - 1) / kBN);
+  // bf16 C is written in 16-byte row pieces: every row start 16-byte aligned
+  a.vec_out = !out_f32 && a.ldc % 8 == 0 && reinterpret_cast<uintptr_t>(a.C) % 16 == 0;
   const int nbm = (a.ntm + kGroupM - 1) / kGroupM, nbn = (a.ntn + kGroupN - 1) / kGroupN;
   const int nblk8 = (nbm * nbn + 7) / 8 * 8;   // blocks, padded to whole rounds of 8 XCDs
   const dim3 grid((unsigned)(nblk8 * kGroupM * kGroupN)), block(kGemmThreads);

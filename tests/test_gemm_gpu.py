@@ -77,6 +77,26 @@ def test_gemm_strided_slices():
     assert torch.all(Cbuf[:, :8] == 7.0) and torch.all(Cbuf[:, 308:] == 7.0)
 
 
+@pytest.mark.parametrize("ldc,c0", [(320, 8), (322, 8), (320, 4)],
+                         ids=["aligned_rows", "odd_row_stride", "misaligned_start"])
+def test_gemm_strided_bf16_output(ldc, c0):
+    """bf16 C inside a wider buffer: 16-byte aligned rows take the staged
+    row-piece stores (with pieces crossing N written element by element),
+    other strides or starts the element stores; columns outside C's window and
+    rows past M stay untouched."""
+    import torch
+    g = torch.Generator(device="cuda:0").manual_seed(11)
+    M, N, K = 700, 300, 200
+    A = torch.randn(M, K, device="cuda:0", generator=g).to(torch.bfloat16)
+    B = torch.randn(N, K, device="cuda:0", generator=g).to(torch.bfloat16)
+    Cbuf = torch.full((M + 1, ldc), 7.0, device="cuda:0").to(torch.bfloat16)
+    C = Cbuf[:M, c0:c0 + N]
+    gemm(A, B, False, C=C, ldc=ldc)
+    torch.cuda.synchronize()
+    assert rel(C, ref(A, B)) <= 4e-3
+    assert torch.all(Cbuf[:, :c0] == 7.0) and torch.all(Cbuf[:, c0 + N:] == 7.0) and torch.all(Cbuf[M] == 7.0)
+
+
 @pytest.mark.parametrize("M,N,K,out_f32", [(32768, 6416, 2048, False), (32768, 2048, 128, True),
                                            (32768, 2048, 2048, False)],
                          ids=["input_projection", "low_rank_up", "output_projection"])
