@@ -291,6 +291,18 @@ def bwd_flops_per_chunk_head(C, K, V):
     }
 
 
+def bwd_chunk_alg_bytes_per_token_head(K, V, e):
+    """Bytes the chunk-gradient launch pair cannot avoid per token-head, with
+    inputs of e bytes per element: the chunk's inputs q, k, g (K each), v and
+    dO (V each) and beta, the chunk-start state S and the end-state gradient
+    dS' (K x V fp32 each, once per 64-token chunk), and the fp32 gradients dq,
+    dk, dg, dv and dbeta it writes. At K = V = 128 with bf16 inputs: 3330 B
+    read + 2052 B written."""
+    reads = (3 * K + 2 * V + 1) * e + 2 * K * V * 4 / 64
+    writes = (3 * K + V + 1) * 4
+    return reads + writes
+
+
 def bench_backward(args, torch, kda, WORKLOADS, workload):
     """The backward (kda_chunk_bwd) on a core workload's shape: one step = all
     four launches for d_o ~ N(0,1) and d_final ~ N(0,1); each launch is also
@@ -337,6 +349,22 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
         if rec.get("source_sha256_16") == kernel_source_hash("bwd") and all(n in rec["kernels"] for n in names[dom]):
             traffic = sum(rec["kernels"][n]["traffic_bytes"] for n in names[dom])
     ach = fl[dom] * nchunk_heads / (stage_ms[dom] / 1e3) / 1e12
+    if dom == "chunk":
+        # the chunk pair streams its operands and results through the fp32 slab:
+        # it is bound by memory traffic, so its roofline is HBM on the bytes it
+        # cannot avoid (see bwd_chunk_alg_bytes_per_token_head), with the
+        # measured bytes beside them
+        ntok_heads = (int(x.cu_seqlens[-1]) if cu is not None else B * T) * H
+        alg_b = bwd_chunk_alg_bytes_per_token_head(K, V, 2 if x.dtype == "bf16" else 4) * ntok_heads
+        gbps = alg_b / (stage_ms[dom] / 1e3) / 1e9
+        roof = {"kernel": "bwd_chunk (chunk_mm + chunk_elem)", "bound": "hbm", "achieved": gbps,
+                "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbps * 1e9 / PEAK_HBM, "traffic": traffic,
+                "alg_bytes_per_launch": alg_b, "traffic_over_alg": None if traffic is None else traffic / alg_b,
+                "alu_TFLOPs": ach, "alu_frac_fp32": ach * 1e12 / PEAK_FP32}
+    else:
+        roof = {"kernel": f"bwd_{dom}", "bound": "alu", "achieved": ach, "peak": PEAK_FP32 / 1e12,
+                "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": traffic,
+                "alg_flops_per_launch": fl[dom] * nchunk_heads}
     print(json.dumps({
         "metric": "KDA chunk-bwd tokens/s (dq, dk, dv, dg, dbeta, dh0)", "value": B * T / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
@@ -345,9 +373,7 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
         "config": {"workload": WORKLOADS[args.workload]["name"] + "_backward", "B": B, "T": T, "H": H, "K": K,
                    "V": V},
         "stage_ms": stage_ms,
-        "roofline": {"kernel": f"bwd_{dom}", "bound": "alu", "achieved": ach, "peak": PEAK_FP32 / 1e12,
-                     "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": traffic,
-                     "alg_flops_per_launch": fl[dom] * nchunk_heads},
+        "roofline": roof,
         "cpu_baseline": cpu,
     }), flush=True)
 
