@@ -76,8 +76,9 @@ typedef struct {
  * and Linear weights [out, in], as in the "KDAChunkwise" docs' projections),
  * row strides lda, ldb, ldc in elements. c_dtype is KDA_DTYPE_BF16 (rounded to
  * nearest even) or KDA_DTYPE_F32. Device pointers; A and B 16-byte aligned with
- * K, lda and ldb multiples of 8; C must not overlap A or B. Asynchronous on
- * `stream`, no allocation; errors as for the other entry points. */
+ * K, lda and ldb multiples of 8 and lda, ldb <= 2^21 (KDA_ERR_UNSUPPORTED
+ * beyond); C must not overlap A or B. Asynchronous on `stream`, no allocation;
+ * errors as for the other entry points. */
 kda_status kda_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                             int64_t ldb, void* C, int64_t ldc, int32_t c_dtype, hipStream_t stream);
 

@@ -265,6 +265,10 @@ kda_status kda_gemm_bf16_nt(int64_t M, int64_t N, int64_t K, const void* A, int6
   if (M == 0 || N == 0) return KDA_OK;
   if (K % 8 || lda % 8 || ldb % 8 || lda < K || ldb < K || ldc < N)
     return fail_msg(KDA_ERR_INVALID_ARG, "K, lda, ldb must be multiples of 8 with lda, ldb >= K and ldc >= N");
+  // the kernel addresses a 256-row operand tile through a buffer resource with
+  // 32-bit byte offsets (up to 512 lda bytes)
+  if (lda > ((int64_t)1 << 21) || ldb > ((int64_t)1 << 21))
+    return fail_msg(KDA_ERR_UNSUPPORTED, "lda and ldb must be at most 2^21 elements");
   if (!A || !B || !C) return fail_msg(KDA_ERR_INVALID_ARG, "A, B and C must be non-NULL");
   if (reinterpret_cast<uintptr_t>(A) % 16 || reinterpret_cast<uintptr_t>(B) % 16 ||
       reinterpret_cast<uintptr_t>(C) % (c_dtype == KDA_DTYPE_F32 ? 4 : 2))

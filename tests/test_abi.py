@@ -363,3 +363,27 @@ def test_validate_report_layout_matches_header():
     assert ctypes.sizeof(_lib.KdaInputReport) == 48
     assert int(re.search(r"#define KDA_VALIDATE_SCRATCH_BYTES (\d+)", text).group(1)) == \
         _lib.KDA_VALIDATE_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(K=12), 1, b"multiples of 8"),
+    (dict(lda=4), 1, b"multiples of 8"),
+    (dict(ldc=3), 1, b"ldc >= N"),
+    (dict(lda=(1 << 21) + 8), 2, b"2^21"),
+    (dict(ldb=(1 << 22)), 2, b"2^21"),
+    (dict(c_dtype=7), 1, b"c_dtype"),
+    (dict(A=None), 1, b"non-NULL"),
+    (dict(A=(1 << 24) + 8), 1, b"16-byte"),
+])
+def test_gemm_rejects_bad_arguments_before_launch(lib, kw, status, msg):
+    """kda_gemm_bf16_nt checks shapes, strides (the kernel's 32-bit buffer
+    offsets bound lda and ldb by 2^21), dtype, NULL and alignment on the host
+    and launches nothing when a check fails (every case here fails one, so the
+    fake addresses never reach a device)."""
+    a = dict(M=300, N=200, K=64, A=1 << 24, lda=64, B=1 << 25, ldb=64, C=1 << 26, ldc=200, c_dtype=1)
+    a.update(kw)
+    vp = lambda x: None if x is None else ctypes.c_void_p(x)
+    st = lib.kda_gemm_bf16_nt(a["M"], a["N"], a["K"], vp(a["A"]), a["lda"], vp(a["B"]), a["ldb"], vp(a["C"]),
+                              a["ldc"], a["c_dtype"], None)
+    assert st == status, lib.kda_last_error()
+    assert msg in lib.kda_last_error()
