@@ -203,7 +203,8 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
   L->HD = p->H * p->D;
   // P's row stride, padded to 8 columns so that every row starts 16-byte aligned
   L->NP = (int)((3 * (int64_t)L->HD + p->H + p->gate_rank + p->out_gate_rank + 7) / 8 * 8);
-  if (L->BT > INT32_MAX / 2 || (int64_t)L->NP * p->M > INT32_MAX || (int64_t)L->HD > 65536)
+  if (L->BT > INT32_MAX / 2 || (int64_t)L->NP * p->M > INT32_MAX || (int64_t)L->HD > 65536 || p->M > (1 << 21) ||
+      p->gate_rank > (1 << 21) || p->out_gate_rank > (1 << 21))
     return fail_msg(KDA_ERR_UNSUPPORTED, "layer too large for 32-bit GEMM sizes");
   kda_fwd_params c = core_params(p);
   size_t cb = 0;
