@@ -18,8 +18,10 @@
  *
  * Implementation: every step runs in this library's HIP kernels: the
  * projections on its bf16 MFMA GEMM (fp32 accumulation, kda_gemm_bf16_nt),
- * conv + SiLU + L2 norm, the gate and beta activations and the RMSNorm /
- * output gate in elementwise kernels, and the core on the same two-kernel
+ * conv + SiLU + L2 norm and beta in an elementwise kernel, the decay-gate
+ * activation inside the core's first stage, the RMSNorm and output gate in the
+ * epilogue of the output-gate up-projection GEMM (the gate factor rounded to
+ * fp16 before it scales the normalised o), and the core on the same two-kernel
  * path as kda_chunk_fwd with fp32 q, k, v, g and beta.
  *
  * Conventions:

@@ -53,6 +53,9 @@ constexpr int kGemmThreads = 256;
 constexpr int kGroupM = 8, kGroupN = 4;   // tiles per XCD block
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ floatx4 zero4f() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx16 zero16() {
@@ -70,7 +73,22 @@ template <>
 __device__ __forceinline__ void store_out<bf16>(bf16* p, float v) { *p = (bf16)v; }
 // KTAIL: K is not a multiple of 64 and the chunks past K are zeroed by selects
 // (without it the loop carries no select between a load and its LDS write)
-template <typename TC, bool KTAIL>
+// sum of x over the D / 8 consecutive lanes of a (row, head) group (D = 64 or
+// 128), on data-parallel-primitive moves inside a 16-lane row: swaps of lane
+// pairs and pairs of pairs within each quad, then the mirror within each half
+// row (pairs quad 0 with 1, 2 with 3) and, for 16 lanes, the mirror within the
+// row (pairs the halves); every lane of the group ends with the group's sum
+__device__ __forceinline__ float head_sum(float x, int d) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  if (d == 128)
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  return x;
+}
+
+// NORM: the output-gate epilogue (bf16 C only, see kda_gemm.h)
+template <typename TC, bool KTAIL, bool NORM = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs a) {
   // LDS buffer b: A slice at smem[b][0, 32 KB), B slice at smem[b][32 KB, 64 KB)
   __shared__ __attribute__((aligned(16))) char smem[2][(kBM + kBN) * kBK * 2];
@@ -300,13 +318,74 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
           for (int g = 0; g < 4; ++g) {
             const int byte = (32 * y + 8 * g + 4 * og) * 2;
             const floatx16& c = acc[x][y];
-            bf16x4 o;
-            o[0] = (bf16)c[4 * g]; o[1] = (bf16)c[4 * g + 1]; o[2] = (bf16)c[4 * g + 2]; o[3] = (bf16)c[4 * g + 3];
-            *reinterpret_cast<bf16x4*>(q + rw * 256 + (((byte >> 4) ^ (rw & 15)) << 4) + (byte & 15)) = o;
+            char* dst = q + rw * 256 + (((byte >> 4) ^ (rw & 15)) << 4) + (byte & 15);
+            if constexpr (NORM) {
+              // the gate factor sigmoid(G) in (0, 1), staged as fp16 (2^-11 relative)
+              half4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (_Float16)(1.f / (1.f + __expf(-c[4 * g + e])));
+              *reinterpret_cast<half4*>(dst) = o;
+            } else {
+              bf16x4 o;
+              o[0] = (bf16)c[4 * g]; o[1] = (bf16)c[4 * g + 1]; o[2] = (bf16)c[4 * g + 2]; o[3] = (bf16)c[4 * g + 3];
+              *reinterpret_cast<bf16x4*>(dst) = o;
+            }
           }
       }
       // the quadrant region is this wave's own: an LDS wait orders the reads
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if constexpr (NORM) {
+        // 32 row pieces of 8 columns per lane, piece i at row 4 i + lane / 16;
+        // the D / 8 lanes of a (row, head) are consecutive, so the head's sum of
+        // squares is a reduction over them (N is a multiple of D: a head lies
+        // wholly inside or past N). o is read in groups of 4 pieces, each group
+        // loaded while the one before it is normalised and stored.
+        constexpr int GP = 4, NG = 32 / GP;
+        floatx4 ob[2][GP][2];
+        auto load_o = [&](int gi, floatx4 (&dst)[GP][2]) {
+#pragma unroll
+          for (int i3 = 0; i3 < GP; ++i3) {
+            const int rw = 4 * (gi * GP + i3) + (lane >> 4), ch = lane & 15;
+            const int64_t row = m0 + wm * 128 + rw, col = n0 + wn * 128 + ch * 8;
+            dst[i3][0] = zero4f();
+            dst[i3][1] = zero4f();
+            if (row < a.M && col < a.N) {
+              dst[i3][0] = *reinterpret_cast<const floatx4*>(a.norm_o + row * a.ldo + col);
+              dst[i3][1] = *reinterpret_cast<const floatx4*>(a.norm_o + row * a.ldo + col + 4);
+            }
+          }
+        };
+        load_o(0, ob[0]);
+        // a lane's 8 channels are the same in every piece: n0 and wn 128 are
+        // multiples of D, so the channel of column 8 ch + e is (8 ch + e) % D
+        const int d0 = (8 * (lane & 15)) % a.norm_d;
+        float nw[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) nw[e] = a.norm_w[d0 + e];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi) {
+          if (gi + 1 < NG) load_o(gi + 1, ob[(gi + 1) & 1]);
+#pragma unroll
+          for (int i3 = 0; i3 < GP; ++i3) {
+            const int rw = 4 * (gi * GP + i3) + (lane >> 4), ch = lane & 15;
+            const int64_t row = m0 + wm * 128 + rw, col = n0 + wn * 128 + ch * 8;
+            const half8 gt = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(
+                                                           q + rw * 256 + ((ch ^ (rw & 15)) << 4)));
+            float ov[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { ov[e] = ob[gi & 1][i3][0][e]; ov[4 + e] = ob[gi & 1][i3][1][e]; }
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += ov[e] * ov[e];
+            const float inv = 1.f / sqrtf(head_sum(ss, a.norm_d) / (float)a.norm_d + a.norm_eps);
+            bf16x8 yv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yv[e] = (bf16)(ov[e] * inv * nw[e] * (float)gt[e]);
+            if (row < a.M && col < a.N) *reinterpret_cast<bf16x8*>(C + row * a.ldc + col) = yv;
+          }
+        }
+        return;
+      }
 #pragma unroll
       for (int i0 = 0; i0 < 32; i0 += 8) {
         u32x4 rv[8];
@@ -363,6 +442,14 @@ hipError_t launch_gemm_bf16(const GemmArgs& a0, int out_f32, hipStream_t s) {
   const int nblk8 = (nbm * nbn + 7) / 8 * 8;   // blocks, padded to whole rounds of 8 XCDs
   const dim3 grid((unsigned)(nblk8 * kGroupM * kGroupN)), block(kGemmThreads);
   const bool ktail = a.K % kBK != 0;
+  if (a.norm_o) {
+    if (out_f32 || !a.vec_out || !a.norm_w || !(a.norm_d == 64 || a.norm_d == 128) || a.N % a.norm_d ||
+        a.ldo % 8 || reinterpret_cast<uintptr_t>(a.norm_o) % 16)
+      return hipErrorInvalidValue;
+    if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, false, true>), grid, block, 0, s, a);
+    return hipGetLastError();
+  }
   if (out_f32) {
     if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<float, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((gemm_bf16_nt_kernel<float, false>), grid, block, 0, s, a);

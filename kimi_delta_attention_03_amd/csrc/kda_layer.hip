@@ -13,8 +13,8 @@
 //   5. core: the two-kernel chunkwise forward on fp32 q, k, v, beta with the
 //      decay g = lb * sigmoid(exp(A_log_h) (g_raw + dt_bias)) applied inside
 //      stage 1+2 (no separate pass over g)
-//   6. Gu   = P_g Wgu^T                    GEMM -> fp32 [BT, HD]
-//   7. norm kernel: y = RMSNorm_D(o) * norm_w * sigmoid(Gu) -> bf16 (in P's space)
+//   6+7. y = RMSNorm_D(o) * norm_w * sigmoid(P_g Wgu^T) -> bf16 [BT, HD]: one
+//      GEMM whose epilogue applies the norm and the gate
 //   8. x_new = y Wo^T                      GEMM, bf16 x bf16 -> bf16 [BT, M]
 // The projections run on this library's MFMA GEMM (kda_gemm.hip); every other
 // step is a kernel of this file or of the core. The elementwise kernels are HBM-bound: each reads
@@ -134,42 +134,12 @@ __global__ __launch_bounds__(kLayerThreads) void layer_prologue_kernel(PrologueA
   }
 }
 
-// y = o / sqrt(mean_D(o^2) + eps) * norm_w * sigmoid(gate), one wave per (token, head)
-template <int D>
-__global__ __launch_bounds__(kLayerThreads) void layer_norm_gate_kernel(const float* o, const float* gate,
-                                                                        const float* norm_w, uint16_t* y,
-                                                                        int64_t nwaves, float eps) {
-  constexpr int CPL = D / kWave;
-  const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * (kLayerThreads / kWave) + (threadIdx.x >> 6);
-  if (wid >= nwaves) return;
-  const size_t base = (size_t)wid * D + CPL * lane;  // o, gate and y share the [BT, H, D] order
-  float x[CPL], gt[CPL];
-  if constexpr (CPL == 2) {
-    const float2 a = *reinterpret_cast<const float2*>(o + base);
-    const float2 b = *reinterpret_cast<const float2*>(gate + base);
-    x[0] = a.x; x[1] = a.y; gt[0] = b.x; gt[1] = b.y;
-  } else {
-    x[0] = o[base];
-    gt[0] = gate[base];
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) ss += x[j] * x[j];
-  const float inv = 1.f / sqrtf(wave_sum(ss) / D + eps);
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const float v = x[j] * inv * norm_w[CPL * lane + j] * sigmoidf_(gt[j]);
-    y[base + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
-  }
-}
-
 // ------------------------------------------------------------------ host side
 
 struct LayerLayout {
   int64_t BT;
   int HD, NP;
-  size_t off_wcat, off_P, off_q, off_k, off_v, off_g, off_beta, off_o, off_gu, off_core, total;
+  size_t off_wcat, off_P, off_q, off_k, off_v, off_g, off_beta, off_o, off_y, off_core, total;
   size_t core_bytes;
 };
 
@@ -224,7 +194,7 @@ kda_status check_layer(const kda_layer_params* p, LayerLayout* L) {
   L->off_g = take(BT * HD * 4);
   L->off_beta = take(BT * p->H * 4);
   L->off_o = take(BT * HD * 4);
-  L->off_gu = take(BT * HD * 4);          // output-gate projection [BT, HD] fp32
+  L->off_y = take(BT * HD * 2);           // y [BT, HD] bf16, the output projection's input
   L->off_core = take(cb);
   L->total = off;
   return KDA_OK;
@@ -380,23 +350,21 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
                             stream);
     if (s != KDA_OK) return s;
   }
-  // 6. output-gate up projection,
-  // 7. RMSNorm * gate -> y (bf16, in P's space: P is dead once both up projections have read it)
-  float* gu = reinterpret_cast<float*>(ws + L.off_gu);
-  s = gemm_nt(w->Wgu, rg, P + off_r + r, NP, gu, HD, true, HD, BT, rg, stream, "output gate");
-  if (s != KDA_OK) return s;
-  uint16_t* y = P;
+  // 6-7. output-gate up projection fused with RMSNorm * gate -> y (bf16): the
+  // GEMM's epilogue reads o and writes y = RMSNorm_D(o) * norm_w *
+  // sigmoid(P_g Wgu^T) into a buffer of its own, so y never overlaps P, which
+  // the same GEMM is still reading (o's rows are 16-byte aligned: the core has
+  // checked them)
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.off_y);
   {
-    const int64_t nw = (int64_t)BT * H;
-    const int wpb = kLayerThreads / kWave;
-    const dim3 grid((unsigned)((nw + wpb - 1) / wpb));
-    if (D == 128)
-      hipLaunchKernelGGL(layer_norm_gate_kernel<128>, grid, dim3(kLayerThreads), 0, stream, o, gu, w->norm_w, y, nw,
-                         p->norm_eps);
-    else
-      hipLaunchKernelGGL(layer_norm_gate_kernel<64>, grid, dim3(kLayerThreads), 0, stream, o, gu, w->norm_w, y, nw,
-                         p->norm_eps);
-    if (hipGetLastError() != hipSuccess) return fail_msg(KDA_ERR_HIP, "norm launch failed");
+    GemmArgs g{};
+    g.A = P + off_r + r; g.lda = NP;
+    g.B = w->Wgu; g.ldb = rg;
+    g.C = y; g.ldc = HD;
+    g.M = BT; g.N = HD; g.K = rg;
+    g.norm_o = o; g.ldo = HD; g.norm_w = w->norm_w; g.norm_d = D; g.norm_eps = p->norm_eps;
+    const hipError_t e = launch_gemm_bf16(g, 0, stream);
+    if (e != hipSuccess) return fail_msg(KDA_ERR_HIP, "GEMM (output gate + norm) launch: %s", hipGetErrorString(e));
   }
   // 8. x_new = y Wo^T
   return gemm_nt(w->Wo, HD, y, HD, x_new, M, false, M, BT, HD, stream, "output projection");

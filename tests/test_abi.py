@@ -161,7 +161,8 @@ def test_layer_workspace_formula(lib):
     core = make_params(2, 128, 2, 128, 128, 0, 0, 0, 128 ** -0.5)
     cb = ctypes.c_size_t(0)
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(core), ctypes.byref(cb)) == 0
-    want = (up(NP * 256 * 2) + up(BT * NP * 2) + 6 * up(BT * HD * 4) + up(BT * 2 * 4) + up(cb.value))
+    want = (up(NP * 256 * 2) + up(BT * NP * 2) + 5 * up(BT * HD * 4) + up(BT * 2 * 4) + up(BT * HD * 2) +
+            up(cb.value))
     assert n.value == want
     info = _lib.KdaLayerWorkspaceInfo()
     assert lib.kda_layer_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
