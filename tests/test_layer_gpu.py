@@ -57,6 +57,26 @@ def test_layer_small_matches_oracle(D):
     assert eo <= TOL_LAYER and ey <= TOL_LAYER
 
 
+@pytest.mark.parametrize("H,D", [(2, 128), (4, 64)])
+def test_layer_prologue_outputs_match_oracle(H, D):
+    """The core's inputs as the layer leaves them in its workspace (q, k, v after
+    conv, SiLU and, for q and k, the L2 norm; beta) against the oracle's
+    intermediates, with three sequences of 192 tokens, so the conv restarts
+    twice inside the 576 rows of the projection, and 4 heads of 64 channels or
+    2 of 128."""
+    B, T, M, r = 3, 192, 256, 32
+    _say(f"layer prologue outputs B={B} T={T} M={M} H={H} D={D} r={r}")
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, rank=r, seed=53 + D)
+    layer, y = run_layer(x, w, H, D)
+    ref, inter = orc.kda_layer_ref(x, w, H, D)
+    ci = layer.core_inputs()
+    ein = {n: rel_err(host(ci[n]), inter[n]) for n in ("q", "k", "v", "beta")}
+    eo = rel_err(host(layer.core_out), inter["o"])
+    ey = rel_err(host(y), ref)
+    _say("  rel err " + " ".join(f"{n}={e:.2e}" for n, e in ein.items()) + f" core o={eo:.2e} x_new={ey:.2e}")
+    assert all(e <= TOL_LAYER for e in ein.values()) and eo <= TOL_LAYER and ey <= TOL_LAYER
+
+
 def test_layer_deterministic_and_causal():
     """Bitwise-equal reruns; changing tokens after n leaves x_new[:, :n+1] unchanged."""
     import torch
