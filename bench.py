@@ -344,23 +344,25 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
     tp = os.path.join(ROOT, "profiles", f"traffic_kda_bwd_{WORKLOADS[args.workload]['name']}.json")
     if os.path.exists(tp):
         rec = json.load(open(tp))
+        chunk_mm = "bwd_chunk_mfma_kernel" if x.dtype == "bf16" else "bwd_chunk_mm_kernel"
         names = {"prep": ["bwd_prep_kernel"], "states_fwd": ["bwd_states_fwd_kernel"],
-                 "states_bwd": ["bwd_states_bwd_kernel"], "chunk": ["bwd_chunk_mm_kernel", "bwd_chunk_elem_kernel"]}
+                 "states_bwd": ["bwd_states_bwd_kernel"], "chunk": [chunk_mm, "bwd_chunk_elem_kernel"]}
         if rec.get("source_sha256_16") == kernel_source_hash("bwd") and all(n in rec["kernels"] for n in names[dom]):
             traffic = sum(rec["kernels"][n]["traffic_bytes"] for n in names[dom])
     ach = fl[dom] * nchunk_heads / (stage_ms[dom] / 1e3) / 1e12
     if dom == "chunk":
-        # the chunk pair streams its operands and results through the fp32 slab:
-        # it is bound by memory traffic, so its roofline is HBM on the bytes it
-        # cannot avoid (see bwd_chunk_alg_bytes_per_token_head), with the
-        # measured bytes beside them
+        # the chunk pair streams its operands and results through the fp32 slab
+        # (its products run on MFMA for bf16 inputs): it is bound by memory
+        # traffic, so its roofline is HBM on the bytes it cannot avoid (see
+        # bwd_chunk_alg_bytes_per_token_head), with the measured bytes beside them
         ntok_heads = (int(x.cu_seqlens[-1]) if cu is not None else B * T) * H
         alg_b = bwd_chunk_alg_bytes_per_token_head(K, V, 2 if x.dtype == "bf16" else 4) * ntok_heads
         gbps = alg_b / (stage_ms[dom] / 1e3) / 1e9
-        roof = {"kernel": "bwd_chunk (chunk_mm + chunk_elem)", "bound": "hbm", "achieved": gbps,
+        pair = "chunk_mfma" if x.dtype == "bf16" else "chunk_mm"
+        roof = {"kernel": f"bwd_chunk ({pair} + chunk_elem)", "bound": "hbm", "achieved": gbps,
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbps * 1e9 / PEAK_HBM, "traffic": traffic,
                 "alg_bytes_per_launch": alg_b, "traffic_over_alg": None if traffic is None else traffic / alg_b,
-                "alu_TFLOPs": ach, "alu_frac_fp32": ach * 1e12 / PEAK_FP32}
+                "flop_rate_TFLOPs": ach}
     else:
         roof = {"kernel": f"bwd_{dom}", "bound": "alu", "achieved": ach, "peak": PEAK_FP32 / 1e12,
                 "unit": "TFLOP/s", "frac": ach * 1e12 / PEAK_FP32, "traffic": traffic,
@@ -369,7 +371,9 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
         "metric": "KDA chunk-bwd tokens/s (dq, dk, dv, dg, dbeta, dh0)", "value": B * T / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": f"{x.dtype} inputs, f32 arithmetic and gradients", "data": "synthetic (seeded numpy generators)",
+        "dtype": ("bf16 inputs; chunk products on bf16 MFMA operands with f32 accumulation; f32 states and gradients"
+                  if x.dtype == "bf16" else "f32 inputs, f32 arithmetic and gradients"),
+        "data": "synthetic (seeded numpy generators)",
         "config": {"workload": WORKLOADS[args.workload]["name"] + "_backward", "B": B, "T": T, "H": H, "K": K,
                    "V": V},
         "stage_ms": stage_ms,

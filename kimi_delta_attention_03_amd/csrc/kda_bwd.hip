@@ -866,6 +866,391 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
                             [&](int i, int j, float x) { P.DL[i * C + j] = j < i ? -x : 0.f; });
 }
 
+// ------------------------------------------- chunk products on MFMA (bf16 input)
+// With bf16 q, k, v (and dO) the products above run on v_mfma_f32_16x16x32_bf16:
+// every operand is rounded to bf16 (the input compute dtype, as in the forward's
+// bf16 path) and every product accumulates in fp32. One workgroup (8 waves) per
+// (chunk, head) keeps all operands and intermediates of the item in LDS, so the
+// slab is read once (S, dS', W, U, KG, Kb, Vb, Aqk, A) and only the gradients
+// the elementwise kernel needs are written back; Vn, dVn, dW, dA and T1 never
+// leave the chip.
+//
+// An operand matrix sits in LDS with its reduction index contiguous: the
+// A operand as [output row][reduction], the B operand as [output column]
+// [reduction], rows padded by 8 elements (16 bytes) so that the 16 rows read by
+// one b128 access fall into distinct banks. Lane (g, i) supplies reduction
+// indices 32 s + 8 g .. + 7 of row i in step s, for both operands. Products
+// that leave their result as an A operand, or in global memory, are issued with
+// the operands swapped (lane (g, i) then holds row i, columns 4 g .. 4 g + 3 of
+// the result); the others keep the MFMA's own layout (rows 4 g .. 4 g + 3,
+// column i), which stores transposed with one 8-byte write per lane.
+//
+// Phases (operands staged from registers loaded one or more phases earlier):
+//   1  Vn = U - W S                               (W, S^T)
+//   2  dVn = Aqk^T dO + KG dS'                    (Aqk^T, dO^T, KG, dS'^T)
+//   3  dKG = Vn dS'^T;  dgamma = rowsum(S * dS')  (dS')
+//   4  dQg = dO S^T, dW = -dVn S^T, dAqk = Tril(dO Vn^T)   (dO, S)
+//   5  dA = dW Kb^T + dVn Vb^T, dKb = A^T dW, dVb = A^T dVn (Kb, Vb, A^T)
+//   6  T1 = A^T dA                                (A staged for phase 7)
+//   7  dL = -StrictTril(T1 A^T)
+constexpr int kMT = 512;  // threads of the MFMA product kernel
+
+// output tiles of an M x N product over 8 waves: each wave a BM x BN block of
+// 16 x 16 tiles
+template <int M, int N>
+struct MTiles {
+  static constexpr int TM = M / 16, TN = N / 16, TPW = TM * TN / 8;
+  static constexpr int BM = TPW >= 4 ? 2 : 1, BN = TPW / BM, WC = TN / BN;
+  static_assert(BM * BN == TPW && (TM / BM) * WC == 8, "8 waves of whole tile blocks");
+  __device__ static int r0(int w) { return 16 * BM * (w / WC); }
+  __device__ static int c0(int w) { return 16 * BN * (w % WC); }
+};
+
+// acc[bm][bn] += sum over R reduction indices of A-row x B-row, for the wave's
+// tile block at (r0, c0); SWAP issues the MFMA with the operands exchanged
+template <int BM, int BN, int R, bool SWAP>
+__device__ __forceinline__ void mfma_rows(floatx4 (&acc)[BM][BN], const bf16* A, int lda, const bf16* B, int ldb,
+                                          int r0, int c0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+  for (int s = 0; s < R; s += 32) {
+    bf16x8 fa[BM], fb[BN];
+#pragma unroll
+    for (int bm = 0; bm < BM; ++bm) fa[bm] = *reinterpret_cast<const bf16x8*>(A + (r0 + 16 * bm + i) * lda + s + 8 * g);
+#pragma unroll
+    for (int bn = 0; bn < BN; ++bn) fb[bn] = *reinterpret_cast<const bf16x8*>(B + (c0 + 16 * bn + i) * ldb + s + 8 * g);
+#pragma unroll
+    for (int bm = 0; bm < BM; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < BN; ++bn)
+        acc[bm][bn] = SWAP ? mma32(acc[bm][bn], fb[bn], fa[bm]) : mma32(acc[bm][bn], fa[bm], fb[bn]);
+  }
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ void zero_acc(floatx4 (&acc)[BM][BN]) {
+#pragma unroll
+  for (int bm = 0; bm < BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < BN; ++bn) acc[bm][bn] = zero4();
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) { return __builtin_convertvector(x, bf16x4); }
+
+// fp32 [ROWS][COLS] matrix (row-major, global) <-> registers, 4 consecutive
+// elements per access; thread t takes groups t, t + kMT, ...
+template <int ROWS, int COLS>
+struct NatStage {
+  static constexpr int N = ROWS * COLS / 4 / kMT;
+  static_assert(N >= 1 && N * 4 * kMT == ROWS * COLS, "whole groups per thread");
+  floatx4 v[N];
+  __device__ void load(const float* src) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      const int e = (int)threadIdx.x + kMT * m, row = e / (COLS / 4), c = 4 * (e % (COLS / 4));
+      v[m] = *reinterpret_cast<const floatx4*>(src + row * COLS + c);
+    }
+  }
+  // bf16 [ROWS][COLS + 8] in LDS
+  __device__ void store(bf16* dst) const {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      const int e = (int)threadIdx.x + kMT * m, row = e / (COLS / 4), c = 4 * (e % (COLS / 4));
+      *reinterpret_cast<bf16x4*>(dst + row * (COLS + 8) + c) = to_bf16x4(v[m]);
+    }
+  }
+};
+
+// fp32 [ROWS][COLS] matrix in 4 x 4 blocks: block b = t + kMT m holds rows
+// 4 (b / (COLS / 4)) + r, columns 4 (b % (COLS / 4)) .. + 3 in v[m][r]; stored
+// to LDS either as is or transposed ([COLS][ROWS + 8])
+template <int ROWS, int COLS>
+struct BlkStage {
+  static constexpr int NB = (ROWS / 4) * (COLS / 4);
+  static constexpr int N = (NB + kMT - 1) / kMT;
+  floatx4 v[N][4];
+  __device__ static bool has(int m) { return NB % kMT == 0 || (int)threadIdx.x + kMT * m < NB; }
+  __device__ static int brow(int m) { return 4 * (((int)threadIdx.x + kMT * m) / (COLS / 4)); }
+  __device__ static int bcol(int m) { return 4 * (((int)threadIdx.x + kMT * m) % (COLS / 4)); }
+  __device__ void load(const float* src) {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (has(m)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[m][r] = *reinterpret_cast<const floatx4*>(src + (brow(m) + r) * COLS + bcol(m));
+      }
+  }
+  __device__ void store(bf16* dst) const {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (has(m)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<bf16x4*>(dst + (brow(m) + r) * (COLS + 8) + bcol(m)) = to_bf16x4(v[m][r]);
+      }
+  }
+  __device__ void store_t(bf16* dst) const {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (has(m)) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<bf16x4*>(dst + (bcol(m) + c) * (ROWS + 8) + brow(m)) =
+              to_bf16x4(floatx4{v[m][0][c], v[m][1][c], v[m][2][c], v[m][3][c]});
+      }
+  }
+};
+
+template <int K>
+__global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
+  constexpr int V = K;
+  constexpr int PK = K + 8, PC = C + 8;      // LDS row pitches (elements)
+  constexpr int CK = C * PK, KK = K * PK, KC = K * PC, CCS = C * PC;  // matrix sizes (elements)
+  // LDS plan (elements): Vn, dVn, dVn^T stay from their phase to their last use;
+  // the operand area Q is re-laid out per phase; dA^T, T1 and A reuse the space
+  // of Vn and dVn once those are dead
+  constexpr int oVn = 0, odVn = CK, odVnT = 2 * CK, oQ = 2 * CK + KC;
+  constexpr int oW = oQ, oST = oQ + CK;                                   // phase 1
+  constexpr int oAqT = oQ, odOT = oQ + CCS, oKG = odOT + KC, odST = oKG + CK;  // phase 2
+  constexpr int odS = oQ;                                                 // phase 3
+  constexpr int odW = oQ, odWT = oQ + CK, odO = odWT + KC, oS = odO + CK;     // phase 4
+  constexpr int oKb = odO, oVb = oKb + CK, oAT = oVb + CK;                // phase 5
+  constexpr int odAT = 0, oT1 = CCS, oA = 2 * CCS;                         // phases 5-7
+  constexpr int kElems = (oS + KK > oAT + CCS ? oS + KK : oAT + CCS) > odST + KK
+                             ? (oS + KK > oAT + CCS ? oS + KK : oAT + CCS)
+                             : odST + KK;
+  static_assert(oA + CCS <= odVnT + KC, "LDS plan");
+  static_assert(oT1 + CCS <= oQ && odAT + CCS <= odVn, "phase 5-7 results over dead matrices");
+  __shared__ __attribute__((aligned(16))) bf16 smem[kElems];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, i = lane & 15;
+  if ((int)blockIdx.x >= items_in_use(a)) return;
+  const ItemB it = chunk_of(a, (int)blockIdx.x / a.H, (int)blockIdx.x % a.H);
+  const SlabPtrs P = slab_ptrs(slab_of(a, it.p, it.h), a.sl);
+
+  using TCV = MTiles<C, V>;   // C x V and C x K results (K == V)
+  using TCC = MTiles<C, C>;
+  floatx4 acc[TCV::BM][TCV::BN];
+  floatx4 acc2[TCC::BM][TCC::BN];
+
+  // ---- loads of phase 1, and the state S (kept in registers until phase 4)
+  NatStage<C, K> rW;
+  BlkStage<K, V> rS;
+  rW.load(P.W);
+  rS.load(P.S);
+  floatx4 rU[TCV::BM][TCV::BN];
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      rU[bm][bn] = *reinterpret_cast<const floatx4*>(P.U + (TCV::r0(w) + 16 * bm + i) * V + TCV::c0(w) + 16 * bn + 4 * g);
+
+  // ---- phase 1: Vn = U - W S
+  rW.store(smem + oW);
+  rS.store_t(smem + oST);
+  // loads of phase 2: Aqk, dO (bf16 rows of the chunk, zero past its end), KG, dS'
+  BlkStage<C, C> rAq;
+  rAq.load(P.AQK);
+  constexpr int NDO = (C / 4) * (V / 4), PDO = (NDO + kMT - 1) / kMT;
+  bf16x4 rdO[PDO][4];
+  auto do_has = [&](int m) { return NDO % kMT == 0 || tid + kMT * m < NDO; };
+  auto do_row = [&](int m) { return 4 * ((tid + kMT * m) / (V / 4)); };
+  auto do_col = [&](int m) { return 4 * ((tid + kMT * m) % (V / 4)); };
+  {
+    const bf16* dO = reinterpret_cast<const bf16*>(a.d_o);
+#pragma unroll
+    for (int m = 0; m < PDO; ++m)
+      if (do_has(m)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = do_row(m) + r, rr = row < it.len ? row : 0;
+          rdO[m][r] = *reinterpret_cast<const bf16x4*>(dO + ((size_t)(it.tok0 + rr) * a.H + it.h) * V + do_col(m));
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (do_row(m) + r >= it.len) rdO[m][r] = bf16x4{0, 0, 0, 0};
+      }
+  }
+  NatStage<C, K> rKG;
+  rKG.load(P.KG);
+  BlkStage<K, V> rdS;
+  rdS.load(P.DS);
+  __syncthreads();
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, K, true>(acc, smem + oW, PK, smem + oST, PK, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      *reinterpret_cast<bf16x4*>(smem + oVn + (TCV::r0(w) + 16 * bm + i) * PK + TCV::c0(w) + 16 * bn + 4 * g) =
+          to_bf16x4(rU[bm][bn] - acc[bm][bn]);
+  __syncthreads();
+
+  // ---- phase 2: dVn = Aqk^T dO + KG dS'
+  rAq.store_t(smem + oAqT);
+#pragma unroll
+  for (int m = 0; m < PDO; ++m)
+    if (do_has(m)) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<bf16x4*>(smem + odOT + (do_col(m) + c) * PC + do_row(m)) =
+            bf16x4{rdO[m][0][c], rdO[m][1][c], rdO[m][2][c], rdO[m][3][c]};
+    }
+  rKG.store(smem + oKG);
+  rdS.store_t(smem + odST);
+  // loads of phase 5
+  NatStage<C, K> rKb, rVb;
+  rKb.load(P.KB);
+  rVb.load(P.VB);
+  BlkStage<C, C> rA;
+  rA.load(P.A);
+  __syncthreads();
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, C, false>(acc, smem + oAqT, PC, smem + odOT, PC, TCV::r0(w), TCV::c0(w), lane);
+  mfma_rows<TCV::BM, TCV::BN, K, false>(acc, smem + oKG, PK, smem + odST, PK, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn) {
+      const int R0 = TCV::r0(w) + 16 * bm, C0 = TCV::c0(w) + 16 * bn;
+      const bf16x4 y = to_bf16x4(acc[bm][bn]);
+      *reinterpret_cast<bf16x4*>(smem + odVnT + (C0 + i) * PC + R0 + 4 * g) = y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) smem[odVn + (R0 + 4 * g + r) * PK + C0 + i] = y[r];
+    }
+  __syncthreads();
+
+  // ---- phase 3: dKG = Vn dS'^T, dgamma = rowsum(S * dS')
+  rdS.store(smem + odS);
+#pragma unroll
+  for (int m = 0; m < BlkStage<K, V>::N; ++m) {
+    floatx4 part = zero4();
+    if (BlkStage<K, V>::has(m)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const floatx4 pr = rS.v[m][r] * rdS.v[m][r];
+        part[r] = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      }
+    }
+    // the V / 4 lanes of one block row are consecutive (V / 4 divides 64)
+#pragma unroll
+    for (int off = 1; off < V / 4; off <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] += __shfl_xor(part[r], off, 64);
+    if (BlkStage<K, V>::has(m) && BlkStage<K, V>::bcol(m) == 0)
+      *reinterpret_cast<floatx4*>(P.DGAM + BlkStage<K, V>::brow(m)) = part;
+  }
+  __syncthreads();
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, V, true>(acc, smem + oVn, PK, smem + odS, PK, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      *reinterpret_cast<floatx4*>(P.DKG + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+  __syncthreads();
+
+  // ---- phase 4: dQg = dO S^T, dW = -dVn S^T, dAqk = Tril(dO Vn^T)
+#pragma unroll
+  for (int m = 0; m < PDO; ++m)
+    if (do_has(m)) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<bf16x4*>(smem + odO + (do_row(m) + r) * PK + do_col(m)) = rdO[m][r];
+    }
+  rS.store(smem + oS);
+  __syncthreads();
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, V, true>(acc, smem + odO, PK, smem + oS, PK, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      *reinterpret_cast<floatx4*>(P.DQG + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, V, false>(acc, smem + odVn, PK, smem + oS, PK, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn) {
+      const int R0 = TCV::r0(w) + 16 * bm, C0 = TCV::c0(w) + 16 * bn;
+      const bf16x4 y = to_bf16x4(-acc[bm][bn]);
+      *reinterpret_cast<bf16x4*>(smem + odWT + (C0 + i) * PC + R0 + 4 * g) = y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) smem[odW + (R0 + 4 * g + r) * PK + C0 + i] = y[r];
+    }
+  zero_acc(acc2);
+  mfma_rows<TCC::BM, TCC::BN, V, true>(acc2, smem + odO, PK, smem + oVn, PK, TCC::r0(w), TCC::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn) {
+      const int row = TCC::r0(w) + 16 * bm + i, col = TCC::c0(w) + 16 * bn + 4 * g;
+      floatx4 y = acc2[bm][bn];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = col + r <= row ? y[r] : 0.f;
+      *reinterpret_cast<floatx4*>(P.DAQK + row * C + col) = y;
+    }
+  __syncthreads();
+
+  // ---- phase 5: dA = dW Kb^T + dVn Vb^T (kept as dA^T), dKb = A^T dW, dVb = A^T dVn
+  rKb.store(smem + oKb);
+  rVb.store(smem + oVb);
+  rA.store_t(smem + oAT);
+  __syncthreads();
+  zero_acc(acc2);
+  mfma_rows<TCC::BM, TCC::BN, K, false>(acc2, smem + odW, PK, smem + oKb, PK, TCC::r0(w), TCC::c0(w), lane);
+  mfma_rows<TCC::BM, TCC::BN, V, false>(acc2, smem + odVn, PK, smem + oVb, PK, TCC::r0(w), TCC::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn)
+      *reinterpret_cast<bf16x4*>(smem + odAT + (TCC::c0(w) + 16 * bn + i) * PC + TCC::r0(w) + 16 * bm + 4 * g) =
+          to_bf16x4(acc2[bm][bn]);
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, C, true>(acc, smem + oAT, PC, smem + odWT, PC, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      *reinterpret_cast<floatx4*>(P.DKB + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+  zero_acc(acc);
+  mfma_rows<TCV::BM, TCV::BN, C, true>(acc, smem + oAT, PC, smem + odVnT, PC, TCV::r0(w), TCV::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+      *reinterpret_cast<floatx4*>(P.DVB + (TCV::r0(w) + 16 * bm + i) * V + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+  __syncthreads();
+
+  // ---- phase 6: T1 = A^T dA (A staged for phase 7 over dead dVn / dVn^T)
+  rA.store(smem + oA);
+  zero_acc(acc2);
+  mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oAT, PC, smem + odAT, PC, TCC::r0(w), TCC::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn)
+      *reinterpret_cast<bf16x4*>(smem + oT1 + (TCC::r0(w) + 16 * bm + i) * PC + TCC::c0(w) + 16 * bn + 4 * g) =
+          to_bf16x4(acc2[bm][bn]);
+  __syncthreads();
+
+  // ---- phase 7: dL = -StrictTril(T1 A^T)
+  zero_acc(acc2);
+  mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oT1, PC, smem + oA, PC, TCC::r0(w), TCC::c0(w), lane);
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn) {
+      const int row = TCC::r0(w) + 16 * bm + i, col = TCC::c0(w) + 16 * bn + 4 * g;
+      floatx4 y;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = col + r < row ? -acc2[bm][bn][r] : 0.f;
+      *reinterpret_cast<floatx4*>(P.DL + row * C + col) = y;
+    }
+}
+
 // the elementwise and gated-sum rules, the L2-norm backward and the reverse
 // cumsum. The four gated sums (per row i, channel d; P = dAqk, dM = Diag(beta) dL,
 // E_ij = exp(G_i - G_j))
@@ -1122,7 +1507,8 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
     if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
   }
   if ((stages & 8) && nitems > 0) {
-    hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+    if (a.bf16_qkv) hipLaunchKernelGGL(bwd_chunk_mfma_kernel<K>, dim3(nitems), dim3(kMT), 0, s, a);
+    else hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
     hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
   }
   return hipGetLastError();

@@ -3,9 +3,9 @@ float64 oracle kda_recurrent_vjp, through the C ABI.
 
 Metric: max|gpu - oracle| / max|oracle| per gradient (dq, dk, dv, dg, dbeta,
 dh0). Bounds: 1e-4 for fp32 inputs and 2e-2 for bf16 inputs, the forward's
-bounds; the backward computes in fp32 throughout, so bf16 cases are in fact
-held to the same fp32-accumulation error as fp32 ones, and the tighter bound
-TOL_BF16_SEEN documents what they reach.
+bounds. With fp32 inputs the backward is fp32 throughout (≈1e-6); with bf16
+inputs its chunk products take bf16 operands with fp32 accumulation, as the
+forward's bf16 path does (≈1e-3 to 6e-3).
 """
 import sys
 
