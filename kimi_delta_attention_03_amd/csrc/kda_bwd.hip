@@ -800,7 +800,7 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
 // pointers to the slab arrays of one (chunk, head)
 struct SlabPtrs {
   float *QN, *KN, *G, *QG, *KG, *W, *KB, *U, *VB, *AQK, *A, *Mm, *BETA, *GAM, *S, *DS, *DO, *VN, *DVN, *DVB, *DQG,
-      *DW, *DKG, *DKB, *DQN, *DKN, *DG, *DAQK, *DA, *T1, *DL, *DGAM;
+      *DW, *DKG, *DKB, *DAQK, *DA, *T1, *DL, *DGAM;
 };
 __device__ __forceinline__ SlabPtrs slab_ptrs(float* sl, const BwdSlab& o) {
   SlabPtrs P;
@@ -808,7 +808,7 @@ __device__ __forceinline__ SlabPtrs slab_ptrs(float* sl, const BwdSlab& o) {
   P.KB = sl + o.kb; P.U = sl + o.u; P.VB = sl + o.vb; P.AQK = sl + o.aqk; P.A = sl + o.a; P.Mm = sl + o.m;
   P.BETA = sl + o.beta; P.GAM = sl + o.gam; P.S = sl + o.S; P.DS = sl + o.dS; P.DO = sl + o.dO; P.VN = sl + o.vn;
   P.DVN = sl + o.dvn; P.DVB = sl + o.dvb; P.DQG = sl + o.dqg; P.DW = sl + o.dw; P.DKG = sl + o.dkg;
-  P.DKB = sl + o.dkb; P.DQN = sl + o.dqn; P.DKN = sl + o.dkn; P.DG = sl + o.dG; P.DAQK = sl + o.daqk;
+  P.DKB = sl + o.dkb; P.DAQK = sl + o.daqk;
   P.DA = sl + o.da; P.T1 = sl + o.t1; P.DL = sl + o.dl; P.DGAM = sl + o.dgam;
   return P;
 }
@@ -1270,6 +1270,8 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float sG[C * K], sKN[C * K], sQN[C * K];
   __shared__ float sP[C * CP], sDM[C * CP];  // dAqk and dM = Diag(beta) dL
   __shared__ float sBeta[C], sDot[2 * C], sDGl[K];
+  __shared__ float sDotP[NCT * 2 * C];  // per channel tile row dots q^ . dq^, k^ . dk^
+  __shared__ float sBT[4 * K];          // 16-row block totals of dG
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1326,8 +1328,8 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   __syncthreads();
 
   // output tiles (row block ib, channel tile ct): wave w takes tiles w, w + 16, ...
-  // The per-element gradients each tile's epilogue needs are loaded up front, so
-  // that no load waits behind an earlier tile's stores.
+  // The per-element gradients each tile needs are loaded up front, so that no
+  // load waits behind an earlier tile's stores.
   constexpr int TPWE = 4 * NCT / kNWW;
   static_assert(TPWE >= 1 && TPWE * kNWW == 4 * NCT, "tile split");
   float pdqg[TPWE][4], pdkb[TPWE][4], pdkg[TPWE][4];
@@ -1342,6 +1344,10 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
       pdkg[t][r] = P.DKG[i * K + d];
     }
   }
+  // dq and dk leave from each tile (with the L2 flag as the gradients of the
+  // normalised rows, completed below); the within-tile reverse sums of dG stay
+  // in registers for dg
+  float sfx[TPWE][4];
 #pragma unroll
   for (int t = 0; t < TPWE; ++t) {
     const int tile = w + kNWW * t;
@@ -1392,16 +1398,61 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
       const float Gl = sG[(C - 1) * K + d];
       const float eg = __expf(Gi), egl = __expf(Gl - Gi);
       const float dqg = pdqg[t][r], dkb = pdkb[t][r], dkg = pdkg[t][r];
-      P.DQN[i * K + d] = s * eg * dqg + s * qa[r];
-      P.DKN[i * K + d] = dkb * bi * eg + dkg * egl + s * ka[r] + qm[r] + km[r];
+      const float gqn = s * eg * dqg + s * qa[r];
+      const float gkn = dkb * bi * eg + dkg * egl + s * ka[r] + qm[r] + km[r];
       // Qg = s q e^G, Kb = beta k e^G and KG = k e^(Gl - G) rebuilt from the staged rows
       float dG = dqg * (s * qi * eg) + dkb * (bi * ki * eg) - dkg * (ki * egl) + qi * s * qa[r] -
                  ki * s * ka[r] + ki * qm[r] - ki * km[r];
       if (i == C - 1) dG += sDGl[d];
-      P.DG[i * K + d] = dG;
+      sfx[t][r] = dG;
+      if (i < it.len) {
+        const size_t idx = ((size_t)(it.tok0 + i) * H + it.h) * K + d;
+        a.dq[idx] = gqn;
+        a.dk[idx] = gkn;
+      }
+      if (a.l2norm) {
+        // row dots over the tile's 16 columns (lane shuffles), one slot per
+        // (channel tile, row)
+        float pq = qi * gqn, pk = ki * gkn;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          pq += __shfl_xor(pq, off, 64);
+          pk += __shfl_xor(pk, off, 64);
+        }
+        if (xi == 0) {
+          sDotP[ct * 2 * C + i] = pq;
+          sDotP[ct * 2 * C + C + i] = pk;
+        }
+      }
     }
+    // dg = reverse cumsum of dG over the chunk rows: within the lane's 4 rows,
+    // then over the later lane groups of the tile (shuffles); the later 16-row
+    // blocks are added below from their totals, each in a fixed order
+#pragma unroll
+    for (int r = 2; r >= 0; --r) sfx[t][r] += sfx[t][r + 1];
+    float tot[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tot[q] = __shfl(sfx[t][0], 16 * q + xi, 64);
+    float later = 0.f;
+#pragma unroll
+    for (int q = 3; q >= 1; --q) later += q > gq ? tot[q] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sfx[t][r] += later;
+    if (gq == 0) sBT[ib * K + d] = ((tot[3] + tot[2]) + tot[1]) + tot[0];
   }
   __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TPWE; ++t) {
+    const int tile = w + kNWW * t, ib = tile / NCT, d = 16 * (tile % NCT) + xi;
+    float after = 0.f;
+#pragma unroll
+    for (int b = 3; b >= 1; --b) after += b > ib ? sBT[b * K + d] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * ib + 4 * gq + r;
+      if (row < it.len) a.dg[((size_t)(it.tok0 + row) * H + it.h) * K + d] = sfx[t][r] + after;
+    }
+  }
   // dbeta and dv: TPR consecutive threads per row, each over a share of the channels
   {
     constexpr int TPR = kBW / C;
@@ -1444,52 +1495,37 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     if (part == 0 && i < it.len) a.dbeta[(size_t)(it.tok0 + i) * H + it.h] = db;
   }
   __syncthreads();
-  // L2-norm backward: row dot products q^ . dq^ and k^ . dk^
-  if (tid < 2 * C) {
-    const int r = tid % C;
-    const float* X = tid < C ? sQN : sKN;
-    const float* D = tid < C ? P.DQN : P.DKN;
-    float acc = 0.f;
-#pragma unroll 16
-    for (int d = 0; d < K; ++d) acc += X[r * K + d] * D[r * K + d];
-    sDot[tid] = acc;
-  }
-  __syncthreads();
-  constexpr int NE = C * K / kBW;
-  float gqv[NE], gkv[NE];
+  // L2-norm backward: dq = (dq^ - q^ (q^ . dq^)) / |q| (dq^ / eps where the norm
+  // is clamped), likewise dk. The row dots are summed over the channel tiles in
+  // a fixed order; each lane then completes the dq, dk elements it stored.
+  if (a.l2norm) {
+    if (tid < 2 * C) {
+      float acc = 0.f;
 #pragma unroll
-  for (int m = 0; m < NE; ++m) {
-    gqv[m] = P.DQN[tid + kBW * m];
-    gkv[m] = P.DKN[tid + kBW * m];
-  }
-#pragma unroll
-  for (int m = 0; m < NE; ++m) {
-    const int e = tid + kBW * m, r = e / K, d = e % K;
-    if (r >= it.len) continue;
-    const size_t idx = ((size_t)(it.tok0 + r) * H + it.h) * K + d;
-    float gradq = gqv[m], gradk = gkv[m];
-    if (a.l2norm) {
-      const float nq = sl[o.nq + r], nk = sl[o.nk + r];
-      gradq = nq > a.l2eps ? (gradq - sQN[e] * sDot[r]) / nq : gradq / a.l2eps;
-      gradk = nk > a.l2eps ? (gradk - sKN[e] * sDot[C + r]) / nk : gradk / a.l2eps;
+      for (int ct = 0; ct < NCT; ++ct) acc += sDotP[ct * 2 * C + tid];
+      sDot[tid] = acc;
     }
-    a.dq[idx] = gradq;
-    a.dk[idx] = gradk;
-  }
-  // dg = reverse cumsum of dG over the chunk
-  if (tid < K) {
-    const int d = tid;
-    float run = 0.f;
+    __syncthreads();
 #pragma unroll
-    for (int half = 1; half >= 0; --half) {  // rows 32..63, then 0..31: loads before stores
-      float col[C / 2];
+    for (int t = 0; t < TPWE; ++t) {
+      const int tile = w + kNWW * t, ib = tile / NCT, d = 16 * (tile % NCT) + xi;
+      float gqv[4], gkv[4];
 #pragma unroll
-      for (int r = 0; r < C / 2; ++r) col[r] = P.DG[(half * (C / 2) + r) * K + d];
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ib + 4 * gq + r;
+        const size_t idx = ((size_t)(it.tok0 + (row < it.len ? row : 0)) * H + it.h) * K + d;
+        gqv[r] = a.dq[idx];
+        gkv[r] = a.dk[idx];
+      }
 #pragma unroll
-      for (int r = C / 2 - 1; r >= 0; --r) {
-        const int row = half * (C / 2) + r;
-        run += col[r];
-        if (row < it.len) a.dg[((size_t)(it.tok0 + row) * H + it.h) * K + d] = run;
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ib + 4 * gq + r;
+        if (row < it.len) {
+          const size_t idx = ((size_t)(it.tok0 + row) * H + it.h) * K + d;
+          const float nq = sl[o.nq + row], nk = sl[o.nk + row];
+          a.dq[idx] = nq > a.l2eps ? (gqv[r] - sQN[row * K + d] * sDot[row]) / nq : gqv[r] / a.l2eps;
+          a.dk[idx] = nk > a.l2eps ? (gkv[r] - sKN[row * K + d] * sDot[C + row]) / nk : gkv[r] / a.l2eps;
+        }
       }
     }
   }

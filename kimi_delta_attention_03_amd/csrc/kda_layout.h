@@ -108,7 +108,7 @@ struct BwdSlab {
   size_t S, dS;                      // [K][V]
   // per-chunk gradients
   size_t dO, vn, dvn, dvb;           // [64][V]
-  size_t dqg, dw, dkg, dkb, dqn, dkn, dG;  // [64][K]
+  size_t dqg, dw, dkg, dkb;          // [64][K]
   size_t daqk, da, t1, dl;           // [64][64]
   size_t dgam;                       // [K]
   size_t floats;                     // slab size
@@ -126,8 +126,7 @@ static inline BwdSlab make_bwd_slab(int K, int V) {
   s.beta = take(C); s.gam = take((size_t)K); s.nq = take(C); s.nk = take(C);
   s.S = take((size_t)K * V); s.dS = take((size_t)K * V);
   s.dO = take(CV); s.vn = take(CV); s.dvn = take(CV); s.dvb = take(CV);
-  s.dqg = take(CK); s.dw = take(CK); s.dkg = take(CK); s.dkb = take(CK); s.dqn = take(CK); s.dkn = take(CK);
-  s.dG = take(CK);
+  s.dqg = take(CK); s.dw = take(CK); s.dkg = take(CK); s.dkb = take(CK);
   s.daqk = take(CC); s.da = take(CC); s.t1 = take(CC); s.dl = take(CC);
   s.dgam = take((size_t)K);
   s.floats = round_up(o, 64);
