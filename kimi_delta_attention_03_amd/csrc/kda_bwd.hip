@@ -265,17 +265,17 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     const float G = sG[r * KP + d], Gl = sG[(C - 1) * KP + d];
     const float qn = sQ[r * KP + d], kn = sK[r * KP + d];
     const float eg = __expf(G);
-    sl[o.qn + e] = qn;
-    sl[o.kn + e] = kn;
-    sl[o.G + e] = G;
     sl[o.qg + e] = a.scale * qn * eg;
     sl[o.kg + e] = kn * __expf(Gl - G);
     sl[o.kb + e] = sB[r] * kn * eg;
   }
+  // Vb for the fp32 product kernel (the bf16 one rebuilds it from v and beta)
+  if (qf32) {
 #pragma unroll
-  for (int m = 0; m < NE; ++m) {
-    const int e = tid + kBW * m;
-    sl[o.vb + e] = sB[e / V] * vv[m];
+    for (int m = 0; m < NE; ++m) {
+      const int e = tid + kBW * m;
+      sl[o.vb + e] = sB[e / V] * vv[m];
+    }
   }
   if (tid < K) sl[o.gam + tid] = __expf(sG[(C - 1) * KP + tid]);
   if (tid < C) sl[o.beta + tid] = sB[tid];
@@ -799,12 +799,12 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
 // ------------------------------------------------------------ chunk gradients
 // pointers to the slab arrays of one (chunk, head)
 struct SlabPtrs {
-  float *QN, *KN, *G, *QG, *KG, *W, *KB, *U, *VB, *AQK, *A, *Mm, *BETA, *GAM, *S, *DS, *DO, *VN, *DVN, *DVB, *DQG,
+  float *QG, *KG, *W, *KB, *U, *VB, *AQK, *A, *Mm, *BETA, *GAM, *S, *DS, *DO, *VN, *DVN, *DVB, *DQG,
       *DW, *DKG, *DKB, *DAQK, *DA, *T1, *DL, *DGAM;
 };
 __device__ __forceinline__ SlabPtrs slab_ptrs(float* sl, const BwdSlab& o) {
   SlabPtrs P;
-  P.QN = sl + o.qn; P.KN = sl + o.kn; P.G = sl + o.G; P.QG = sl + o.qg; P.KG = sl + o.kg; P.W = sl + o.w;
+  P.QG = sl + o.qg; P.KG = sl + o.kg; P.W = sl + o.w;
   P.KB = sl + o.kb; P.U = sl + o.u; P.VB = sl + o.vb; P.AQK = sl + o.aqk; P.A = sl + o.a; P.Mm = sl + o.m;
   P.BETA = sl + o.beta; P.GAM = sl + o.gam; P.S = sl + o.S; P.DS = sl + o.dS; P.DO = sl + o.dO; P.VN = sl + o.vn;
   P.DVN = sl + o.dvn; P.DVB = sl + o.dvb; P.DQG = sl + o.dqg; P.DW = sl + o.dw; P.DKG = sl + o.dkg;
@@ -1103,7 +1103,17 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
   // loads of phase 5
   NatStage<C, K> rKb, rVb;
   rKb.load(P.KB);
-  rVb.load(P.VB);
+  {
+    // Vb = beta v, rebuilt from the inputs as the chunk-term kernel builds it
+    // (rows past the chunk end are zero)
+    const bf16* vin = reinterpret_cast<const bf16*>(a.v);
+#pragma unroll
+    for (int m = 0; m < NatStage<C, V>::N; ++m) {
+      const int e = tid + kMT * m, row = e / (V / 4), c = 4 * (e % (V / 4)), rr = row < it.len ? row : 0;
+      const floatx4 vv = widen4(*reinterpret_cast<const bf16x4*>(vin + ((size_t)(it.tok0 + rr) * a.H + it.h) * V + c));
+      rVb.v[m] = row < it.len ? P.BETA[row] * vv : zero4();
+    }
+  }
   BlkStage<C, C> rA;
   rA.load(P.A);
   __syncthreads();
@@ -1284,17 +1294,38 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   const int qf32 = !a.bf16_qkv;
   const float s = a.scale;
 
-  // staging: every load of the thread first, then the LDS stores
+  // staging: every load of the thread first, then the LDS stores. q^, k^ and G
+  // are rebuilt from the inputs with the same operations, in the same order, as
+  // the chunk-term kernel builds them (normalised with its stored row norms;
+  // the gate cumsum sequential over the rows of a channel), so they are
+  // bitwise its values; rows past the chunk end are zero tokens.
   constexpr int N4 = C * K / 4 / kBW, NPP = C * C / kBW;
   static_assert(N4 * 4 * kBW == C * K && NPP * kBW == C * C, "staging split");
-  floatx4 rg4[N4], rk4[N4], rq4[N4];
+  floatx4 rk4[N4], rq4[N4], rg4[N4];
   float rp[NPP], rl[NPP], rbeta[NPP];
+  auto in_idx = [&](int m) {
+    const int e = tid + kBW * m, row = e / (K / 4), c = 4 * (e % (K / 4)), rr = row < it.len ? row : 0;
+    return ((size_t)(it.tok0 + rr) * H + it.h) * K + c;
+  };
+  if (qf32) {
 #pragma unroll
-  for (int m = 0; m < N4; ++m) {
-    const int e = tid + kBW * m;
-    rg4[m] = reinterpret_cast<const floatx4*>(P.G)[e];
-    rk4[m] = reinterpret_cast<const floatx4*>(P.KN)[e];
-    rq4[m] = reinterpret_cast<const floatx4*>(P.QN)[e];
+    for (int m = 0; m < N4; ++m) {
+      rq4[m] = load4_f32(reinterpret_cast<const float*>(a.q) + in_idx(m));
+      rk4[m] = load4_f32(reinterpret_cast<const float*>(a.k) + in_idx(m));
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < N4; ++m) {
+      rq4[m] = load4_f32(reinterpret_cast<const bf16*>(a.q) + in_idx(m));
+      rk4[m] = load4_f32(reinterpret_cast<const bf16*>(a.k) + in_idx(m));
+    }
+  }
+  if (a.g_f32) {
+#pragma unroll
+    for (int m = 0; m < N4; ++m) rg4[m] = load4_f32(reinterpret_cast<const float*>(a.g) + in_idx(m));
+  } else {
+#pragma unroll
+    for (int m = 0; m < N4; ++m) rg4[m] = load4_f32(reinterpret_cast<const bf16*>(a.g) + in_idx(m));
   }
 #pragma unroll
   for (int m = 0; m < NPP; ++m) {
@@ -1304,12 +1335,20 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     rbeta[m] = P.BETA[e / C];
   }
   const float rb = tid < C ? P.BETA[tid] : 0.f;
+  float qinv[N4], kinv[N4];
 #pragma unroll
   for (int m = 0; m < N4; ++m) {
-    const int e = tid + kBW * m;
-    reinterpret_cast<floatx4*>(sG)[e] = rg4[m];
-    reinterpret_cast<floatx4*>(sKN)[e] = rk4[m];
-    reinterpret_cast<floatx4*>(sQN)[e] = rq4[m];
+    const int row = (tid + kBW * m) / (K / 4);
+    qinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nq + row], a.l2eps) : 1.f;
+    kinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nk + row], a.l2eps) : 1.f;
+  }
+#pragma unroll
+  for (int m = 0; m < N4; ++m) {
+    const int e = tid + kBW * m, row = e / (K / 4);
+    const bool in = row < it.len;
+    reinterpret_cast<floatx4*>(sQN)[e] = in ? (a.l2norm ? rq4[m] * qinv[m] : rq4[m]) : zero4();
+    reinterpret_cast<floatx4*>(sKN)[e] = in ? (a.l2norm ? rk4[m] * kinv[m] : rk4[m]) : zero4();
+    reinterpret_cast<floatx4*>(sG)[e] = in ? rg4[m] : zero4();
   }
 #pragma unroll
   for (int m = 0; m < NPP; ++m) {
@@ -1324,6 +1363,15 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
 #pragma unroll 16
     for (int r = 0; r < C; ++r) acc += P.DKG[r * K + tid] * P.KG[r * K + tid];
     sDGl[tid] = acc;
+  }
+  __syncthreads();
+  // gate cumsum in place, sequential over the rows of each channel
+  if (tid < K) {
+    float run = 0.f;
+    for (int r = 0; r < C; ++r) {
+      run += sG[r * K + tid];
+      sG[r * K + tid] = run;
+    }
   }
   __syncthreads();
 

@@ -99,8 +99,9 @@ static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, i
 // in floats from the slab start; matrices are row-major with the chunk row
 // (64) or the key channel (K) first, as named.
 struct BwdSlab {
-  // chunk terms recomputed from the inputs (natural-log gates)
-  size_t qn, kn, G, qg, kg, w, kb;   // [64][K]: normalised q, k; cumsum; s q e^G; k e^(Gl-G); A Kb; beta k e^G
+  // chunk terms recomputed from the inputs (natural-log gates; the normalised q,
+  // k and the gate cumsum are rebuilt where needed and not stored)
+  size_t qg, kg, w, kb;              // [64][K]: s q e^G; k e^(Gl-G); A Kb; beta k e^G
   size_t u, vb;                      // [64][V]: A Vb; beta v
   size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
   size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
@@ -119,8 +120,7 @@ static inline BwdSlab make_bwd_slab(int K, int V) {
   size_t o = 0;
   auto take = [&](size_t n) { const size_t r = o; o += n; return r; };
   const size_t C = kChunk, CK = C * (size_t)K, CV = C * (size_t)V, CC = C * C;
-  s.qn = take(CK); s.kn = take(CK); s.G = take(CK); s.qg = take(CK); s.kg = take(CK); s.w = take(CK);
-  s.kb = take(CK);
+  s.qg = take(CK); s.kg = take(CK); s.w = take(CK); s.kb = take(CK);
   s.u = take(CV); s.vb = take(CV);
   s.aqk = take(CC); s.a = take(CC); s.m = take(CC);
   s.beta = take(C); s.gam = take((size_t)K); s.nq = take(C); s.nk = take(C);

@@ -215,7 +215,7 @@ def test_decode_rejects_bad_params_before_launch(lib):
 
 def test_backward_workspace_formula(lib):
     """Backward workspace = forward metadata + one fp32 slab per (chunk slot, head):
-    11 [64 x K] + 6 [64 x V] + 7 [64 x 64] matrices, 3 row vectors, 2 [K] vectors and
+    8 [64 x K] + 6 [64 x V] + 7 [64 x 64] matrices, 3 row vectors, 2 [K] vectors and
     2 [K x V] states, rounded up to 64 floats."""
     for K in (64, 128):
         p = P(K=K, V=K, B=2, T=256, H=3)
@@ -223,7 +223,7 @@ def test_backward_workspace_formula(lib):
         assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == 0
         info = _lib.KdaWorkspaceInfo()
         assert lib.kda_workspace_layout(ctypes.byref(p), ctypes.byref(info)) == 0
-        slab = 11 * 64 * K + 6 * 64 * K + 7 * 64 * 64 + 3 * 64 + 2 * K + 2 * K * K
+        slab = 8 * 64 * K + 6 * 64 * K + 7 * 64 * 64 + 3 * 64 + 2 * K + 2 * K * K
         slab = (slab + 63) // 64 * 64
         assert n.value == info.records_offset + info.chunk_slots * 3 * slab * 4
 
