@@ -29,6 +29,11 @@ def _asm(src, tmp_path):
 
 
 def masked_mfma_count(asm: str) -> int:
+    """MFMAs on the fall-through path of an EXEC-masked region with no
+    s_cbranch_execz skip. An unconditional s_branch ends the fall-through path:
+    the code after it is another block, entered only by jumps (a masked body
+    that the compiler moved elsewhere is scanned at its own place, after its
+    own s_and_saveexec)."""
     bad, in_mask, skipped = 0, False, False
     for line in asm.splitlines():
         t = line.strip()
@@ -36,7 +41,7 @@ def masked_mfma_count(asm: str) -> int:
             in_mask, skipped = True, False
         elif in_mask and t.startswith("s_cbranch_execz"):
             skipped = True
-        elif in_mask and re.match(r"s_(or|mov)_b64\s+exec", t):
+        elif in_mask and (re.match(r"s_(or|mov)_b64\s+exec", t) or re.match(r"s_branch\s", t)):
             in_mask = False
         elif in_mask and not skipped and t.startswith("v_mfma"):
             bad += 1
@@ -61,3 +66,17 @@ def test_detector_flags_masked_mfma():
     assert masked_mfma_count(snippet) == 1
     skipped = snippet.replace("vcc\n", "vcc\n    s_cbranch_execz .L1\n")
     assert masked_mfma_count(skipped) == 0
+    # a masked store block placed out of line, jumping back into its body; the
+    # block after the unconditional branch is entered by a scalar branch
+    out_of_line = """
+    s_and_saveexec_b64 s[0:1], s[2:3]
+    s_cbranch_execnz .L37
+    s_branch .L38
+.L81:
+    v_mfma_f32_16x16x4_f32 v[0:3], v28, v33, v[0:3]
+    """
+    assert masked_mfma_count(out_of_line) == 0
+    # an MFMA before the branch is still on the masked path
+    before = out_of_line.replace("    s_cbranch_execnz .L37\n",
+                                 "    v_mfma_f32_16x16x4_f32 v[0:3], v28, v33, v[0:3]\n    s_cbranch_execnz .L37\n")
+    assert masked_mfma_count(before) == 1
