@@ -421,7 +421,9 @@ def bench_layer(args, torch, kda):
     bf = ("Wqkv", "Wb", "Wad", "Wau", "Wgd", "Wgu", "Wo")
     wd = {n: torch.from_numpy(a).to(torch.bfloat16 if n in bf else torch.float32).to("cuda:0") for n, a in w.items()}
     xd = torch.from_numpy(x).to(torch.bfloat16).to("cuda:0")
-    layer = kda.KdaLayer(wd, B, T, H, D)
+    # the input-projection weights packed back to back once, as at model load:
+    # the layer then reads them in place
+    layer = kda.KdaLayer(kda.pack_layer_weights(wd), B, T, H, D)
     for _ in range(args.warmup):
         layer(xd)
     ms = time_loop(lambda: layer(xd), args.steps, torch)

@@ -71,6 +71,12 @@ typedef struct {
   const float* norm_w;     /* fp32 [D] */
   const void* Wo;          /* bf16 [M, H D] */
 } kda_layer_weights;
+/* The input projection multiplies x by the row concatenation [Wqkv; Wad; Wgd;
+ * Wb] ([3 H D + gate_rank + out_gate_rank + H, M]). If the four matrices
+ * already sit back to back in that order in one allocation (Wad starting where
+ * Wqkv ends, and so on) with Wqkv 16-byte aligned, the GEMM reads them in
+ * place; otherwise each call first copies them into the workspace (four
+ * device-to-device copies on `stream`). */
 
 /* The layer's projection GEMM on its own (bf16 operands, fp32 accumulation,
  * hand-written MFMA kernel): C[m, n] = sum_k A[m, k] B[n, k] for A [M, K] and

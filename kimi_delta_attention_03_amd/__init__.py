@@ -450,6 +450,30 @@ class KdaLayer:
         return self.x_new
 
 
+def pack_layer_weights(weights):
+    """A copy of the weight dict whose input-projection matrices Wqkv, Wad, Wgd
+    and Wb are views of one bf16 allocation, back to back in that order
+    (include/kda_layer.h): kda_layer_fwd then reads them in place instead of
+    copying them at every call. One device copy, at load time."""
+    torch = _torch()
+    names = ("Wqkv", "Wad", "Wgd", "Wb")
+    for n in names:
+        t = weights[n]
+        if not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 2:
+            raise KdaValueError(1, f"layer weight {n} must be a 2-D bf16 GPU tensor")
+    M = weights["Wqkv"].shape[1]
+    if any(weights[n].shape[1] != M for n in names):
+        raise KdaValueError(1, "Wqkv, Wad, Wgd and Wb must have the same number of columns")
+    buf = torch.cat([weights[n].contiguous() for n in names], dim=0)
+    out = dict(weights)
+    at = 0
+    for n in names:
+        rows = weights[n].shape[0]
+        out[n] = buf[at:at + rows]
+        at += rows
+    return out
+
+
 def layer_fwd(x, weights, H, D, **kw):
     """KDA layer forward on the GPU: x bf16 [B, T, M] -> x_new bf16 [B, T, M]."""
     B, T, _ = x.shape

@@ -303,20 +303,28 @@ kda_status kda_layer_fwd(const kda_layer_params* p, const kda_layer_weights* w, 
   float* beta = reinterpret_cast<float*>(ws + L.off_beta);
   float* o = core_out ? core_out : reinterpret_cast<float*>(ws + L.off_o);
 
-  // 1. concatenated input projections (rows of width M)
+  // 1. concatenated input projections (rows of width M): read in place when the
+  // caller keeps [Wqkv; Wad; Wgd; Wb] back to back, else copied
   const size_t rowb = (size_t)M * 2;
-  size_t at = 0;
   const struct { const void* src; size_t rows; } parts[] = {
       {w->Wqkv, (size_t)3 * HD}, {w->Wad, (size_t)r}, {w->Wgd, (size_t)rg}, {w->Wb, (size_t)H}};
-  for (const auto& pt : parts) {
-    if (hipMemcpyAsync(reinterpret_cast<char*>(wcat) + at, pt.src, pt.rows * rowb, hipMemcpyDeviceToDevice, stream) !=
-        hipSuccess)
-      return fail_msg(KDA_ERR_HIP, "weight copy failed");
-    at += pt.rows * rowb;
+  bool adjacent = reinterpret_cast<uintptr_t>(w->Wqkv) % 16 == 0;
+  for (int i = 1; i < 4; ++i)
+    adjacent = adjacent && static_cast<const char*>(parts[i].src) ==
+                               static_cast<const char*>(parts[i - 1].src) + parts[i - 1].rows * rowb;
+  const void* wproj = adjacent ? w->Wqkv : static_cast<const void*>(wcat);
+  if (!adjacent) {
+    size_t at = 0;
+    for (const auto& pt : parts) {
+      if (hipMemcpyAsync(reinterpret_cast<char*>(wcat) + at, pt.src, pt.rows * rowb, hipMemcpyDeviceToDevice,
+                         stream) != hipSuccess)
+        return fail_msg(KDA_ERR_HIP, "weight copy failed");
+      at += pt.rows * rowb;
+    }
   }
   // 2. P = x Wcat^T
   const int NW = 3 * HD + r + rg + H;  // rows of Wcat (columns of P in use)
-  s = gemm_nt(wcat, M, x, M, P, NP, false, NW, BT, M, stream, "input projections");
+  s = gemm_nt(wproj, M, x, M, P, NP, false, NW, BT, M, stream, "input projections");
   if (s != KDA_OK) return s;
   // 3. prologue
   {

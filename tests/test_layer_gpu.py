@@ -34,11 +34,14 @@ def dev_weights(w):
     return {n: to_dev(a, torch.bfloat16 if n in BF16_W else torch.float32) for n, a in w.items()}
 
 
-def run_layer(x, w, H, D, keep_core=True):
+def run_layer(x, w, H, D, keep_core=True, packed=False):
     import kimi_delta_attention_03_amd as kda
     import torch
     B, T, _ = x.shape
-    layer = kda.KdaLayer(dev_weights(w), B, T, H, D, keep_core_output=keep_core)
+    wd = dev_weights(w)
+    if packed:
+        wd = kda.pack_layer_weights(wd)
+    layer = kda.KdaLayer(wd, B, T, H, D, keep_core_output=keep_core)
     y = layer(to_dev(x, torch.bfloat16))
     torch.cuda.synchronize()
     return layer, y
@@ -55,6 +58,20 @@ def test_layer_small_matches_oracle(D):
     ey = rel_err(host(y), ref)
     _say(f"  rel err core o={eo:.2e} x_new={ey:.2e}")
     assert eo <= TOL_LAYER and ey <= TOL_LAYER
+
+
+def test_layer_packed_projection_weights_bitwise_equal():
+    """Input-projection weights packed back to back (read in place by the GEMM)
+    and as four separate tensors (copied into the workspace at every call) give
+    the same x_new bit for bit."""
+    import torch
+    B, T, M, H, D, r = 2, 192, 256, 3, 64, 32
+    _say(f"layer packed vs separate weights B={B} T={T} M={M} H={H} D={D}")
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, rank=r, seed=61)
+    _, y1 = run_layer(x, w, H, D, keep_core=False)
+    y1 = y1.clone()
+    _, y2 = run_layer(x, w, H, D, keep_core=False, packed=True)
+    assert torch.equal(y1, y2)
 
 
 @pytest.mark.parametrize("H,D", [(2, 128), (4, 64)])
@@ -106,7 +123,7 @@ def workload4():
     x, w = layer_inputs()
     H, D = 16, 128
     _say("layer workload 4: GPU run")
-    layer, y = run_layer(x, w, H, D)
+    layer, y = run_layer(x, w, H, D, packed=True)
     ci = layer.core_inputs()
     got = {"x_new": host(y), "o": host(layer.core_out)}
     for n in ("q", "k", "v", "g_raw", "beta"):
