@@ -292,7 +292,7 @@ def bwd_flops_per_chunk_head(C, K, V):
 
 
 def bwd_chunk_alg_bytes_per_token_head(K, V, e):
-    """Bytes the chunk-gradient launch pair cannot avoid per token-head, with
+    """Bytes the chunk-gradient stage cannot avoid per token-head, with
     inputs of e bytes per element: the chunk's inputs q, k, g (K each), v and
     dO (V each) and beta, the chunk-start state S and the end-state gradient
     dS' (K x V fp32 each, once per 64-token chunk), and the fp32 gradients dq,
@@ -344,22 +344,22 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
     tp = os.path.join(ROOT, "profiles", f"traffic_kda_bwd_{WORKLOADS[args.workload]['name']}.json")
     if os.path.exists(tp):
         rec = json.load(open(tp))
-        chunk_mm = "bwd_chunk_mfma_kernel" if x.dtype == "bf16" else "bwd_chunk_mm_kernel"
+        chunk = (["bwd_chunk_fused_kernel"] if x.dtype == "bf16" else ["bwd_chunk_mm_kernel", "bwd_chunk_elem_kernel"])
         names = {"prep": ["bwd_prep_kernel"], "states_fwd": ["bwd_states_fwd_kernel"],
-                 "states_bwd": ["bwd_states_bwd_kernel"], "chunk": [chunk_mm, "bwd_chunk_elem_kernel"]}
+                 "states_bwd": ["bwd_states_bwd_kernel"], "chunk": chunk}
         if rec.get("source_sha256_16") == kernel_source_hash("bwd") and all(n in rec["kernels"] for n in names[dom]):
             traffic = sum(rec["kernels"][n]["traffic_bytes"] for n in names[dom])
     ach = fl[dom] * nchunk_heads / (stage_ms[dom] / 1e3) / 1e12
     if dom == "chunk":
-        # the chunk pair streams its operands and results through the fp32 slab
-        # (its products run on MFMA for bf16 inputs): it is bound by memory
-        # traffic, so its roofline is HBM on the bytes it cannot avoid (see
-        # bwd_chunk_alg_bytes_per_token_head), with the measured bytes beside them
+        # the chunk-gradient launch(es) stream their operands through the fp32
+        # slab (for bf16 inputs one fused kernel with its products on MFMA): bound
+        # by memory traffic, so the roofline is HBM on the bytes they cannot avoid
+        # (see bwd_chunk_alg_bytes_per_token_head), with the measured bytes beside them
         ntok_heads = (int(x.cu_seqlens[-1]) if cu is not None else B * T) * H
         alg_b = bwd_chunk_alg_bytes_per_token_head(K, V, 2 if x.dtype == "bf16" else 4) * ntok_heads
         gbps = alg_b / (stage_ms[dom] / 1e3) / 1e9
-        pair = "chunk_mfma" if x.dtype == "bf16" else "chunk_mm"
-        roof = {"kernel": f"bwd_chunk ({pair} + chunk_elem)", "bound": "hbm", "achieved": gbps,
+        kname = "bwd_chunk_fused" if x.dtype == "bf16" else "bwd_chunk (chunk_mm + chunk_elem)"
+        roof = {"kernel": kname, "bound": "hbm", "achieved": gbps,
                 "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": gbps * 1e9 / PEAK_HBM, "traffic": traffic,
                 "alg_bytes_per_launch": alg_b, "traffic_over_alg": None if traffic is None else traffic / alg_b,
                 "flop_rate_TFLOPs": ach}

@@ -22,19 +22,22 @@
 // to dq, dk, dv, dg (reverse cumsum of dG), dbeta; with the optional L2 norm,
 // dq = (dq^ - q^ (q^ . dq^)) / |q| (or dq^ / eps where the norm is clamped).
 //
-// Four stages, five launches:
+// Four stages:
 //   prep        per (chunk, head): the chunk terms above, from the inputs
 //   states_fwd  per (sequence, head, 16 columns): chunk-start states, in order
 //   states_bwd  per (sequence, head, 16 columns): dS' per chunk, in reverse; dh0
-//   chunk       per (chunk, head): every other gradient, as two launches (the
-//               matrix products, then the elementwise and gated-sum rules)
-// Every intermediate lives in a per-(chunk, head) fp32 slab of the workspace.
-// prep and the elementwise kernel are latency-bound chains of phases and run
-// 16 waves per workgroup (one workgroup per CU by LDS); the product kernel runs
-// 4 waves with its operand slices double-buffered; the two state passes run 8
-// waves, 4 on the per-chunk MFMA chain and 4 that load and stage the chunk
-// operands ahead of it. Loads are issued before stores throughout: on this GPU
-// a memory-counter wait also waits for every earlier store.
+//   chunk       per (chunk, head): every other gradient. With bf16 q/k/v one
+//               fused launch (products on bf16 MFMA, then the elementwise and
+//               gated-sum rules, the item on chip); with fp32 two launches (fp32
+//               products through the slab, then the rules)
+// The chunk terms and states live in a per-(chunk, head) fp32 slab of the
+// workspace. prep and the fp32 elementwise kernel are latency-bound chains of
+// phases and run 16 waves per workgroup (one workgroup per CU by LDS); the fp32
+// product kernel runs 4 waves with its operand slices double-buffered; the two
+// state passes run 8 waves, 4 on the per-chunk MFMA chain and 4 that load and
+// stage the chunk operands ahead of it. Loads are issued before stores
+// throughout: on this GPU a memory-counter wait also waits for every earlier
+// store.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -866,14 +869,89 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
                             [&](int i, int j, float x) { P.DL[i * C + j] = j < i ? -x : 0.f; });
 }
 
-// ------------------------------------------- chunk products on MFMA (bf16 input)
+// The four gated sums of the chunk reverse step (per row i, channel d; P = dAqk,
+// dM = Diag(beta) dL, E_ij = exp(G_i - G_j))
+//   query side  sum_{j<=i} P_ij k_j E_ij,   sum_{j<i} dM_ij k_j E_ij
+//   key side    sum_{r>=i} P_ri q_r E_ri,   sum_{r>i} dM_ri k_r E_ri
+// as fp32 MFMA products over 16-row blocks with one reference per block (the
+// rebasing of "KDA Doesn't Care About the Future", section "The rebasing
+// trick"): with rho_b = G of the first row of block b, a key j of block b
+// carries exp(rho_b - G_j) (at most 15 steps of decay) and the query row
+// exp(G_i - rho_b) <= 1 for i >= 16 b; the key side uses the reference of row
+// i's own block the same way. For the 16 x 16 tile (row block ib, channel
+// d = 16 ct + xi) of lane (gq, xi): qa, qm, ka, km hold rows 16 ib + 4 gq + r.
+// LDS operands in fp32: G, k^, q^ as [C][K]; P and dM as [C][C + 4].
+template <int K>
+__device__ __forceinline__ void gated_sums(const float* sG, const float* sKN, const float* sQN, const float* sP,
+                                           const float* sDM, int ib, int d, int gq, int xi, floatx4& qa,
+                                           floatx4& qm, floatx4& ka, floatx4& km) {
+  constexpr int CP = C + 4;
+  qa = zero4(); qm = zero4(); ka = zero4(); km = zero4();
+  // query side: key blocks b <= ib
+  for (int b = 0; b <= ib; ++b) {
+    const float rho = sG[(16 * b) * K + d];
+    floatx4 accA = zero4(), accM = zero4();
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += 4) {
+      const int j = 16 * b + k0 + gq;
+      const float kf = sKN[j * K + d] * __expf(rho - sG[j * K + d]);
+      accA = mfma4(sP[(16 * ib + xi) * CP + j], kf, accA);
+      accM = mfma4(sDM[(16 * ib + xi) * CP + j], kf, accM);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = __expf(sG[(16 * ib + 4 * gq + r) * K + d] - rho);
+      qa[r] += e * accA[r];
+      qm[r] += e * accM[r];
+    }
+  }
+  // key side: query blocks b >= ib, reference of block ib
+  {
+    const float rho = sG[(16 * ib) * K + d];
+    for (int b = ib; b < 4; ++b) {
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const int r = 16 * b + k0 + gq;
+        const float e = __expf(sG[r * K + d] - rho);
+        ka = mfma4(sP[r * CP + 16 * ib + xi], sQN[r * K + d] * e, ka);
+        km = mfma4(sDM[r * CP + 16 * ib + xi], sKN[r * K + d] * e, km);
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float f = __expf(rho - sG[(16 * ib + 4 * gq + r) * K + d]);
+      ka[r] *= f;
+      km[r] *= f;
+    }
+  }
+}
+
+// the elementwise rules of element (row i, channel d): the gradients of the
+// normalised q and k and of G (before the reverse cumsum), from dQg, dKb, dKG
+// and the four gated sums; Qg = s q e^G, Kb = beta k e^G and KG = k e^(Gl - G)
+// are rebuilt from the staged rows
+template <int K>
+__device__ __forceinline__ void elem_rules(const float* sG, const float* sQN, const float* sKN, const float* sBeta,
+                                           const float* sDGl, int i, int d, float s, float dqg, float dkb, float dkg,
+                                           float qa, float qm, float ka, float km, float& gqn, float& gkn,
+                                           float& dG) {
+  const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
+  const float Gl = sG[(C - 1) * K + d];
+  const float eg = __expf(Gi), egl = __expf(Gl - Gi);
+  gqn = s * eg * dqg + s * qa;
+  gkn = dkb * bi * eg + dkg * egl + s * ka + qm + km;
+  dG = dqg * (s * qi * eg) + dkb * (bi * ki * eg) - dkg * (ki * egl) + qi * s * qa - ki * s * ka + ki * qm - ki * km;
+  if (i == C - 1) dG += sDGl[d];
+}
+
+// ----------------------------- chunk gradients, fused, on MFMA (bf16 input)
 // With bf16 q, k, v (and dO) the products above run on v_mfma_f32_16x16x32_bf16:
 // every operand is rounded to bf16 (the input compute dtype, as in the forward's
 // bf16 path) and every product accumulates in fp32. One workgroup (8 waves) per
-// (chunk, head) keeps all operands and intermediates of the item in LDS, so the
-// slab is read once (S, dS', W, U, KG, Kb, Vb, Aqk, A) and only the gradients
-// the elementwise kernel needs are written back; Vn, dVn, dW, dA and T1 never
-// leave the chip.
+// (chunk, head) keeps all operands and intermediates of the item on chip, reads
+// each slab array once and writes only the gradients: Vn, dVn, dW, dA and T1
+// stay in LDS, and dQg, dKb, dKG, dAqk, dL stay in registers for the
+// elementwise phase that follows the products in the same workgroup.
 //
 // An operand matrix sits in LDS with its reduction index contiguous: the
 // A operand as [output row][reduction], the B operand as [output column]
@@ -893,7 +971,9 @@ __global__ __launch_bounds__(kBT) void bwd_chunk_mm_kernel(BwdArgs a) {
 //   5  dA = dW Kb^T + dVn Vb^T, dKb = A^T dW, dVb = A^T dVn (Kb, Vb, A^T)
 //   6  T1 = A^T dA                                (A staged for phase 7)
 //   7  dL = -StrictTril(T1 A^T)
-constexpr int kMT = 512;  // threads of the MFMA product kernel
+//   then the elementwise phase: gated sums and rules per tile of the C x K
+//   tiling, dq, dk, dg, dv, dbeta
+constexpr int kMT = 512;  // threads of the fused kernel
 
 // output tiles of an M x N product over 8 waves: each wave a BM x BN block of
 // 16 x 16 tiles
@@ -1002,38 +1082,62 @@ struct BlkStage {
 };
 
 template <int K>
-__global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   constexpr int V = K;
-  constexpr int PK = K + 8, PC = C + 8;      // LDS row pitches (elements)
+  constexpr int PK = K + 8, PC = C + 8;      // LDS row pitches of the bf16 operands (elements)
   constexpr int CK = C * PK, KK = K * PK, KC = K * PC, CCS = C * PC;  // matrix sizes (elements)
-  // LDS plan (elements): Vn, dVn, dVn^T stay from their phase to their last use;
-  // the operand area Q is re-laid out per phase; dA^T, T1 and A reuse the space
-  // of Vn and dVn once those are dead
+  // LDS plan of the product phases (bf16 elements): Vn, dVn, dVn^T stay from
+  // their phase to their last use; the operand area Q is re-laid out per phase;
+  // dA^T, T1 and A reuse the space of Vn and dVn once those are dead
   constexpr int oVn = 0, odVn = CK, odVnT = 2 * CK, oQ = 2 * CK + KC;
-  constexpr int oW = oQ, oST = oQ + CK;                                   // phase 1
+  constexpr int oW = oQ, oST = oQ + CK;                                        // phase 1
   constexpr int oAqT = oQ, odOT = oQ + CCS, oKG = odOT + KC, odST = oKG + CK;  // phase 2
-  constexpr int odS = oQ;                                                 // phase 3
-  constexpr int odW = oQ, odWT = oQ + CK, odO = odWT + KC, oS = odO + CK;     // phase 4
-  constexpr int oKb = odO, oVb = oKb + CK, oAT = oVb + CK;                // phase 5
-  constexpr int odAT = 0, oT1 = CCS, oA = 2 * CCS;                         // phases 5-7
-  constexpr int kElems = (oS + KK > oAT + CCS ? oS + KK : oAT + CCS) > odST + KK
-                             ? (oS + KK > oAT + CCS ? oS + KK : oAT + CCS)
-                             : odST + KK;
+  constexpr int odS = oQ;                                                      // phase 3
+  constexpr int odW = oQ, odWT = oQ + CK, odO = odWT + KC, oS = odO + CK;      // phase 4
+  constexpr int oKb = odO, oVb = oKb + CK, oAT = oVb + CK;                     // phase 5
+  constexpr int odAT = 0, oT1 = CCS, oA = 2 * CCS;                             // phases 5-7
+  constexpr int kMM = (oS + KK > oAT + CCS ? oS + KK : oAT + CCS) > odST + KK
+                          ? (oS + KK > oAT + CCS ? oS + KK : oAT + CCS)
+                          : odST + KK;
   static_assert(oA + CCS <= odVnT + KC, "LDS plan");
   static_assert(oT1 + CCS <= oQ && odAT + CCS <= odVn, "phase 5-7 results over dead matrices");
-  __shared__ __attribute__((aligned(16))) bf16 smem[kElems];
+  // the elementwise phase lays the same memory out as fp32: G, k^, q^ [C][K],
+  // dAqk and Diag(beta) dL [C][C + 4], per channel tile row dots, 16-row block
+  // totals of dG and the per wave row partial column sums of dKG * KG
+  using TCV = MTiles<C, V>;   // C x V and C x K results (K == V)
+  using TCC = MTiles<C, C>;
+  constexpr int CP = C + 4, NCT = K / 16;
+  constexpr int WRV = 8 / TCV::WC;            // wave rows of the C x K tiling
+  constexpr int fG = 0, fKN = C * K, fQN = 2 * C * K, fP = 3 * C * K, fDM = fP + C * CP, fDotP = fDM + C * CP,
+                fBT = fDotP + NCT * 2 * C, fDGlP = fBT + 4 * K, kEF = fDGlP + WRV * K;
+  constexpr int kBytes = (2 * kMM > 4 * kEF ? 2 * kMM : 4 * kEF);
+  __shared__ __attribute__((aligned(16))) char lds[kBytes];
+  bf16* smem = reinterpret_cast<bf16*>(lds);
+  float* sF = reinterpret_cast<float*>(lds);
+  // dbeta partial sums per row: dVb . v per wave column of the C x V tiling,
+  // dKb . (k^ e^G) likewise, and dL . M per wave column of the C x C tiling
+  constexpr int kDbSlots = 2 * TCV::WC + TCC::WC;
+  __shared__ float sBeta[C], sDot[2 * C], sDGl[K], sDgam[K], sDbP[kDbSlots * C];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, i = lane & 15;
   if ((int)blockIdx.x >= items_in_use(a)) return;
   const ItemB it = chunk_of(a, (int)blockIdx.x / a.H, (int)blockIdx.x % a.H);
-  const SlabPtrs P = slab_ptrs(slab_of(a, it.p, it.h), a.sl);
+  float* sl = slab_of(a, it.p, it.h);
+  const BwdSlab& o = a.sl;
+  const SlabPtrs P = slab_ptrs(sl, o);
+  const int H = a.H;
+  const int r0v = TCV::r0(w), c0v = TCV::c0(w), r0c = TCC::r0(w), c0c = TCC::c0(w);
 
-  using TCV = MTiles<C, V>;   // C x V and C x K results (K == V)
-  using TCC = MTiles<C, C>;
   floatx4 acc[TCV::BM][TCV::BN];
   floatx4 acc2[TCC::BM][TCC::BN];
+  // results kept in registers for the elementwise phase, in the MFMA's own
+  // layout (lane (g, i): rows 4 g + r, column i of each 16 x 16 tile), which is
+  // the layout of its tiles: dQg, dKb, dKG over the C x K tiling; dAqk and dL
+  // with rows i, columns 4 g + r over the C x C tiling
+  floatx4 kQG[TCV::BM][TCV::BN], kKB[TCV::BM][TCV::BN], kKG[TCV::BM][TCV::BN];
+  floatx4 kAQ[TCC::BM][TCC::BN], kDL[TCC::BM][TCC::BN];
 
   // ---- loads of phase 1, and the state S (kept in registers until phase 4)
   NatStage<C, K> rW;
@@ -1045,7 +1149,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
   for (int bm = 0; bm < TCV::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCV::BN; ++bn)
-      rU[bm][bn] = *reinterpret_cast<const floatx4*>(P.U + (TCV::r0(w) + 16 * bm + i) * V + TCV::c0(w) + 16 * bn + 4 * g);
+      rU[bm][bn] = *reinterpret_cast<const floatx4*>(P.U + (r0v + 16 * bm + i) * V + c0v + 16 * bn + 4 * g);
 
   // ---- phase 1: Vn = U - W S
   rW.store(smem + oW);
@@ -1066,7 +1170,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int row = do_row(m) + r, rr = row < it.len ? row : 0;
-          rdO[m][r] = *reinterpret_cast<const bf16x4*>(dO + ((size_t)(it.tok0 + rr) * a.H + it.h) * V + do_col(m));
+          rdO[m][r] = *reinterpret_cast<const bf16x4*>(dO + ((size_t)(it.tok0 + rr) * H + it.h) * V + do_col(m));
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -1079,12 +1183,12 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
   rdS.load(P.DS);
   __syncthreads();
   zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, K, true>(acc, smem + oW, PK, smem + oST, PK, TCV::r0(w), TCV::c0(w), lane);
+  mfma_rows<TCV::BM, TCV::BN, K, true>(acc, smem + oW, PK, smem + oST, PK, r0v, c0v, lane);
 #pragma unroll
   for (int bm = 0; bm < TCV::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCV::BN; ++bn)
-      *reinterpret_cast<bf16x4*>(smem + oVn + (TCV::r0(w) + 16 * bm + i) * PK + TCV::c0(w) + 16 * bn + 4 * g) =
+      *reinterpret_cast<bf16x4*>(smem + oVn + (r0v + 16 * bm + i) * PK + c0v + 16 * bn + 4 * g) =
           to_bf16x4(rU[bm][bn] - acc[bm][bn]);
   __syncthreads();
 
@@ -1100,17 +1204,16 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
     }
   rKG.store(smem + oKG);
   rdS.store_t(smem + odST);
-  // loads of phase 5
+  // loads of phase 5: Kb, and Vb = beta v rebuilt from the inputs as the
+  // chunk-term kernel builds it (rows past the chunk end are zero), and A
   NatStage<C, K> rKb, rVb;
   rKb.load(P.KB);
   {
-    // Vb = beta v, rebuilt from the inputs as the chunk-term kernel builds it
-    // (rows past the chunk end are zero)
     const bf16* vin = reinterpret_cast<const bf16*>(a.v);
 #pragma unroll
     for (int m = 0; m < NatStage<C, V>::N; ++m) {
       const int e = tid + kMT * m, row = e / (V / 4), c = 4 * (e % (V / 4)), rr = row < it.len ? row : 0;
-      const floatx4 vv = widen4(*reinterpret_cast<const bf16x4*>(vin + ((size_t)(it.tok0 + rr) * a.H + it.h) * V + c));
+      const floatx4 vv = widen4(*reinterpret_cast<const bf16x4*>(vin + ((size_t)(it.tok0 + rr) * H + it.h) * V + c));
       rVb.v[m] = row < it.len ? P.BETA[row] * vv : zero4();
     }
   }
@@ -1118,13 +1221,13 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
   rA.load(P.A);
   __syncthreads();
   zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, C, false>(acc, smem + oAqT, PC, smem + odOT, PC, TCV::r0(w), TCV::c0(w), lane);
-  mfma_rows<TCV::BM, TCV::BN, K, false>(acc, smem + oKG, PK, smem + odST, PK, TCV::r0(w), TCV::c0(w), lane);
+  mfma_rows<TCV::BM, TCV::BN, C, false>(acc, smem + oAqT, PC, smem + odOT, PC, r0v, c0v, lane);
+  mfma_rows<TCV::BM, TCV::BN, K, false>(acc, smem + oKG, PK, smem + odST, PK, r0v, c0v, lane);
 #pragma unroll
   for (int bm = 0; bm < TCV::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCV::BN; ++bn) {
-      const int R0 = TCV::r0(w) + 16 * bm, C0 = TCV::c0(w) + 16 * bn;
+      const int R0 = r0v + 16 * bm, C0 = c0v + 16 * bn;
       const bf16x4 y = to_bf16x4(acc[bm][bn]);
       *reinterpret_cast<bf16x4*>(smem + odVnT + (C0 + i) * PC + R0 + 4 * g) = y;
 #pragma unroll
@@ -1132,7 +1235,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
     }
   __syncthreads();
 
-  // ---- phase 3: dKG = Vn dS'^T, dgamma = rowsum(S * dS')
+  // ---- phase 3: dKG = Vn dS'^T (kept), dgamma = rowsum(S * dS')
   rdS.store(smem + odS);
 #pragma unroll
   for (int m = 0; m < BlkStage<K, V>::N; ++m) {
@@ -1150,19 +1253,14 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) part[r] += __shfl_xor(part[r], off, 64);
     if (BlkStage<K, V>::has(m) && BlkStage<K, V>::bcol(m) == 0)
-      *reinterpret_cast<floatx4*>(P.DGAM + BlkStage<K, V>::brow(m)) = part;
+      *reinterpret_cast<floatx4*>(sDgam + BlkStage<K, V>::brow(m)) = part;
   }
   __syncthreads();
-  zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, V, true>(acc, smem + oVn, PK, smem + odS, PK, TCV::r0(w), TCV::c0(w), lane);
-#pragma unroll
-  for (int bm = 0; bm < TCV::BM; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < TCV::BN; ++bn)
-      *reinterpret_cast<floatx4*>(P.DKG + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+  zero_acc(kKG);
+  mfma_rows<TCV::BM, TCV::BN, V, false>(kKG, smem + oVn, PK, smem + odS, PK, r0v, c0v, lane);
   __syncthreads();
 
-  // ---- phase 4: dQg = dO S^T, dW = -dVn S^T, dAqk = Tril(dO Vn^T)
+  // ---- phase 4: dQg = dO S^T (kept), dW = -dVn S^T, dAqk = Tril(dO Vn^T) (kept)
 #pragma unroll
   for (int m = 0; m < PDO; ++m)
     if (do_has(m)) {
@@ -1170,108 +1268,339 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_mfma_kernel(BwdArgs a) {
       for (int r = 0; r < 4; ++r) *reinterpret_cast<bf16x4*>(smem + odO + (do_row(m) + r) * PK + do_col(m)) = rdO[m][r];
     }
   rS.store(smem + oS);
+  // v in the C x V tiling's layout, for the dbeta term of dVb in phase 5
+  float vt[TCV::BM][TCV::BN][4];
+  {
+    const bf16* vin = reinterpret_cast<const bf16*>(a.v);
+#pragma unroll
+    for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < TCV::BN; ++bn)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = r0v + 16 * bm + 4 * g + r, rr = row < it.len ? row : 0;
+          const float x = to_f32(vin[((size_t)(it.tok0 + rr) * H + it.h) * V + c0v + 16 * bn + i]);
+          vt[bm][bn][r] = row < it.len ? x : 0.f;
+        }
+  }
   __syncthreads();
+  zero_acc(kQG);
+  mfma_rows<TCV::BM, TCV::BN, V, false>(kQG, smem + odO, PK, smem + oS, PK, r0v, c0v, lane);
   zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, V, true>(acc, smem + odO, PK, smem + oS, PK, TCV::r0(w), TCV::c0(w), lane);
-#pragma unroll
-  for (int bm = 0; bm < TCV::BM; ++bm)
-#pragma unroll
-    for (int bn = 0; bn < TCV::BN; ++bn)
-      *reinterpret_cast<floatx4*>(P.DQG + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
-  zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, V, false>(acc, smem + odVn, PK, smem + oS, PK, TCV::r0(w), TCV::c0(w), lane);
+  mfma_rows<TCV::BM, TCV::BN, V, false>(acc, smem + odVn, PK, smem + oS, PK, r0v, c0v, lane);
 #pragma unroll
   for (int bm = 0; bm < TCV::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCV::BN; ++bn) {
-      const int R0 = TCV::r0(w) + 16 * bm, C0 = TCV::c0(w) + 16 * bn;
+      const int R0 = r0v + 16 * bm, C0 = c0v + 16 * bn;
       const bf16x4 y = to_bf16x4(-acc[bm][bn]);
       *reinterpret_cast<bf16x4*>(smem + odWT + (C0 + i) * PC + R0 + 4 * g) = y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) smem[odW + (R0 + 4 * g + r) * PK + C0 + i] = y[r];
     }
-  zero_acc(acc2);
-  mfma_rows<TCC::BM, TCC::BN, V, true>(acc2, smem + odO, PK, smem + oVn, PK, TCC::r0(w), TCC::c0(w), lane);
+  zero_acc(kAQ);
+  mfma_rows<TCC::BM, TCC::BN, V, true>(kAQ, smem + odO, PK, smem + oVn, PK, r0c, c0c, lane);
 #pragma unroll
   for (int bm = 0; bm < TCC::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCC::BN; ++bn) {
-      const int row = TCC::r0(w) + 16 * bm + i, col = TCC::c0(w) + 16 * bn + 4 * g;
-      floatx4 y = acc2[bm][bn];
+      const int row = r0c + 16 * bm + i, col = c0c + 16 * bn + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = col + r <= row ? y[r] : 0.f;
-      *reinterpret_cast<floatx4*>(P.DAQK + row * C + col) = y;
+      for (int r = 0; r < 4; ++r) kAQ[bm][bn][r] = col + r <= row ? kAQ[bm][bn][r] : 0.f;
     }
   __syncthreads();
 
-  // ---- phase 5: dA = dW Kb^T + dVn Vb^T (kept as dA^T), dKb = A^T dW, dVb = A^T dVn
+  // ---- phase 5: dA = dW Kb^T + dVn Vb^T (kept as dA^T), dKb = A^T dW (kept),
+  // dVb = A^T dVn -> dv = beta dVb and the dbeta term dVb . v
   rKb.store(smem + oKb);
   rVb.store(smem + oVb);
   rA.store_t(smem + oAT);
   __syncthreads();
   zero_acc(acc2);
-  mfma_rows<TCC::BM, TCC::BN, K, false>(acc2, smem + odW, PK, smem + oKb, PK, TCC::r0(w), TCC::c0(w), lane);
-  mfma_rows<TCC::BM, TCC::BN, V, false>(acc2, smem + odVn, PK, smem + oVb, PK, TCC::r0(w), TCC::c0(w), lane);
+  mfma_rows<TCC::BM, TCC::BN, K, false>(acc2, smem + odW, PK, smem + oKb, PK, r0c, c0c, lane);
+  mfma_rows<TCC::BM, TCC::BN, V, false>(acc2, smem + odVn, PK, smem + oVb, PK, r0c, c0c, lane);
 #pragma unroll
   for (int bm = 0; bm < TCC::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCC::BN; ++bn)
-      *reinterpret_cast<bf16x4*>(smem + odAT + (TCC::c0(w) + 16 * bn + i) * PC + TCC::r0(w) + 16 * bm + 4 * g) =
+      *reinterpret_cast<bf16x4*>(smem + odAT + (c0c + 16 * bn + i) * PC + r0c + 16 * bm + 4 * g) =
           to_bf16x4(acc2[bm][bn]);
+  zero_acc(kKB);
+  mfma_rows<TCV::BM, TCV::BN, C, false>(kKB, smem + oAT, PC, smem + odWT, PC, r0v, c0v, lane);
   zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, C, true>(acc, smem + oAT, PC, smem + odWT, PC, TCV::r0(w), TCV::c0(w), lane);
+  mfma_rows<TCV::BM, TCV::BN, C, false>(acc, smem + oAT, PC, smem + odVnT, PC, r0v, c0v, lane);
 #pragma unroll
-  for (int bm = 0; bm < TCV::BM; ++bm)
+  for (int bm = 0; bm < TCV::BM; ++bm) {
+    floatx4 part = zero4();
 #pragma unroll
-    for (int bn = 0; bn < TCV::BN; ++bn)
-      *reinterpret_cast<floatx4*>(P.DKB + (TCV::r0(w) + 16 * bm + i) * K + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
-  zero_acc(acc);
-  mfma_rows<TCV::BM, TCV::BN, C, true>(acc, smem + oAT, PC, smem + odVnT, PC, TCV::r0(w), TCV::c0(w), lane);
+    for (int r = 0; r < 4; ++r) {
+      const int row = r0v + 16 * bm + 4 * g + r;
+      const float b = P.BETA[row];
 #pragma unroll
-  for (int bm = 0; bm < TCV::BM; ++bm)
+      for (int bn = 0; bn < TCV::BN; ++bn) {
+        part[r] += acc[bm][bn][r] * vt[bm][bn][r];
+        if (row < it.len) a.dv[((size_t)(it.tok0 + row) * H + it.h) * V + c0v + 16 * bn + i] = b * acc[bm][bn][r];
+      }
+    }
+    // over the 16 columns of each tile (lanes i of one group g)
 #pragma unroll
-    for (int bn = 0; bn < TCV::BN; ++bn)
-      *reinterpret_cast<floatx4*>(P.DVB + (TCV::r0(w) + 16 * bm + i) * V + TCV::c0(w) + 16 * bn + 4 * g) = acc[bm][bn];
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[r] += __shfl_xor(part[r], off, 64);
+    if (i == 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sDbP[(w % TCV::WC) * C + r0v + 16 * bm + 4 * g + r] = part[r];
+  }
   __syncthreads();
 
-  // ---- phase 6: T1 = A^T dA (A staged for phase 7 over dead dVn / dVn^T)
+  // ---- phase 6: T1 = A^T dA (A staged for phase 7 over dead dVn / dVn^T);
+  // loads of the elementwise phase: q, k, g rows (zero past the chunk end) and
+  // the row norms
+  constexpr int N4 = C * K / 4 / kMT;
+  static_assert(N4 >= 1 && N4 * 4 * kMT == C * K, "staging split");
+  floatx4 rq4[N4], rk4[N4], rg4[N4];
+  float qinv[N4], kinv[N4];
+  {
+    auto in_idx = [&](int m) {
+      const int e = tid + kMT * m, row = e / (K / 4), c = 4 * (e % (K / 4)), rr = row < it.len ? row : 0;
+      return ((size_t)(it.tok0 + rr) * H + it.h) * K + c;
+    };
+#pragma unroll
+    for (int m = 0; m < N4; ++m) {
+      rq4[m] = load4_f32(reinterpret_cast<const bf16*>(a.q) + in_idx(m));
+      rk4[m] = load4_f32(reinterpret_cast<const bf16*>(a.k) + in_idx(m));
+    }
+    if (a.g_f32) {
+#pragma unroll
+      for (int m = 0; m < N4; ++m) rg4[m] = load4_f32(reinterpret_cast<const float*>(a.g) + in_idx(m));
+    } else {
+#pragma unroll
+      for (int m = 0; m < N4; ++m) rg4[m] = load4_f32(reinterpret_cast<const bf16*>(a.g) + in_idx(m));
+    }
+#pragma unroll
+    for (int m = 0; m < N4; ++m) {
+      const int row = (tid + kMT * m) / (K / 4);
+      qinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nq + row], a.l2eps) : 1.f;
+      kinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nk + row], a.l2eps) : 1.f;
+    }
+  }
   rA.store(smem + oA);
   zero_acc(acc2);
-  mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oAT, PC, smem + odAT, PC, TCC::r0(w), TCC::c0(w), lane);
+  mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oAT, PC, smem + odAT, PC, r0c, c0c, lane);
 #pragma unroll
   for (int bm = 0; bm < TCC::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCC::BN; ++bn)
-      *reinterpret_cast<bf16x4*>(smem + oT1 + (TCC::r0(w) + 16 * bm + i) * PC + TCC::c0(w) + 16 * bn + 4 * g) =
+      *reinterpret_cast<bf16x4*>(smem + oT1 + (r0c + 16 * bm + i) * PC + c0c + 16 * bn + 4 * g) =
           to_bf16x4(acc2[bm][bn]);
   __syncthreads();
 
-  // ---- phase 7: dL = -StrictTril(T1 A^T)
-  zero_acc(acc2);
-  mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oT1, PC, smem + oA, PC, TCC::r0(w), TCC::c0(w), lane);
+  // ---- phase 7: dL = -StrictTril(T1 A^T) (kept)
+  zero_acc(kDL);
+  mfma_rows<TCC::BM, TCC::BN, C, true>(kDL, smem + oT1, PC, smem + oA, PC, r0c, c0c, lane);
 #pragma unroll
   for (int bm = 0; bm < TCC::BM; ++bm)
 #pragma unroll
     for (int bn = 0; bn < TCC::BN; ++bn) {
-      const int row = TCC::r0(w) + 16 * bm + i, col = TCC::c0(w) + 16 * bn + 4 * g;
-      floatx4 y;
+      const int row = r0c + 16 * bm + i, col = c0c + 16 * bn + 4 * g;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] = col + r < row ? -acc2[bm][bn][r] : 0.f;
-      *reinterpret_cast<floatx4*>(P.DL + row * C + col) = y;
+      for (int r = 0; r < 4; ++r) kDL[bm][bn][r] = col + r < row ? -kDL[bm][bn][r] : 0.f;
     }
+  __syncthreads();
+
+  // ---- elementwise phase (the LDS now holds the fp32 layout)
+  float* sG = sF + fG;
+  float* sKN = sF + fKN;
+  float* sQN = sF + fQN;
+  float* sP = sF + fP;
+  float* sDM = sF + fDM;
+  float* sDotP = sF + fDotP;   // [NCT][2 C]
+  float* sBT = sF + fBT;       // [4][K]
+  float* sDGlP = sF + fDGlP;   // [WRV][K]
+#pragma unroll
+  for (int m = 0; m < N4; ++m) {
+    const int e = tid + kMT * m, row = e / (K / 4);
+    const bool in = row < it.len;
+    reinterpret_cast<floatx4*>(sQN)[e] = in ? (a.l2norm ? rq4[m] * qinv[m] : rq4[m]) : zero4();
+    reinterpret_cast<floatx4*>(sKN)[e] = in ? (a.l2norm ? rk4[m] * kinv[m] : rk4[m]) : zero4();
+    reinterpret_cast<floatx4*>(sG)[e] = in ? rg4[m] : zero4();
+  }
+  if (tid < C) sBeta[tid] = P.BETA[tid];
+  // dAqk and Diag(beta) dL (rows i, columns 4 g + r of each tile); the dbeta
+  // term dL . M over the lane's columns, then the tile's lane groups
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm) {
+    const int row = r0c + 16 * bm + i;
+    const float b = P.BETA[row];
+    float part = 0.f;
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn) {
+      const int col = c0c + 16 * bn + 4 * g;
+      const floatx4 mm = *reinterpret_cast<const floatx4*>(P.Mm + row * C + col);
+      *reinterpret_cast<floatx4*>(sP + row * CP + col) = kAQ[bm][bn];
+      *reinterpret_cast<floatx4*>(sDM + row * CP + col) = b * kDL[bm][bn];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += kDL[bm][bn][r] * mm[r];
+    }
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (g == 0) sDbP[(2 * TCV::WC + w % TCC::WC) * C + row] = part;
+  }
+  // column sums of dKG * KG over the wave's rows (for the gradient of the last
+  // row's cumulative gate), per wave row of the C x K tiling
+#pragma unroll
+  for (int bn = 0; bn < TCV::BN; ++bn) {
+    const int col = c0v + 16 * bn + i;
+    float part = 0.f;
+#pragma unroll
+    for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part += kKG[bm][bn][r] * P.KG[(r0v + 16 * bm + 4 * g + r) * K + col];
+    part += __shfl_xor(part, 16, 64);
+    part += __shfl_xor(part, 32, 64);
+    if (g == 0) sDGlP[(w / TCV::WC) * K + col] = part;
+  }
+  __syncthreads();
+  // gate cumsum in place, sequential over the rows of each channel (bitwise the
+  // chunk-term kernel's G); the last row's gate gradient from its parts
+  if (tid < K) {
+    float run = 0.f;
+    for (int r = 0; r < C; ++r) {
+      run += sG[r * K + tid];
+      sG[r * K + tid] = run;
+    }
+  } else if (tid < 2 * K) {
+    const int d = tid - K;
+    float acc1 = sDgam[d] * P.GAM[d];
+#pragma unroll
+    for (int q = 0; q < WRV; ++q) acc1 += sDGlP[q * K + d];
+    sDGl[d] = acc1;
+  }
+  __syncthreads();
+
+  // tiles of the C x K tiling (the wave's own): the gated sums, the elementwise
+  // rules; dq, dk leave here (with the L2 flag as the gradients of the
+  // normalised rows, completed below); the within-tile reverse sums of dG stay
+  // in registers; the dbeta term dKb . (k^ e^G)
+  const float s = a.scale;
+  float sfx[TCV::BM][TCV::BN][4];
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm) {
+    floatx4 dbk = zero4();
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn) {
+      const int ib = (r0v >> 4) + bm, ct = (c0v >> 4) + bn, d = 16 * ct + i;
+      floatx4 qa, qm, ka, km;
+      gated_sums<K>(sG, sKN, sQN, sP, sDM, ib, d, g, i, qa, qm, ka, km);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ib + 4 * g + r;
+        const float qi = sQN[row * K + d], ki = sKN[row * K + d];
+        float gqn, gkn;
+        elem_rules<K>(sG, sQN, sKN, sBeta, sDGl, row, d, s, kQG[bm][bn][r], kKB[bm][bn][r], kKG[bm][bn][r], qa[r],
+                      qm[r], ka[r], km[r], gqn, gkn, sfx[bm][bn][r]);
+        dbk[r] += kKB[bm][bn][r] * ki * __expf(sG[row * K + d]);
+        if (row < it.len) {
+          const size_t idx = ((size_t)(it.tok0 + row) * H + it.h) * K + d;
+          a.dq[idx] = gqn;
+          a.dk[idx] = gkn;
+        }
+        if (a.l2norm) {
+          float pq = qi * gqn, pk = ki * gkn;
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) {
+            pq += __shfl_xor(pq, off, 64);
+            pk += __shfl_xor(pk, off, 64);
+          }
+          if (i == 0) {
+            sDotP[ct * 2 * C + row] = pq;
+            sDotP[ct * 2 * C + C + row] = pk;
+          }
+        }
+      }
+      // dg: reverse sums within the lane's 4 rows, then over the later lane
+      // groups of the tile; the later 16-row blocks are added below
+#pragma unroll
+      for (int r = 2; r >= 0; --r) sfx[bm][bn][r] += sfx[bm][bn][r + 1];
+      float tot[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[q] = __shfl(sfx[bm][bn][0], 16 * q + i, 64);
+      float later = 0.f;
+#pragma unroll
+      for (int q = 3; q >= 1; --q) later += q > g ? tot[q] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sfx[bm][bn][r] += later;
+      if (g == 0) sBT[ib * K + d] = ((tot[3] + tot[2]) + tot[1]) + tot[0];
+    }
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dbk[r] += __shfl_xor(dbk[r], off, 64);
+    if (i == 0)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sDbP[(TCV::WC + w % TCV::WC) * C + r0v + 16 * bm + 4 * g + r] = dbk[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn) {
+      const int ib = (r0v >> 4) + bm, d = c0v + 16 * bn + i;
+      float after = 0.f;
+#pragma unroll
+      for (int b = 3; b >= 1; --b) after += b > ib ? sBT[b * K + d] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * ib + 4 * g + r;
+        if (row < it.len) a.dg[((size_t)(it.tok0 + row) * H + it.h) * K + d] = sfx[bm][bn][r] + after;
+      }
+    }
+  if (tid < C && tid < it.len) {
+    float db = 0.f;
+#pragma unroll
+    for (int q = 0; q < kDbSlots; ++q) db += sDbP[q * C + tid];
+    a.dbeta[(size_t)(it.tok0 + tid) * H + it.h] = db;
+  }
+  // L2-norm backward: dq = (dq^ - q^ (q^ . dq^)) / |q| (dq^ / eps where the norm
+  // is clamped), likewise dk; each lane completes the elements it stored
+  if (a.l2norm) {
+    if (tid < 2 * C) {
+      float acc1 = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc1 += sDotP[ct * 2 * C + tid];
+      sDot[tid] = acc1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+      for (int bn = 0; bn < TCV::BN; ++bn) {
+        const int ib = (r0v >> 4) + bm, d = c0v + 16 * bn + i;
+        float gqv[4], gkv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * ib + 4 * g + r;
+          const size_t idx = ((size_t)(it.tok0 + (row < it.len ? row : 0)) * H + it.h) * K + d;
+          gqv[r] = a.dq[idx];
+          gkv[r] = a.dk[idx];
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * ib + 4 * g + r;
+          if (row < it.len) {
+            const size_t idx = ((size_t)(it.tok0 + row) * H + it.h) * K + d;
+            const float nq = sl[o.nq + row], nk = sl[o.nk + row];
+            a.dq[idx] = nq > a.l2eps ? (gqv[r] - sQN[row * K + d] * sDot[row]) / nq : gqv[r] / a.l2eps;
+            a.dk[idx] = nk > a.l2eps ? (gkv[r] - sKN[row * K + d] * sDot[C + row]) / nk : gkv[r] / a.l2eps;
+          }
+        }
+      }
+  }
 }
 
-// the elementwise and gated-sum rules, the L2-norm backward and the reverse
-// cumsum. The four gated sums (per row i, channel d; P = dAqk, dM = Diag(beta) dL,
-// E_ij = exp(G_i - G_j))
-//   query side  sum_{j<=i} P_ij k_j E_ij,   sum_{j<i} dM_ij k_j E_ij
-//   key side    sum_{r>=i} P_ri q_r E_ri,   sum_{r>i} dM_ri k_r E_ri
-// run as fp32 MFMA products over 16-row blocks with one reference per block
-// (the rebasing of "KDA Doesn't Care About the Future", section "The rebasing
-// trick"): with rho_b = G of the first row of block b, a key j of block b
-// carries exp(rho_b - G_j) (at most 15 steps of decay) and the query row
-// exp(G_i - rho_b) <= 1 for i >= 16 b; the key side uses the reference of row
-// i's own block the same way.
+// the elementwise and gated-sum rules (gated_sums, elem_rules), the L2-norm
+// backward and the reverse cumsum, for fp32 q/k/v (bf16 input runs them inside
+// bwd_chunk_fused_kernel)
 template <int K>
 __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
   constexpr int V = K;
@@ -1401,58 +1730,15 @@ __global__ __launch_bounds__(kBW) void bwd_chunk_elem_kernel(BwdArgs a) {
     const int tile = w + kNWW * t;
     const int ib = tile / NCT, ct = tile % NCT;
     const int d = 16 * ct + xi;
-    floatx4 qa = zero4(), qm = zero4(), ka = zero4(), km = zero4();
-    // query side: key blocks b <= ib
-    for (int b = 0; b <= ib; ++b) {
-      const float rho = sG[(16 * b) * K + d];
-      floatx4 accA = zero4(), accM = zero4();
-#pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4) {
-        const int j = 16 * b + k0 + gq;
-        const float kf = sKN[j * K + d] * __expf(rho - sG[j * K + d]);
-        accA = mfma4(sP[(16 * ib + xi) * CP + j], kf, accA);
-        accM = mfma4(sDM[(16 * ib + xi) * CP + j], kf, accM);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __expf(sG[(16 * ib + 4 * gq + r) * K + d] - rho);
-        qa[r] += e * accA[r];
-        qm[r] += e * accM[r];
-      }
-    }
-    // key side: query blocks b >= ib, reference of block ib
-    {
-      const float rho = sG[(16 * ib) * K + d];
-      for (int b = ib; b < 4; ++b) {
-#pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) {
-          const int r = 16 * b + k0 + gq;
-          const float e = __expf(sG[r * K + d] - rho);
-          ka = mfma4(sP[r * CP + 16 * ib + xi], sQN[r * K + d] * e, ka);
-          km = mfma4(sDM[r * CP + 16 * ib + xi], sKN[r * K + d] * e, km);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float f = __expf(rho - sG[(16 * ib + 4 * gq + r) * K + d]);
-        ka[r] *= f;
-        km[r] *= f;
-      }
-    }
+    floatx4 qa, qm, ka, km;
+    gated_sums<K>(sG, sKN, sQN, sP, sDM, ib, d, gq, xi, qa, qm, ka, km);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = 16 * ib + 4 * gq + r;
-      const float Gi = sG[i * K + d], qi = sQN[i * K + d], ki = sKN[i * K + d], bi = sBeta[i];
-      const float Gl = sG[(C - 1) * K + d];
-      const float eg = __expf(Gi), egl = __expf(Gl - Gi);
-      const float dqg = pdqg[t][r], dkb = pdkb[t][r], dkg = pdkg[t][r];
-      const float gqn = s * eg * dqg + s * qa[r];
-      const float gkn = dkb * bi * eg + dkg * egl + s * ka[r] + qm[r] + km[r];
-      // Qg = s q e^G, Kb = beta k e^G and KG = k e^(Gl - G) rebuilt from the staged rows
-      float dG = dqg * (s * qi * eg) + dkb * (bi * ki * eg) - dkg * (ki * egl) + qi * s * qa[r] -
-                 ki * s * ka[r] + ki * qm[r] - ki * km[r];
-      if (i == C - 1) dG += sDGl[d];
-      sfx[t][r] = dG;
+      const float qi = sQN[i * K + d], ki = sKN[i * K + d];
+      float gqn, gkn;
+      elem_rules<K>(sG, sQN, sKN, sBeta, sDGl, i, d, s, pdqg[t][r], pdkb[t][r], pdkg[t][r], qa[r], qm[r], ka[r],
+                    km[r], gqn, gkn, sfx[t][r]);
       if (i < it.len) {
         const size_t idx = ((size_t)(it.tok0 + i) * H + it.h) * K + d;
         a.dq[idx] = gqn;
@@ -1591,9 +1877,12 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
     if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
   }
   if ((stages & 8) && nitems > 0) {
-    if (a.bf16_qkv) hipLaunchKernelGGL(bwd_chunk_mfma_kernel<K>, dim3(nitems), dim3(kMT), 0, s, a);
-    else hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
-    hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
+    if (a.bf16_qkv) {
+      hipLaunchKernelGGL(bwd_chunk_fused_kernel<K>, dim3(nitems), dim3(kMT), 0, s, a);
+    } else {
+      hipLaunchKernelGGL(bwd_chunk_mm_kernel<K>, dim3(nitems), dim3(kBT), 0, s, a);
+      hipLaunchKernelGGL(bwd_chunk_elem_kernel<K>, dim3(nitems), dim3(kBW), 0, s, a);
+    }
   }
   return hipGetLastError();
 }
