@@ -1151,10 +1151,8 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
     for (int bn = 0; bn < TCV::BN; ++bn)
       rU[bm][bn] = *reinterpret_cast<const floatx4*>(P.U + (r0v + 16 * bm + i) * V + c0v + 16 * bn + 4 * g);
 
-  // ---- phase 1: Vn = U - W S
-  rW.store(smem + oW);
-  rS.store_t(smem + oST);
-  // loads of phase 2: Aqk, dO (bf16 rows of the chunk, zero past its end), KG, dS'
+  // loads of phase 2, issued with those of phase 1: Aqk, dO (bf16 rows of the
+  // chunk; rows past its end are zeroed where they are staged), KG, dS'
   BlkStage<C, C> rAq;
   rAq.load(P.AQK);
   constexpr int NDO = (C / 4) * (V / 4), PDO = (NDO + kMT - 1) / kMT;
@@ -1162,6 +1160,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   auto do_has = [&](int m) { return NDO % kMT == 0 || tid + kMT * m < NDO; };
   auto do_row = [&](int m) { return 4 * ((tid + kMT * m) / (V / 4)); };
   auto do_col = [&](int m) { return 4 * ((tid + kMT * m) % (V / 4)); };
+  auto do_val = [&](int m, int r) { return do_row(m) + r < it.len ? rdO[m][r] : bf16x4{0, 0, 0, 0}; };
   {
     const bf16* dO = reinterpret_cast<const bf16*>(a.d_o);
 #pragma unroll
@@ -1172,15 +1171,16 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
           const int row = do_row(m) + r, rr = row < it.len ? row : 0;
           rdO[m][r] = *reinterpret_cast<const bf16x4*>(dO + ((size_t)(it.tok0 + rr) * H + it.h) * V + do_col(m));
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (do_row(m) + r >= it.len) rdO[m][r] = bf16x4{0, 0, 0, 0};
       }
   }
   NatStage<C, K> rKG;
   rKG.load(P.KG);
   BlkStage<K, V> rdS;
   rdS.load(P.DS);
+
+  // ---- phase 1: Vn = U - W S
+  rW.store(smem + oW);
+  rS.store_t(smem + oST);
   __syncthreads();
   zero_acc(acc);
   mfma_rows<TCV::BM, TCV::BN, K, true>(acc, smem + oW, PK, smem + oST, PK, r0v, c0v, lane);
@@ -1197,10 +1197,10 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = 0; m < PDO; ++m)
     if (do_has(m)) {
+      const bf16x4 d0 = do_val(m, 0), d1 = do_val(m, 1), d2 = do_val(m, 2), d3 = do_val(m, 3);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<bf16x4*>(smem + odOT + (do_col(m) + c) * PC + do_row(m)) =
-            bf16x4{rdO[m][0][c], rdO[m][1][c], rdO[m][2][c], rdO[m][3][c]};
+        *reinterpret_cast<bf16x4*>(smem + odOT + (do_col(m) + c) * PC + do_row(m)) = bf16x4{d0[c], d1[c], d2[c], d3[c]};
     }
   rKG.store(smem + oKG);
   rdS.store_t(smem + odST);
@@ -1265,11 +1265,16 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   for (int m = 0; m < PDO; ++m)
     if (do_has(m)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<bf16x4*>(smem + odO + (do_row(m) + r) * PK + do_col(m)) = rdO[m][r];
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<bf16x4*>(smem + odO + (do_row(m) + r) * PK + do_col(m)) = do_val(m, r);
     }
   rS.store(smem + oS);
-  // v in the C x V tiling's layout, for the dbeta term of dVb in phase 5
-  float vt[TCV::BM][TCV::BN][4];
+  // v in the C x V tiling's layout, for the dbeta term of dVb in phase 5, and
+  // beta of the tiling's rows, for dv
+  float vt[TCV::BM][TCV::BN][4], bta[TCV::BM][4];
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bta[bm][r] = P.BETA[r0v + 16 * bm + 4 * g + r];
   {
     const bf16* vin = reinterpret_cast<const bf16*>(a.v);
 #pragma unroll
@@ -1335,7 +1340,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = r0v + 16 * bm + 4 * g + r;
-      const float b = P.BETA[row];
+      const float b = bta[bm][r];
 #pragma unroll
       for (int bn = 0; bn < TCV::BN; ++bn) {
         part[r] += acc[bm][bn][r] * vt[bm][bn][r];
@@ -1380,10 +1385,29 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
 #pragma unroll
     for (int m = 0; m < N4; ++m) {
       const int row = (tid + kMT * m) / (K / 4);
-      qinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nq + row], a.l2eps) : 1.f;
-      kinv[m] = a.l2norm ? 1.f / fmaxf(sl[o.nk + row], a.l2eps) : 1.f;
+      qinv[m] = a.l2norm ? sl[o.nq + row] : 1.f;   // row norms; inverted when staged
+      kinv[m] = a.l2norm ? sl[o.nk + row] : 1.f;
     }
   }
+  // and the elementwise phase's slab operands: M and beta over the C x C
+  // tiling, KG over the C x K tiling, beta of row tid, gamma of channel tid - K
+  floatx4 rMm[TCC::BM][TCC::BN];
+  float bdl[TCC::BM], rKGt[TCV::BM][TCV::BN][4];
+#pragma unroll
+  for (int bm = 0; bm < TCC::BM; ++bm) {
+    bdl[bm] = P.BETA[r0c + 16 * bm + i];
+#pragma unroll
+    for (int bn = 0; bn < TCC::BN; ++bn)
+      rMm[bm][bn] = *reinterpret_cast<const floatx4*>(P.Mm + (r0c + 16 * bm + i) * C + c0c + 16 * bn + 4 * g);
+  }
+#pragma unroll
+  for (int bm = 0; bm < TCV::BM; ++bm)
+#pragma unroll
+    for (int bn = 0; bn < TCV::BN; ++bn)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rKGt[bm][bn][r] = P.KG[(r0v + 16 * bm + 4 * g + r) * K + c0v + 16 * bn + i];
+  const float rbeta0 = tid < C ? P.BETA[tid] : 0.f;
+  const float rgam = tid >= K && tid < 2 * K ? P.GAM[tid - K] : 0.f;
   rA.store(smem + oA);
   zero_acc(acc2);
   mfma_rows<TCC::BM, TCC::BN, C, true>(acc2, smem + oAT, PC, smem + odAT, PC, r0c, c0c, lane);
@@ -1421,22 +1445,23 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   for (int m = 0; m < N4; ++m) {
     const int e = tid + kMT * m, row = e / (K / 4);
     const bool in = row < it.len;
-    reinterpret_cast<floatx4*>(sQN)[e] = in ? (a.l2norm ? rq4[m] * qinv[m] : rq4[m]) : zero4();
-    reinterpret_cast<floatx4*>(sKN)[e] = in ? (a.l2norm ? rk4[m] * kinv[m] : rk4[m]) : zero4();
+    const float qi = 1.f / fmaxf(qinv[m], a.l2eps), ki = 1.f / fmaxf(kinv[m], a.l2eps);
+    reinterpret_cast<floatx4*>(sQN)[e] = in ? (a.l2norm ? rq4[m] * qi : rq4[m]) : zero4();
+    reinterpret_cast<floatx4*>(sKN)[e] = in ? (a.l2norm ? rk4[m] * ki : rk4[m]) : zero4();
     reinterpret_cast<floatx4*>(sG)[e] = in ? rg4[m] : zero4();
   }
-  if (tid < C) sBeta[tid] = P.BETA[tid];
+  if (tid < C) sBeta[tid] = rbeta0;
   // dAqk and Diag(beta) dL (rows i, columns 4 g + r of each tile); the dbeta
   // term dL . M over the lane's columns, then the tile's lane groups
 #pragma unroll
   for (int bm = 0; bm < TCC::BM; ++bm) {
     const int row = r0c + 16 * bm + i;
-    const float b = P.BETA[row];
+    const float b = bdl[bm];
     float part = 0.f;
 #pragma unroll
     for (int bn = 0; bn < TCC::BN; ++bn) {
       const int col = c0c + 16 * bn + 4 * g;
-      const floatx4 mm = *reinterpret_cast<const floatx4*>(P.Mm + row * C + col);
+      const floatx4 mm = rMm[bm][bn];
       *reinterpret_cast<floatx4*>(sP + row * CP + col) = kAQ[bm][bn];
       *reinterpret_cast<floatx4*>(sDM + row * CP + col) = b * kDL[bm][bn];
 #pragma unroll
@@ -1455,7 +1480,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
 #pragma unroll
     for (int bm = 0; bm < TCV::BM; ++bm)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) part += kKG[bm][bn][r] * P.KG[(r0v + 16 * bm + 4 * g + r) * K + col];
+      for (int r = 0; r < 4; ++r) part += kKG[bm][bn][r] * rKGt[bm][bn][r];
     part += __shfl_xor(part, 16, 64);
     part += __shfl_xor(part, 32, 64);
     if (g == 0) sDGlP[(w / TCV::WC) * K + col] = part;
@@ -1471,7 +1496,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
     }
   } else if (tid < 2 * K) {
     const int d = tid - K;
-    float acc1 = sDgam[d] * P.GAM[d];
+    float acc1 = sDgam[d] * rgam;
 #pragma unroll
     for (int q = 0; q < WRV; ++q) acc1 += sDGlP[q * K + d];
     sDGl[d] = acc1;
