@@ -564,8 +564,16 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
       for (int m = 0; m < NSC; ++m) rS[m] = sST[(lt & 15) * SP + (lt >> 4) + 16 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
+      // with bf16 q/k/v the product kernel reads S as bf16 (its MFMA operand
+      // type), so it is stored rounded, in the first half of its slab array
+      if (a.bf16_qkv) {
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) sl[o.S + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+        for (int m = 0; m < NSC; ++m)
+          reinterpret_cast<bf16*>(sl + o.S)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = (bf16)rS[m];
+      } else {
+#pragma unroll
+        for (int m = 0; m < NSC; ++m) sl[o.S + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+      }
       if (cc + 1 < nch) stage(cur, (cc + 1) & 1);
     };
     if (nch > 0) {
@@ -773,8 +781,15 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       for (int m = 0; m < NSC; ++m) rS[m] = sdST[(lt & 15) * SP + (lt >> 4) + 16 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
+      // the gradient of the chunk-end state; bf16 for bf16 q/k/v, as S
+      if (a.bf16_qkv) {
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];  // gradient of the chunk-end state
+        for (int m = 0; m < NSC; ++m)
+          reinterpret_cast<bf16*>(sl + o.dS)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = (bf16)rS[m];
+      } else {
+#pragma unroll
+        for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+      }
       if (cc > 0) stage1(cur, (cc - 1) & 1);
       fetch1(cur, cc - 3);
       __syncthreads();  // C
@@ -1060,6 +1075,15 @@ struct BlkStage {
         for (int r = 0; r < 4; ++r) v[m][r] = *reinterpret_cast<const floatx4*>(src + (brow(m) + r) * COLS + bcol(m));
       }
   }
+  // the same blocks from a bf16 [ROWS][COLS] matrix, widened
+  __device__ void load(const bf16* src) {
+#pragma unroll
+    for (int m = 0; m < N; ++m)
+      if (has(m)) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[m][r] = load4_f32(src + (brow(m) + r) * COLS + bcol(m));
+      }
+  }
   __device__ void store(bf16* dst) const {
 #pragma unroll
     for (int m = 0; m < N; ++m)
@@ -1143,7 +1167,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   NatStage<C, K> rW;
   BlkStage<K, V> rS;
   rW.load(P.W);
-  rS.load(P.S);
+  rS.load(reinterpret_cast<const bf16*>(P.S));
   floatx4 rU[TCV::BM][TCV::BN];
 #pragma unroll
   for (int bm = 0; bm < TCV::BM; ++bm)
@@ -1176,7 +1200,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   NatStage<C, K> rKG;
   rKG.load(P.KG);
   BlkStage<K, V> rdS;
-  rdS.load(P.DS);
+  rdS.load(reinterpret_cast<const bf16*>(P.DS));
 
   // ---- phase 1: Vn = U - W S
   rW.store(smem + oW);

@@ -106,7 +106,7 @@ struct BwdSlab {
   size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
   size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
   // chunk-start state and the gradient of the chunk-end state
-  size_t S, dS;                      // [K][V]
+  size_t S, dS;                      // [K][V] (bf16, in the first half, for bf16 q/k/v)
   // per-chunk gradients
   size_t dO, vn, dvn, dvb;           // [64][V]
   size_t dqg, dw, dkg, dkb;          // [64][K]
