@@ -371,7 +371,8 @@ def bench_backward(args, torch, kda, WORKLOADS, workload):
         "metric": "KDA chunk-bwd tokens/s (dq, dk, dv, dg, dbeta, dh0)", "value": B * T / (ms / 1e3),
         "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16 inputs; chunk products on bf16 MFMA operands with f32 accumulation; f32 states and gradients"
+        "dtype": ("bf16 inputs; chunk and state-gradient products on bf16 MFMA operands with f32 accumulation; "
+                  "f32 states and gradients"
                   if x.dtype == "bf16" else "f32 inputs, f32 arithmetic and gradients"),
         "data": "synthetic (seeded numpy generators)",
         "config": {"workload": WORKLOADS[args.workload]["name"] + "_backward", "B": B, "T": T, "H": H, "K": K,

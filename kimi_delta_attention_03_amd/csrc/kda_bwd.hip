@@ -114,6 +114,8 @@ __device__ __forceinline__ void seq_chunks(const BwdArgs& a, int seq, int& p0, i
   }
 }
 
+__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) { return __builtin_convertvector(x, bf16x4); }
+
 // fp32 16x16x4 MFMA step: lane (g, i) = (l / 16, l % 16) gives A[i][g] and
 // B[g][i] of a 4-deep slice; the accumulator lane holds rows 4 g + r, column i
 __device__ __forceinline__ floatx4 mfma4(float a, float b, floatx4 c) {
@@ -781,15 +783,215 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_kernel(BwdArgs a) {
       for (int m = 0; m < NSC; ++m) rS[m] = sdST[(lt & 15) * SP + (lt >> 4) + 16 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
-      // the gradient of the chunk-end state; bf16 for bf16 q/k/v, as S
-      if (a.bf16_qkv) {
 #pragma unroll
-        for (int m = 0; m < NSC; ++m)
-          reinterpret_cast<bf16*>(sl + o.dS)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = (bf16)rS[m];
-      } else {
-#pragma unroll
-        for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+      for (int m = 0; m < NSC; ++m) sl[o.dS + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];  // gradient of the chunk-end state
+      if (cc > 0) stage1(cur, (cc - 1) & 1);
+      fetch1(cur, cc - 3);
+      __syncthreads();  // C
+      if (cc > 0) stage2();
+      fetch2(cc - 2);
+    };
+    if (nch > 0) {
+      G1 X, Y;  // X: chunks of the parity of nch - 1, Y: the other parity
+      fetch1(X, nch - 1);
+      fetch2(nch - 1);
+      fetch1(Y, nch - 2);
+      stage1(X, (nch - 1) & 1);
+      stage2();
+      fetch1(X, nch - 3);
+      fetch2(nch - 2);
+      // step cc stages chunk cc - 1: from Y when cc = nch - 1, nch - 3, ..., from X otherwise
+      for (int cc = nch - 1; cc >= 0; cc -= 2) {
+        step(cc, Y);
+        if (cc - 1 >= 0) step(cc - 1, X);
       }
+    }
+  }
+}
+
+// State gradients for bf16 q/k/v: the same recurrence, barriers and loader
+// schedule as bwd_states_bwd_kernel, with the products on
+// v_mfma_f32_16x16x32_bf16 (operands rounded to bf16, the input compute dtype,
+// accumulation and the state dS in fp32). Every operand sits in LDS with its
+// reduction index contiguous (rows padded by 8 elements): KG [c][k], Aqk^T
+// [c][j], Qg^T [k][j], W^T [k][j], and dO^T, dVn^T, dS'^T [column][reduction];
+// lane (g, i) supplies reduction indices 32 s + 8 g .. + 7 of row i, one 16-byte
+// read per operand and step. A 16 x 16 result tile keeps the MFMA's layout (rows
+// 4 g + r, column i), so dVn and dS leave as 8-byte transposed writes.
+template <int K>
+__global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a) {
+  constexpr int V = K, NVB = V / 16, TPW = K / 64, NF = C * K / 4 / kBT;
+  constexpr int PK = K + 8, PC = C + 8;  // bf16 row pitches
+  __shared__ __attribute__((aligned(16))) bf16 sKG[C * PK], sAqT[C * PC], sQGT[K * PC], sWT[K * PC];
+  __shared__ __attribute__((aligned(16))) bf16 sdOT[2][16 * PC], sdVnT[16 * PC], sdST[16 * PK];
+  __shared__ float sGam[2][K];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the NVB workgroups of one (sequence, head) get ids congruent modulo 8: with
+  // round-robin dispatch over the 8 XCDs they share one L2 for the chunk operands
+  const int bid = (int)blockIdx.x, slot = bid >> 3;
+  const int u = (slot / NVB) * 8 + (bid & 7), vb = slot % NVB;
+  if (u >= a.nunits) return;
+  const int seq = u / a.H, h = u % a.H;
+  const BwdSlab& o = a.sl;
+  int p0, nch;
+  seq_chunks(a, seq, p0, nch);
+  const int col = 16 * vb + xi;
+
+  if (w < 4) {
+    // ---------------------------------------------------------- compute waves
+    floatx4 dS[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * (TPW * w + t) + 4 * gq + r;
+        dS[t][r] = a.d_final ? a.d_final[((size_t)u * K + row) * V + col] : 0.f;
+      }
+      *reinterpret_cast<bf16x4*>(sdST + xi * PK + 16 * (TPW * w + t) + 4 * gq) = to_bf16x4(dS[t]);
+    }
+    for (int cc = nch - 1; cc >= 0; --cc) {
+      const int b = cc & 1;
+      __syncthreads();  // A
+      // dVn rows 16 w .. 16 w + 15 = Aqk^T dO + KG dS'
+      {
+        floatx4 acc0 = zero4(), acc1 = zero4();
+#pragma unroll
+        for (int s = 0; s < C; s += 32) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sAqT + (16 * w + xi) * PC + s + 8 * gq);
+          const bf16x8 fb = *reinterpret_cast<const bf16x8*>(&sdOT[b][xi * PC + s + 8 * gq]);
+          acc0 = mma32(acc0, fa, fb);
+        }
+#pragma unroll
+        for (int s = 0; s < K; s += 32) {
+          const bf16x8 fa = *reinterpret_cast<const bf16x8*>(sKG + (16 * w + xi) * PK + s + 8 * gq);
+          const bf16x8 fb = *reinterpret_cast<const bf16x8*>(sdST + xi * PK + s + 8 * gq);
+          acc1 = mma32(acc1, fa, fb);
+        }
+        *reinterpret_cast<bf16x4*>(sdVnT + xi * PC + 16 * w + 4 * gq) = to_bf16x4(acc0 + acc1);
+      }
+      __syncthreads();  // B
+      // dS = Diag(gamma) dS' + Qg^T dO - W^T dVn
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int rt = TPW * w + t;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dS[t][r] *= sGam[b][16 * rt + 4 * gq + r];
+        floatx4 acc2 = zero4();
+#pragma unroll
+        for (int s = 0; s < C; s += 32) {
+          const bf16x8 fq = *reinterpret_cast<const bf16x8*>(sQGT + (16 * rt + xi) * PC + s + 8 * gq);
+          const bf16x8 fo = *reinterpret_cast<const bf16x8*>(&sdOT[b][xi * PC + s + 8 * gq]);
+          const bf16x8 fw = *reinterpret_cast<const bf16x8*>(sWT + (16 * rt + xi) * PC + s + 8 * gq);
+          const bf16x8 fv = *reinterpret_cast<const bf16x8*>(sdVnT + xi * PC + s + 8 * gq);
+          dS[t] = mma32(dS[t], fq, fo);
+          acc2 = mma32(acc2, fw, fv);
+        }
+        dS[t] -= acc2;
+        *reinterpret_cast<bf16x4*>(sdST + xi * PK + 16 * rt + 4 * gq) = to_bf16x4(dS[t]);
+      }
+      __syncthreads();  // C
+    }
+    if (a.dh0) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * (TPW * w + t) + 4 * gq + r;
+          a.dh0[((size_t)u * K + row) * V + col] = dS[t][r];
+        }
+    }
+  } else {
+    // ----------------------------------------------------------- loader waves
+    const int lt = tid - kBT;
+    constexpr int NSC = K / 16;
+    // Aqk as 4 x 4 blocks (one per loader thread for C = 64), Qg and W as
+    // [C][K] blocks (two per thread at K = 128), staged transposed
+    constexpr int NBQ = (C / 4) * (K / 4) / kBT;
+    static_assert(NBQ * kBT == (C / 4) * (K / 4) && (C / 4) * (C / 4) <= kBT, "block split");
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    struct G1 {
+      floatx4 kg[NF], aq[4];
+      u32x2 o16;
+      bool ok;
+      float g;
+    };
+    floatx4 rQG[NBQ][4], rW[NBQ][4];
+    const bool aq_has = lt < (C / 4) * (C / 4);
+    const int aq_r = 4 * (lt / (C / 4)), aq_c = 4 * (lt % (C / 4));
+    // loads are unconditional: the chunk index is clamped to 0
+    auto fetch1 = [&](G1& r1, int cc) {
+      cc = cc > 0 ? cc : 0;
+      const float* sl = slab_of(a, p0 + cc, h);
+#pragma unroll
+      for (int m = 0; m < NF; ++m) r1.kg[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        r1.aq[r] = *reinterpret_cast<const floatx4*>(sl + o.aqk + (aq_has ? (aq_r + r) * C + aq_c : 0));
+      const ItemB it = chunk_of(a, p0 + cc, h);
+      const int r = lt >> 2, c0 = 16 * vb + 4 * (lt & 3);
+      r1.ok = r < it.len;
+      const size_t at = ((size_t)(it.tok0 + (r1.ok ? r : 0)) * a.H + h) * V + c0;  // row 0 is always valid
+      r1.o16 = *reinterpret_cast<const u32x2*>(reinterpret_cast<const bf16*>(a.d_o) + at);
+      r1.g = sl[o.gam + (lt < K ? lt : 0)];
+    };
+    auto fetch2 = [&](int cc) {
+      cc = cc > 0 ? cc : 0;
+      const float* sl = slab_of(a, p0 + cc, h);
+#pragma unroll
+      for (int m = 0; m < NBQ; ++m) {
+        const int bl = lt + kBT * m, br = 4 * (bl / (K / 4)), bc = 4 * (bl % (K / 4));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rQG[m][r] = *reinterpret_cast<const floatx4*>(sl + o.qg + (br + r) * K + bc);
+          rW[m][r] = *reinterpret_cast<const floatx4*>(sl + o.w + (br + r) * K + bc);
+        }
+      }
+    };
+    auto stage1 = [&](const G1& r1, int b) {
+#pragma unroll
+      for (int m = 0; m < NF; ++m) {
+        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
+        *reinterpret_cast<bf16x4*>(sKG + r * PK + d) = to_bf16x4(r1.kg[m]);
+      }
+      if (aq_has) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          *reinterpret_cast<bf16x4*>(sAqT + (aq_c + c) * PC + aq_r) =
+              to_bf16x4(floatx4{r1.aq[0][c], r1.aq[1][c], r1.aq[2][c], r1.aq[3][c]});
+      }
+      const bf16x4 dob = r1.ok ? __builtin_bit_cast(bf16x4, r1.o16) : bf16x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sdOT[b][(4 * (lt & 3) + c) * PC + (lt >> 2)] = dob[c];
+      if (lt < K) sGam[b][lt] = r1.g;
+    };
+    auto stage2 = [&]() {
+#pragma unroll
+      for (int m = 0; m < NBQ; ++m) {
+        const int bl = lt + kBT * m, br = 4 * (bl / (K / 4)), bc = 4 * (bl % (K / 4));
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          *reinterpret_cast<bf16x4*>(sQGT + (bc + c) * PC + br) =
+              to_bf16x4(floatx4{rQG[m][0][c], rQG[m][1][c], rQG[m][2][c], rQG[m][3][c]});
+          *reinterpret_cast<bf16x4*>(sWT + (bc + c) * PC + br) =
+              to_bf16x4(floatx4{rW[m][0][c], rW[m][1][c], rW[m][2][c], rW[m][3][c]});
+        }
+      }
+    };
+    // group 1 has two register sets: set cur holds chunk cc - 1 at step cc and
+    // is refilled with chunk cc - 3 once staged (two chunks of latency)
+    auto step = [&](int cc, G1& cur) {
+      __syncthreads();  // A
+      bf16 rS[NSC];
+#pragma unroll
+      for (int m = 0; m < NSC; ++m) rS[m] = sdST[(lt & 15) * PK + (lt >> 4) + 16 * m];
+      __syncthreads();  // B
+      float* sl = slab_of(a, p0 + cc, h);
+      // the gradient of the chunk-end state, as the recurrence used it (bf16)
+#pragma unroll
+      for (int m = 0; m < NSC; ++m)
+        reinterpret_cast<bf16*>(sl + o.dS)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
       if (cc > 0) stage1(cur, (cc - 1) & 1);
       fetch1(cur, cc - 3);
       __syncthreads();  // C
@@ -1030,7 +1232,6 @@ __device__ __forceinline__ void zero_acc(floatx4 (&acc)[BM][BN]) {
     for (int bn = 0; bn < BN; ++bn) acc[bm][bn] = zero4();
 }
 
-__device__ __forceinline__ bf16x4 to_bf16x4(floatx4 x) { return __builtin_convertvector(x, bf16x4); }
 
 // fp32 [ROWS][COLS] matrix (row-major, global) <-> registers, 4 consecutive
 // elements per access; thread t takes groups t, t + kMT, ...
@@ -1923,7 +2124,10 @@ hipError_t launch_k(const BwdArgs& a, int nitems, int stages, hipStream_t s) {
   if (a.nunits > 0) {
     if ((stages & 2) && nitems > 0)
       hipLaunchKernelGGL(bwd_states_fwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
-    if (stages & 4) hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
+    if (stages & 4) {
+      if (a.bf16_qkv) hipLaunchKernelGGL(bwd_states_bwd_bf16_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
+      else hipLaunchKernelGGL(bwd_states_bwd_kernel<K>, dim3(sgrid), dim3(2 * kBT), 0, s, a);
+    }
   }
   if ((stages & 8) && nitems > 0) {
     if (a.bf16_qkv) {
