@@ -13,6 +13,7 @@ struct GemmArgs {
   int64_t M, N, K, lda, ldb, ldc;
   int ntm, ntn;        // tiles along M and N (set by the launcher)
   int vec_out;         // C rows 16-byte aligned: bf16 C staged for row stores (set by the launcher)
+  int vec4;            // runs of 4 elements of C aligned to their size: vector stores (set by the launcher)
   // optional output-gate epilogue (bf16 C only): with norm_o set, the product G
   // is not stored; instead C[m, n] = o[m, n] * rsqrt(mean over n's head of o^2
   // + norm_eps) * norm_w[n % norm_d] * sigmoid(G[m, n]), heads of norm_d columns
@@ -24,6 +25,8 @@ struct GemmArgs {
 };
 
 // C = A B^T on MFMA (bf16 operands, fp32 accumulation); out_f32 selects fp32 C.
+// K <= 128 takes a kernel of its own (whole K per pass, several workgroups per
+// CU), larger K the 256 x 256 tiled pipeline.
 // With a.norm_o set (bf16 C, 16-byte aligned rows of C and o, ldc and ldo
 // multiples of 8, N a multiple of norm_d) the output-gate epilogue runs instead
 // of the plain store; hipErrorInvalidValue if those conditions do not hold.

@@ -39,6 +39,7 @@
 // rows: 32 store instructions per lane instead of 256 two-byte ones.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdint>
 
 #include "kda_device.h"
@@ -57,6 +58,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ floatx4 zero4f() { return floatx4{0.f, 0.f, 0.f, 0.f}; }
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx16 zero16() {
   floatx16 z;
@@ -429,6 +431,264 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_nt_kernel(GemmArgs 
   }
 }
 
+// ---------------------------------------------------------------------------
+// K <= 128 (the layer's rank-r up-projections): the whole K of a tile is one
+// pass of 8 k steps, so the product is cheap and the kernel is bound by its
+// output writes and, with the output-gate epilogue, by reading o. The 256 x 256
+// pipeline above holds one workgroup per CU, and all of them reach their
+// epilogue at once: HBM then takes the stores of every tile in a burst and
+// idles during the products and the next tile's first loads.
+//
+// Here a workgroup of 4 waves keeps the B tile of one 128-column block in LDS
+// (32 KB, loaded once) and walks row tiles of 128 rows; two or three such
+// workgroups share a CU, so one's loads and stores overlap another's products.
+// Wave w computes rows 32 w .. 32 w + 31 against the 128 columns as 4 tiles of
+// v_mfma_f32_32x32x16_bf16. The A fragments of a row tile (8 x 16 bytes per
+// lane) come straight from global memory into registers, the next tile's
+// issued before this tile's epilogue.
+//
+// Every global access of the epilogue covers whole 128-byte lines:
+// - fp32 C keeps A as the first MFMA operand (element r of lane l is row
+//   8 (r / 4) + 4 (l / 32) + r % 4, column l % 32 of a tile), so one store
+//   instruction writes 128 contiguous bytes of each of two rows;
+// - bf16 C takes B first (lane l holds row l % 32 at runs of four columns).
+//   With the output-gate epilogue, sigmoid of the product is staged per wave in
+//   LDS (fp16, 8 KB) and the rows are then processed as pieces: lanes 0-31 hold
+//   columns 4 (l % 32) .. + 3 of one row and lanes 32-63 of the next, so o is
+//   read as 512 contiguous bytes per row (issued before the products) and y
+//   written as 256; a head's sum of squares is a reduction over D / 4 lanes.
+//
+// B in LDS: row r (column n0 + r of C) holds 16 chunks of 8 bf16, chunk ch at
+// byte 256 r + 16 (ch ^ (r % 16)): the 16 lanes of one read phase take rows
+// r .. r + 15 at one chunk and hit 16 distinct 4-bank groups. The gate stage
+// uses the same row format (128 fp16 per row).
+//
+// Workgroup mapping: id b runs on XCD b % 8; the workgroups of XCD x take the
+// row tiles congruent to x mod 8 for every column block, so each A tile is
+// read from HBM once and then served by that XCD's L2.
+constexpr int kSBM = 128, kSBN = 128;
+
+// sum of x over the n consecutive lanes of an aligned group (n = 16 or 32):
+// lane pair and pair-of-pair swaps, the mirror within each 8 lanes and within
+// each 16 (each step leaves every lane with its group's partial sum), then the
+// other 16-lane half for n = 32
+__device__ __forceinline__ float group_sum(float x, int n) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false));
+  if (n == 32) x += __shfl_xor(x, 16, 64);
+  return x;
+}
+
+template <typename TC, bool NORM>
+__global__ __launch_bounds__(kGemmThreads, NORM ? 2 : 3) void gemm_smallk_kernel(GemmArgs a, int cpw) {
+  constexpr bool kTr = sizeof(TC) == 2;   // B as the first operand
+  __shared__ __attribute__((aligned(16))) char sB[kSBN * 256];
+  __shared__ __attribute__((aligned(16))) char sG[NORM ? 4 * 32 * 256 : 16];   // gate stage, 8 KB per wave
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int x = bid & 7, sl = bid >> 3;
+  const int cb = __builtin_amdgcn_readfirstlane(sl % a.ntn);
+  const int sub = __builtin_amdgcn_readfirstlane(sl / a.ntn);
+  const int64_t n0 = (int64_t)cb * kSBN;
+  const bf16* A = static_cast<const bf16*>(a.A);
+  const bf16* B = static_cast<const bf16*>(a.B);
+  const int kch = (int)(a.K / 8);  // 16-byte chunks of K (K is a multiple of 8)
+
+  // B tile of this column block, zero past N and past K
+  for (int e = tid; e < kSBN * 16; e += kGemmThreads) {
+    const int r = e >> 4, ch = e & 15;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n0 + r < a.N && ch < kch) v = *reinterpret_cast<const u32x4*>(B + (n0 + r) * a.ldb + ch * 8);
+    *reinterpret_cast<u32x4*>(sB + r * 256 + ((ch ^ (r & 15)) << 4)) = v;
+  }
+  __syncthreads();
+
+  const int64_t step = 8 * (int64_t)cpw;
+  int64_t tm = x + 8 * (int64_t)sub;
+  if (tm >= a.ntm) return;
+
+  const int orow = lane & 31, og = lane >> 5;
+  const int key = orow & 15;
+  // A fragments of row tile t: lane l reads row 32 w + l % 32, chunk 2 s + l / 32
+  // for k step s, through a buffer resource over the tile's rows (rows past M
+  // read as zero); chunks past K are zeroed by a select
+  bf16x8 fa[8];
+  auto load_a = [&](int64_t t) {
+    const int64_t m0 = t * kSBM;
+    const int64_t rows = a.M - m0 < kSBM ? a.M - m0 : kSBM;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16*>(A + m0 * a.lda), (short)0, (int)(rows * a.lda * 2), 0x00020000);
+    const int voff = (int)(((32 * w + orow) * a.lda + og * 8) * 2);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 32 * s, 0));
+      fa[s] = __builtin_bit_cast(bf16x8, 2 * s + og < kch ? v : u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  load_a(tm);
+  TC* C = static_cast<TC*>(a.C);
+  // output-gate epilogue: this lane's four columns n0 + 4 (l % 32) .. + 3 and their weights
+  const int pc = 4 * orow;
+  const bool pcol = n0 + pc < a.N;
+  floatx4 nw = zero4f();
+  if constexpr (NORM) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) nw[e] = a.norm_w[(pc + e) % a.norm_d];
+  }
+  char* gst = sG + (NORM ? w * 32 * 256 : 0);
+
+  for (; tm < a.ntm; tm += step) {
+    const int64_t r0 = tm * kSBM + 32 * w;   // first row of this wave
+    // o for the epilogue, issued ahead of the products: piece i is row
+    // r0 + 2 i + l / 32 at columns n0 + 4 (l % 32) .. + 3. o and C go through
+    // buffer resources over the wave's 32 rows (rows past M lie outside them:
+    // loads read zero, stores are dropped); a lane whose columns lie past N
+    // points its offset past the end too
+    floatx4 ov[16];
+    __amdgpu_buffer_rsrc_t rc;
+    int coff = 0;
+    if constexpr (NORM) {
+      const int64_t left = a.M - r0, nrow = left < 0 ? 0 : (left < 32 ? left : 32);
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(a.norm_o + r0 * a.ldo + n0), (short)0, (int)(nrow * a.ldo * 4), 0x00020000);
+      rc = __builtin_amdgcn_make_buffer_rsrc(C + r0 * a.ldc + n0, (short)0, (int)(nrow * a.ldc * 2), 0x00020000);
+      const int ooff = pcol ? (int)((og * a.ldo + pc) * 4) : 0x40000000;
+      coff = pcol ? (int)((og * a.ldc + pc) * 2) : 0x40000000;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        ov[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(ro, ooff, (int)(2 * i * a.ldo * 4), 0));
+    }
+    floatx16 acc[4];
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[y] = zero16();
+    // B fragments one k step ahead of the products (two register sets; left
+    // to itself the compiler hoists all 32 reads and the registers overflow)
+    auto read_b = [&](int s, bf16x8 (&fb)[4]) {
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        fb[y] = *reinterpret_cast<const bf16x8*>(sB + y * 32 * 256 + orow * 256 + (((2 * s + og) ^ key) << 4));
+    };
+    bf16x8 fb[2][4];
+    read_b(0, fb[0]);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s + 1 < 8) read_b(s + 1, fb[(s + 1) & 1]);
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+        acc[y] = kTr ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[s & 1][y], fa[s], acc[y], 0, 0, 0)
+                     : __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s], fb[s & 1][y], acc[y], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the next row tile's A fragments (the last tile reloads its own)
+    load_a(tm + step < a.ntm ? tm + step : tm);
+
+    if constexpr (NORM) {
+      // stage sigmoid(G) for this wave's 32 rows: lane l writes row l % 32 at
+      // columns 32 y + 8 q + 4 (l / 32) .. + 3, 8 bytes into chunk 4 y + q
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          half4 gv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) gv[e] = (_Float16)(1.f / (1.f + __expf(-acc[y][4 * q + e])));
+          *reinterpret_cast<half4*>(gst + orow * 256 + (((4 * y + q) ^ key) << 4) + 8 * og) = gv;
+        }
+      // the stage is this wave's own: an LDS wait orders its reads after the writes
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      const int dl = a.norm_d / 4;   // lanes per head
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int rw = 2 * i + og;
+        const half4 gv = *reinterpret_cast<const half4*>(gst + rw * 256 + (((orow >> 1) ^ (rw & 15)) << 4) +
+                                                         8 * (orow & 1));
+        float ss = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss += ov[i][e] * ov[i][e];
+        const float inv = 1.f / sqrtf(group_sum(ss, dl) / (float)a.norm_d + a.norm_eps);
+        bf16x4 yv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) yv[e] = (bf16)(ov[i][e] * inv * nw[e] * (float)gv[e]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, yv), rc, coff, (int)(2 * i * a.ldc * 2), 0);
+      }
+    } else if constexpr (kTr) {
+      // bf16 C without the gate: runs of four columns of row r0 + l % 32
+      const int64_t row = r0 + orow;
+      if (row < a.M) {
+#pragma unroll
+        for (int y = 0; y < 4; ++y)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = n0 + 32 * y + 8 * q + 4 * og;
+            if (a.vec4 && col + 4 <= a.N) {
+              bf16x4 o;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[e] = (bf16)acc[y][4 * q + e];
+              *reinterpret_cast<bf16x4*>(C + row * a.ldc + col) = o;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < a.N) store_out<TC>(C + row * a.ldc + col + e, acc[y][4 * q + e]);
+            }
+          }
+      }
+    } else {
+      // fp32 C: element r of tile y is row r0 + 8 (r / 4) + 4 (l / 32) + r % 4,
+      // column n0 + 32 y + l % 32
+      const bool full = r0 + 32 <= a.M && n0 + kSBN <= a.N;   // uniform
+#pragma unroll
+      for (int y = 0; y < 4; ++y) {
+        const int64_t col = n0 + 32 * y + orow;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = r0 + 8 * (r >> 2) + 4 * og + (r & 3);
+          if (full || (row < a.M && col < a.N)) store_out<TC>(C + row * a.ldc + col, acc[y][r]);
+        }
+      }
+    }
+  }
+}
+
+// resident workgroups per CU of one instantiation, computed once per process
+template <typename TC, bool NORM>
+static int smallk_occupancy() {
+  static std::atomic<int> occ_cache{-1};
+  int occ = occ_cache.load(std::memory_order_relaxed);
+  if (occ < 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, gemm_smallk_kernel<TC, NORM>, kGemmThreads, 0) !=
+            hipSuccess || n < 1)
+      n = 1;
+    occ = n;
+    occ_cache.store(n, std::memory_order_relaxed);
+  }
+  return occ;
+}
+
+template <typename TC, bool NORM>
+static hipError_t launch_smallk(GemmArgs a, hipStream_t s) {
+  a.ntm = (int)((a.M + kSBM - 1) / kSBM);
+  a.ntn = (int)((a.N + kSBN - 1) / kSBN);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  // resident workgroups per XCD, split evenly over the column blocks
+  const int per_xcd = smallk_occupancy<TC, NORM>() * cus / 8;
+  int cpw = per_xcd / a.ntn;
+  if (cpw < 1) cpw = 1;
+  const int64_t row_groups = ((int64_t)a.ntm + 7) / 8;   // row tiles per XCD and column block
+  if (cpw > row_groups) cpw = (int)row_groups;
+  const dim3 grid((unsigned)(8 * (int64_t)a.ntn * cpw)), block(kGemmThreads);
+  hipLaunchKernelGGL((gemm_smallk_kernel<TC, NORM>), grid, block, 0, s, a, cpw);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gemm_bf16(const GemmArgs& a0, int out_f32, hipStream_t s) {
@@ -442,13 +702,19 @@ hipError_t launch_gemm_bf16(const GemmArgs& a0, int out_f32, hipStream_t s) {
   const int nblk8 = (nbm * nbn + 7) / 8 * 8;   // blocks, padded to whole rounds of 8 XCDs
   const dim3 grid((unsigned)(nblk8 * kGroupM * kGroupN)), block(kGemmThreads);
   const bool ktail = a.K % kBK != 0;
+  const bool smallk = a.K <= kSBN;
   if (a.norm_o) {
     if (out_f32 || !a.vec_out || !a.norm_w || !(a.norm_d == 64 || a.norm_d == 128) || a.N % a.norm_d ||
         a.ldo % 8 || reinterpret_cast<uintptr_t>(a.norm_o) % 16)
       return hipErrorInvalidValue;
+    if (smallk) return launch_smallk<bf16, true>(a, s);
     if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, true, true>), grid, block, 0, s, a);
     else hipLaunchKernelGGL((gemm_bf16_nt_kernel<bf16, false, true>), grid, block, 0, s, a);
     return hipGetLastError();
+  }
+  if (smallk) {
+    a.vec4 = a.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(a.C) % (out_f32 ? 16 : 8) == 0;
+    return out_f32 ? launch_smallk<float, false>(a, s) : launch_smallk<bf16, false>(a, s);
   }
   if (out_f32) {
     if (ktail) hipLaunchKernelGGL((gemm_bf16_nt_kernel<float, true>), grid, block, 0, s, a);

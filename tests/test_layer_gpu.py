@@ -60,6 +60,21 @@ def test_layer_small_matches_oracle(D):
     assert eo <= TOL_LAYER and ey <= TOL_LAYER
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_layer_partial_row_tile_matches_oracle(D):
+    """B T = 320 tokens: the rank-r projections end in a partial 128-row tile
+    whose last two 32-row blocks lie wholly past the end."""
+    B, T, M, H, r = 1, 320, 128, 3, 24
+    _say(f"layer B={B} T={T} M={M} H={H} D={D} r={r}")
+    x, w = layer_inputs(B=B, T=T, M=M, H=H, D=D, rank=r, seed=43 + D)
+    layer, y = run_layer(x, w, H, D)
+    ref, inter = orc.kda_layer_ref(x, w, H, D)
+    eo = rel_err(host(layer.core_out), inter["o"])
+    ey = rel_err(host(y), ref)
+    _say(f"  rel err core o={eo:.2e} x_new={ey:.2e}")
+    assert eo <= TOL_LAYER and ey <= TOL_LAYER
+
+
 def test_layer_packed_projection_weights_bitwise_equal():
     """Input-projection weights packed back to back (read in place by the GEMM)
     and as four separate tensors (copied into the workspace at every call) give
