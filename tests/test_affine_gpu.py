@@ -72,6 +72,24 @@ def test_affine_summary_matches_oracle(dtype, K, varlen):
     assert em <= TOL[dtype] and en <= TOL[dtype]
 
 
+def test_affine_summary_fp32_many_sequences():
+    """40 sequences x 2 heads in fp32 at K = 128: more stage 3+4 workgroups than
+    CUs, so the summary passes run in rounds."""
+    import kimi_delta_attention_03_amd as kda
+    import torch
+    lengths = np.random.default_rng(72).integers(0, 200, size=40)
+    x = core_inputs(1, None, 2, 128, 128, dtype="fp32", seed=73, lengths=lengths, g_low=-0.05)
+    _say("affine summary fp32 K=128, 40 sequences")
+    cu = torch.from_numpy(x.cu_seqlens.astype(np.int32)).to("cuda:0")
+    M, N = kda.affine_summary(to_dev(x.q, torch.float32), to_dev(x.k, torch.float32), to_dev(x.v, torch.float32),
+                              to_dev(x.g, torch.float32), to_dev(x.beta, torch.float32), scale=x.scale, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    M_ref, N_ref = oracle_summary(x)
+    em, en = rel_err(host(M), M_ref), rel_err(host(N), N_ref)
+    _say(f"  rel err M={em:.2e} N={en:.2e}")
+    assert em <= TOL["fp32"] and en <= TOL["fp32"]
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_context_parallel_merge_on_one_gpu(dtype):
     """Two halves of each sequence summarised independently (as two ranks would),

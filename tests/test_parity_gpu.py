@@ -53,6 +53,22 @@ def test_small_multi_chunk(dtype, K):
     check(x)
 
 
+@pytest.mark.parametrize("varlen", [False, True], ids=["fixed", "varlen"])
+def test_fp32_more_workgroups_than_cus(varlen):
+    """fp32 at K = 128 with more (sequence, head) pairs than one stage 3+4
+    workgroup per CU covers (8 column blocks each, 256 CUs), so the workgroups
+    run in rounds; the variable-length case adds ragged last chunks and empty
+    and one-token sequences."""
+    if varlen:
+        lengths = np.random.default_rng(31).integers(0, 260, size=40)
+        lengths[[2, 17]] = [0, 1]
+        x = core_inputs(1, None, 2, 128, 128, dtype="fp32", seed=32, init_std=0.1, lengths=lengths)
+    else:
+        x = core_inputs(3, 320, 12, 128, 128, dtype="fp32", seed=33, init_std=0.1)
+    _say(f"fp32 K=128 many units varlen={varlen} q={x.q.shape}")
+    check(x)
+
+
 def test_workload0_tiny_fp32():
     _say("workload 0: B=1 H=2 T=256 K=V=64 fp32")
     check(workload(0))
