@@ -157,7 +157,8 @@ typedef struct {
   size_t off_chunk_table;  /* varlen: int32 pairs (first token, valid length) per chunk slot */
   size_t off_seq_table;    /* varlen: int32 pairs (first chunk slot, chunk count) per sequence */
   size_t off_order;        /* varlen: sequences ordered longest first */
-  int32_t segments;        /* kda_chunk_fwd runs fixed-length inputs in this many segments along T */
+  int32_t segments;        /* kda_chunk_fwd runs fixed-length bf16 inputs in this many segments along T
+                              (1 for fp32 and variable-length inputs) */
   int32_t segment_chunks;  /* chunks per row in each segment (the last may be shorter); the records
                               of one segment fill the chunk slots from 0 */
 } kda_workspace_info;

@@ -205,14 +205,17 @@ kda_status do_stage34(const kda_fwd_params* p, const float* init, void* o, float
   return KDA_OK;
 }
 
-// Fixed-length inputs are processed in segments of whole chunks along T: stage
-// 1+2 of a segment, then stage 3+4 of it, the fp32 state handed from one
+// Fixed-length bf16 inputs are processed in segments of whole chunks along T:
+// stage 1+2 of a segment, then stage 3+4 of it, the fp32 state handed from one
 // segment to the next through two buffers in the workspace (an exact hand-off:
 // stage 3+4 keeps the state in fp32 throughout). A segment's records (about
 // kSegmentRecordBytes) are read back by stage 3+4 while they still sit in the
 // 256 MB memory-side cache, instead of from HBM after the whole problem's
-// records have streamed through it. The result is bitwise the same for any
-// segmentation, since every chunk's arithmetic is unchanged.
+// records have streamed through it: with bf16 operands stage 3+4 is bound by
+// the delivery of its records. With fp32 operands it is bound by its fp32
+// products instead, and the segments' extra launch ramps cost more than the
+// cache saves, so fp32 inputs run in one pass. The result is bitwise the same
+// for any segmentation, since every chunk's arithmetic is unchanged.
 constexpr size_t kSegmentRecordBytes = (size_t)144 << 20;
 
 struct SegmentPlan {
@@ -224,7 +227,7 @@ struct SegmentPlan {
 
 SegmentPlan plan_segments(const kda_fwd_params* p, const kda::Layout& L) {
   SegmentPlan sp{1, 0, 0, 0};
-  if (p->num_seqs > 0 || p->B == 0 || p->T == 0) return sp;
+  if (p->num_seqs > 0 || p->B == 0 || p->T == 0 || p->qkv_dtype != KDA_DTYPE_BF16) return sp;
   const int64_t nt = p->T / 64;
   sp.nc = (int)nt;
   const size_t per_chunk = (size_t)p->B * (size_t)p->H * L.rec_bytes;  // records of one chunk index

@@ -228,6 +228,18 @@ def test_backward_workspace_formula(lib):
         assert n.value == info.records_offset + info.chunk_slots * 3 * slab * 4
 
 
+def test_segment_plan_bf16_only(lib):
+    """Long fixed-length bf16 inputs are planned in segments along T; fp32 and
+    variable-length inputs in one pass."""
+    from kimi_delta_attention_03_amd import make_params, workspace_layout
+    bf = workspace_layout(make_params(1, 32768, 32, 128, 128, 1, 1, 1, 128 ** -0.5))
+    assert bf.segments == 8 and bf.segment_chunks == 64
+    f32 = workspace_layout(make_params(4, 8192, 16, 128, 128, 0, 0, 0, 128 ** -0.5))
+    assert f32.segments == 1
+    var = workspace_layout(make_params(1, 32768, 32, 128, 128, 1, 1, 1, 128 ** -0.5, num_seqs=4))
+    assert var.segments == 1
+
+
 def test_backward_rejects_before_launch(lib):
     """Bad stage masks, workspace, pointers and alignment are reported without a launch."""
     p = P()

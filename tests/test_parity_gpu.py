@@ -243,13 +243,13 @@ def test_varlen_many_sequences_unsorted_path():
     assert np.array_equal(fs[[3, 4000]], x.initial_state[[3, 4000]])
 
 
-@pytest.mark.parametrize("dtype,B,T,H", [("bf16", 3, 67 * 64, 16), ("fp32", 2, 66 * 64, 16)])
-def test_segmented_forward_bitwise_equals_one_pass(dtype, B, T, H):
-    """Long fixed-length inputs run in segments along T with the fp32 state handed
-    over in the workspace (kda_chunk_fwd); stage 1+2 and stage 3+4 called once each
-    over the whole problem (kda_chunk_fwd_stage12 / _stage34) compute the same chunks.
-    The two must agree bitwise, with and without final_state; the shapes give 2
-    (uneven) and 3 segments."""
+@pytest.mark.parametrize("dtype,B,T,H,nseg", [("bf16", 3, 67 * 64, 16, 2), ("bf16", 1, 280 * 64, 16, 3)])
+def test_segmented_forward_bitwise_equals_one_pass(dtype, B, T, H, nseg):
+    """Long fixed-length bf16 inputs run in segments along T with the fp32 state
+    handed over in the workspace (kda_chunk_fwd); stage 1+2 and stage 3+4 called
+    once each over the whole problem (kda_chunk_fwd_stage12 / _stage34) compute the
+    same chunks. The two must agree bitwise, with and without final_state; the
+    shapes give 2 uneven segments (34 + 33 chunks) and 3 (94 + 94 + 92)."""
     import kimi_delta_attention_03_amd as kda
     import torch
     _say(f"segmented vs one pass {dtype} B={B} T={T} H={H}")
@@ -257,6 +257,7 @@ def test_segmented_forward_bitwise_equals_one_pass(dtype, B, T, H):
     d = dev_inputs(x)
     args = (d["q"], d["k"], d["v"], d["g"], d["beta"])
     fwd = kda.KdaForward(*args, scale=x.scale, initial_state=d["initial_state"])
+    assert kda.workspace_layout(fwd.params).segments == nseg
     o1, f1 = fwd()
     o1, f1 = o1.clone(), f1.clone()
     fwd.o.zero_()
