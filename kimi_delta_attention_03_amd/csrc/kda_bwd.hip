@@ -529,9 +529,12 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
     // ----------------------------------------------------------- loader waves
     // thread lt loads W and KG as float4 (chunk-row-major), one float4 of the
     // U block and one gamma, and copies K / 16 entries of the chunk-start
-    // state (column lt % 16) to the checkpoint
+    // state to the checkpoint as runs of four columns (rows lt / 4 + 64 m,
+    // columns 4 (lt % 4) .. + 3 of the block): one 8- or 16-byte store per run
+    // rather than four element stores, which cost the CU's vector-memory path
+    // as much as full ones
     const int lt = tid - kBT;
-    constexpr int NSC = K / 16;
+    constexpr int NSR = K / 64;   // runs per thread
     struct Regs { floatx4 w[NF], kg[NF], u; float g; };
     // two register sets: the loads of chunk c + 2 are issued while chunk c
     // computes and staged one chunk later. The chunk index is clamped, so the
@@ -561,20 +564,26 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
     auto step = [&](int cc, Regs& cur, Regs& nxt) {
       __syncthreads();  // A
       fetch(nxt, cc + 2);
-      float rS[NSC];
+      // sST is column-major (column c at c * SP): the 4 reads of a run hit 16
+      // rows x 4 column groups of distinct banks
+      floatx4 rS[NSR];
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) rS[m] = sST[(lt & 15) * SP + (lt >> 4) + 16 * m];
+      for (int m = 0; m < NSR; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rS[m][c] = sST[(4 * (lt & 3) + c) * SP + (lt >> 2) + 64 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
       // with bf16 q/k/v the product kernel reads S as bf16 (its MFMA operand
       // type), so it is stored rounded, in the first half of its slab array
       if (a.bf16_qkv) {
 #pragma unroll
-        for (int m = 0; m < NSC; ++m)
-          reinterpret_cast<bf16*>(sl + o.S)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = (bf16)rS[m];
+        for (int m = 0; m < NSR; ++m)
+          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.S) + ((lt >> 2) + 64 * m) * V + 16 * vb +
+                                     4 * (lt & 3)) = to_bf16x4(rS[m]);
       } else {
 #pragma unroll
-        for (int m = 0; m < NSC; ++m) sl[o.S + ((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+        for (int m = 0; m < NSR; ++m)
+          *reinterpret_cast<floatx4*>(sl + o.S + ((lt >> 2) + 64 * m) * V + 16 * vb + 4 * (lt & 3)) = rS[m];
       }
       if (cc + 1 < nch) stage(cur, (cc + 1) & 1);
     };
@@ -905,7 +914,7 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
   } else {
     // ----------------------------------------------------------- loader waves
     const int lt = tid - kBT;
-    constexpr int NSC = K / 16;
+    constexpr int NSR = K / 64;   // runs of the dS' copy per thread
     // Aqk as 4 x 4 blocks (one per loader thread for C = 64), Qg and W as
     // [C][K] blocks (two per thread at K = 128), staged transposed
     constexpr int NBQ = (C / 4) * (K / 4) / kBT;
@@ -983,15 +992,20 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     // is refilled with chunk cc - 3 once staged (two chunks of latency)
     auto step = [&](int cc, G1& cur) {
       __syncthreads();  // A
-      bf16 rS[NSC];
+      // the gradient of the chunk-end state, as the recurrence used it (bf16),
+      // to the slab as runs of four columns (rows lt / 4 + 64 m), one 8-byte
+      // store per run
+      bf16x4 rS[NSR];
 #pragma unroll
-      for (int m = 0; m < NSC; ++m) rS[m] = sdST[(lt & 15) * PK + (lt >> 4) + 16 * m];
+      for (int m = 0; m < NSR; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) rS[m][c] = sdST[(4 * (lt & 3) + c) * PK + (lt >> 2) + 64 * m];
       __syncthreads();  // B
       float* sl = slab_of(a, p0 + cc, h);
-      // the gradient of the chunk-end state, as the recurrence used it (bf16)
 #pragma unroll
-      for (int m = 0; m < NSC; ++m)
-        reinterpret_cast<bf16*>(sl + o.dS)[((lt >> 4) + 16 * m) * V + 16 * vb + (lt & 15)] = rS[m];
+      for (int m = 0; m < NSR; ++m)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.dS) + ((lt >> 2) + 64 * m) * V + 16 * vb +
+                                   4 * (lt & 3)) = rS[m];
       if (cc > 0) stage1(cur, (cc - 1) & 1);
       fetch1(cur, cc - 3);
       __syncthreads();  // C
