@@ -235,8 +235,8 @@ def relation_kk(kc, bc, rho):
     """L[h, i, j] = beta_i * sum_d k_{i,d} k_{j,d} rho[i,j,d], j < i.
 
     [Tokamax] 9.1.5: L = StrictTril(D_beta K+ (K-)^T); the beta of the later
-    position i multiplies row i ([K3]: "multiplied by the future position's
-    beta").
+    position i multiplies row i ([K3], section "Constructing the triangular
+    interaction system", states the same row scaling).
     """
     c = kc.shape[0]
     strict = np.tril(np.ones((c, c)), -1)
@@ -272,8 +272,9 @@ def wy_factors(A, kc, vc, bc, G):
 def gated_keys(kc, G):
     """kg_r = k_r * exp(G_C - G_r): each write carried to the chunk end.
 
-    [Tokamax] 9.1.5 (bar K); [K3] "K_decay transports each within-chunk key
-    to the end of the chunk". Shape (H, c, K).
+    [Tokamax] 9.1.5 (bar K); [K3], section "Carrying one state between
+    chunks": the decayed keys move every key of the chunk forward to the
+    chunk's last position. Shape (H, c, K).
     """
     return (kc * np.exp(G[-1][None] - G)).transpose(1, 0, 2)
 
