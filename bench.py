@@ -604,7 +604,8 @@ def main():
                      "traffic": measured_traffic(cfg["name"], dom),
                      "alg_bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
         "record": {"library": build_info(),
-                   "tokens_logical": tokens, "tokens_chunk_aligned": aligned, "segments": seg,
+                   "tokens_logical": tokens, "tokens_chunk_aligned": aligned, "sequence_lengths": seg,
+                   "t_segments": {"count": nseg, "chunks_per_segment": int(info.segment_chunks) if nseg > 1 else None},
                    "flags": {"use_qk_l2norm": False, "gate": "log_decay (g given)",
                              "initial_state": init is not None, "final_state": True, "chunk_size": 64},
                    "torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
