@@ -270,7 +270,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     const float G = sG[r * KP + d], Gl = sG[(C - 1) * KP + d];
     const float qn = sQ[r * KP + d], kn = sK[r * KP + d];
     const float eg = __expf(G);
-    sl[o.qg + e] = a.scale * qn * eg;
+    if (qf32) sl[o.qg + e] = a.scale * qn * eg;
     sl[o.kg + e] = kn * __expf(Gl - G);
     sl[o.kb + e] = sB[r] * kn * eg;
   }
@@ -280,6 +280,16 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     for (int m = 0; m < NE; ++m) {
       const int e = tid + kBW * m;
       sl[o.vb + e] = sB[e / V] * vv[m];
+    }
+  }
+  // with bf16 inputs only the bf16 state-gradient pass reads Qg, as a bf16 MFMA
+  // operand with the chunk row contiguous: stored so, Qg^T [K][C] in bf16 in the
+  // first half of its slab array (the same fp32 value, rounded once)
+  if (!qf32) {
+    bf16* qgt = reinterpret_cast<bf16*>(sl + o.qg);
+    for (int e = tid; e < C * K; e += kBW) {
+      const int d = e / C, r = e % C;
+      qgt[e] = (bf16)(a.scale * sQ[r * KP + d] * __expf(sG[r * KP + d]));
     }
   }
   if (tid < K) sl[o.gam + tid] = __expf(sG[(C - 1) * KP + tid]);
@@ -417,6 +427,10 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         sl[o.w + ii * K + d] = accW[r];
         sl[o.u + ii * V + d] = accU[r];
       }
+      // bf16 inputs: also W^T [K][C] in bf16 for the bf16 state-gradient pass, in
+      // the slab array of Vb (which only fp32 inputs use)
+      if (!qf32)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.vb) + d * C + 16 * ib + 4 * gq) = to_bf16x4(accW);
     }
   }
 }
@@ -915,10 +929,14 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     // ----------------------------------------------------------- loader waves
     const int lt = tid - kBT;
     constexpr int NSR = K / 64;   // runs of the dS' copy per thread
-    // Aqk as 4 x 4 blocks (one per loader thread for C = 64), Qg and W as
-    // [C][K] blocks (two per thread at K = 128), staged transposed
-    constexpr int NBQ = (C / 4) * (K / 4) / kBT;
-    static_assert(NBQ * kBT == (C / 4) * (K / 4) && (C / 4) * (C / 4) <= kBT, "block split");
+    // Aqk as 4 x 4 blocks (one per loader thread for C = 64), staged
+    // transposed; Qg^T and W^T come from the slab already in bf16 [K][C] (the
+    // chunk-term kernel writes them so for bf16 inputs) and are copied as
+    // 16-byte pieces: piece q = lt + 256 m is row q / (C / 8), columns
+    // 8 (q % (C / 8)) .. + 7
+    constexpr int NQP = K * C / 8 / kBT;
+    static_assert(NQP * kBT == K * C / 8 && (C / 4) * (C / 4) <= kBT, "piece split");
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     struct G1 {
       floatx4 kg[NF], aq[4];
@@ -926,7 +944,7 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
       bool ok;
       float g;
     };
-    floatx4 rQG[NBQ][4], rW[NBQ][4];
+    u32x4 rQG[NQP], rW[NQP];
     const bool aq_has = lt < (C / 4) * (C / 4);
     const int aq_r = 4 * (lt / (C / 4)), aq_c = 4 * (lt % (C / 4));
     // loads are unconditional: the chunk index is clamped to 0
@@ -948,14 +966,12 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     auto fetch2 = [&](int cc) {
       cc = cc > 0 ? cc : 0;
       const float* sl = slab_of(a, p0 + cc, h);
+      const bf16* qgt = reinterpret_cast<const bf16*>(sl + o.qg);
+      const bf16* wt = reinterpret_cast<const bf16*>(sl + o.vb);
 #pragma unroll
-      for (int m = 0; m < NBQ; ++m) {
-        const int bl = lt + kBT * m, br = 4 * (bl / (K / 4)), bc = 4 * (bl % (K / 4));
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          rQG[m][r] = *reinterpret_cast<const floatx4*>(sl + o.qg + (br + r) * K + bc);
-          rW[m][r] = *reinterpret_cast<const floatx4*>(sl + o.w + (br + r) * K + bc);
-        }
+      for (int m = 0; m < NQP; ++m) {
+        rQG[m] = *reinterpret_cast<const u32x4*>(qgt + 8 * (lt + kBT * m));
+        rW[m] = *reinterpret_cast<const u32x4*>(wt + 8 * (lt + kBT * m));
       }
     };
     auto stage1 = [&](const G1& r1, int b) {
@@ -977,15 +993,10 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     };
     auto stage2 = [&]() {
 #pragma unroll
-      for (int m = 0; m < NBQ; ++m) {
-        const int bl = lt + kBT * m, br = 4 * (bl / (K / 4)), bc = 4 * (bl % (K / 4));
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          *reinterpret_cast<bf16x4*>(sQGT + (bc + c) * PC + br) =
-              to_bf16x4(floatx4{rQG[m][0][c], rQG[m][1][c], rQG[m][2][c], rQG[m][3][c]});
-          *reinterpret_cast<bf16x4*>(sWT + (bc + c) * PC + br) =
-              to_bf16x4(floatx4{rW[m][0][c], rW[m][1][c], rW[m][2][c], rW[m][3][c]});
-        }
+      for (int m = 0; m < NQP; ++m) {
+        const int q = lt + kBT * m, k = q / (C / 8), j0 = 8 * (q % (C / 8));
+        *reinterpret_cast<u32x4*>(sQGT + k * PC + j0) = rQG[m];
+        *reinterpret_cast<u32x4*>(sWT + k * PC + j0) = rW[m];
       }
     };
     // group 1 has two register sets: set cur holds chunk cc - 1 at step cc and

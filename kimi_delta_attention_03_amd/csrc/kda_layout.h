@@ -101,8 +101,9 @@ static inline Layout make_layout(int K, int V, int elem, int64_t B, int64_t T, i
 struct BwdSlab {
   // chunk terms recomputed from the inputs (natural-log gates; the normalised q,
   // k and the gate cumsum are rebuilt where needed and not stored)
-  size_t qg, kg, w, kb;              // [64][K]: s q e^G; k e^(Gl-G); A Kb; beta k e^G
-  size_t u, vb;                      // [64][V]: A Vb; beta v
+  size_t qg, kg, w, kb;              // [64][K]: s q e^G (bf16 inputs: its transpose [K][64] in bf16,
+                                     // first half); k e^(Gl-G); A Kb; beta k e^G
+  size_t u, vb;                      // [64][V]: A Vb; beta v (bf16 inputs: W^T [K][64] in bf16, first half)
   size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
   size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
   // chunk-start state and the gradient of the chunk-end state
