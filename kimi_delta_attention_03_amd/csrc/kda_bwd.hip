@@ -271,7 +271,11 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     const float qn = sQ[r * KP + d], kn = sK[r * KP + d];
     const float eg = __expf(G);
     if (qf32) sl[o.qg + e] = a.scale * qn * eg;
-    sl[o.kg + e] = kn * __expf(Gl - G);
+    const float kgv = kn * __expf(Gl - G);
+    sl[o.kg + e] = kgv;
+    // bf16 inputs: a bf16 copy for the bf16 state-gradient pass (its MFMA
+    // operand type), in the second half of the Vb array
+    if (!qf32) reinterpret_cast<bf16*>(sl + o.vb)[K * C + e] = (bf16)kgv;
     sl[o.kb + e] = sB[r] * kn * eg;
   }
   // Vb for the fp32 product kernel (the bf16 one rebuilds it from v and beta)
@@ -316,6 +320,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         accQ = mfma4(sQ[i * KP + d] * ei, kj, accQ);
         accK = mfma4(sK[i * KP + d] * ei, kj, accK);
       }
+      floatx4 aqv;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ii = 16 * ib + 4 * gq + r, jj = 16 * jb + xi;
@@ -324,7 +329,14 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         sl[o.aqk + ii * C + jj] = aq;
         sl[o.m + ii * C + jj] = mv;
         sL[ii * CP + jj] = sB[ii] * mv;
+        aqv[r] = aq;
       }
+      // bf16 inputs: Aqk^T [C][C] in bf16 for the bf16 state-gradient pass, in
+      // the array of dQg (which only fp32 inputs use): lane (g, i) holds rows
+      // 16 ib + 4 g .. + 3 of column 16 jb + i
+      if (!qf32)
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.dqg) + (16 * jb + xi) * C + 16 * ib + 4 * gq) =
+            to_bf16x4(aqv);
     }
     // the blocks above the diagonal are zero
     for (int e = tid; e < C * C; e += kBW) {
@@ -333,6 +345,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         sl[o.aqk + e] = 0.f;
         sl[o.m + e] = 0.f;
         sL[ii * CP + jj] = 0.f;
+        if (!qf32) reinterpret_cast<bf16*>(sl + o.dqg)[jj * C + ii] = bf16(0.f);
       }
     }
   }
@@ -929,33 +942,31 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     // ----------------------------------------------------------- loader waves
     const int lt = tid - kBT;
     constexpr int NSR = K / 64;   // runs of the dS' copy per thread
-    // Aqk as 4 x 4 blocks (one per loader thread for C = 64), staged
-    // transposed; Qg^T and W^T come from the slab already in bf16 [K][C] (the
-    // chunk-term kernel writes them so for bf16 inputs) and are copied as
-    // 16-byte pieces: piece q = lt + 256 m is row q / (C / 8), columns
-    // 8 (q % (C / 8)) .. + 7
-    constexpr int NQP = K * C / 8 / kBT;
-    static_assert(NQP * kBT == K * C / 8 && (C / 4) * (C / 4) <= kBT, "piece split");
+    // KG [C][K], Aqk^T [C][C], Qg^T and W^T [K][C] come from the slab already
+    // in bf16 (the chunk-term kernel writes them so for bf16 inputs) and are
+    // copied to LDS as 16-byte pieces: piece q = lt + 256 m of an [R][S] matrix
+    // is row q / (S / 8), columns 8 (q % (S / 8)) .. + 7
+    constexpr int NQP = K * C / 8 / kBT, NAP = C * C / 8 / kBT;
+    static_assert(NQP * kBT == K * C / 8 && NAP * kBT == C * C / 8, "piece split");
     typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     struct G1 {
-      floatx4 kg[NF], aq[4];
+      u32x4 kg[NQP], aq[NAP];
       u32x2 o16;
       bool ok;
       float g;
     };
     u32x4 rQG[NQP], rW[NQP];
-    const bool aq_has = lt < (C / 4) * (C / 4);
-    const int aq_r = 4 * (lt / (C / 4)), aq_c = 4 * (lt % (C / 4));
     // loads are unconditional: the chunk index is clamped to 0
     auto fetch1 = [&](G1& r1, int cc) {
       cc = cc > 0 ? cc : 0;
       const float* sl = slab_of(a, p0 + cc, h);
+      const bf16* kgb = reinterpret_cast<const bf16*>(sl + o.vb) + K * C;
+      const bf16* aqt = reinterpret_cast<const bf16*>(sl + o.dqg);
 #pragma unroll
-      for (int m = 0; m < NF; ++m) r1.kg[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
+      for (int m = 0; m < NQP; ++m) r1.kg[m] = *reinterpret_cast<const u32x4*>(kgb + 8 * (lt + kBT * m));
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        r1.aq[r] = *reinterpret_cast<const floatx4*>(sl + o.aqk + (aq_has ? (aq_r + r) * C + aq_c : 0));
+      for (int m = 0; m < NAP; ++m) r1.aq[m] = *reinterpret_cast<const u32x4*>(aqt + 8 * (lt + kBT * m));
       const ItemB it = chunk_of(a, p0 + cc, h);
       const int r = lt >> 2, c0 = 16 * vb + 4 * (lt & 3);
       r1.ok = r < it.len;
@@ -976,15 +987,14 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_bwd_bf16_kernel(BwdArgs a)
     };
     auto stage1 = [&](const G1& r1, int b) {
 #pragma unroll
-      for (int m = 0; m < NF; ++m) {
-        const int e = 4 * (lt + kBT * m), r = e / K, d = e % K;
-        *reinterpret_cast<bf16x4*>(sKG + r * PK + d) = to_bf16x4(r1.kg[m]);
+      for (int m = 0; m < NQP; ++m) {
+        const int q = lt + kBT * m;
+        *reinterpret_cast<u32x4*>(sKG + (q / (K / 8)) * PK + 8 * (q % (K / 8))) = r1.kg[m];
       }
-      if (aq_has) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          *reinterpret_cast<bf16x4*>(sAqT + (aq_c + c) * PC + aq_r) =
-              to_bf16x4(floatx4{r1.aq[0][c], r1.aq[1][c], r1.aq[2][c], r1.aq[3][c]});
+      for (int m = 0; m < NAP; ++m) {
+        const int q = lt + kBT * m;
+        *reinterpret_cast<u32x4*>(sAqT + (q / (C / 8)) * PC + 8 * (q % (C / 8))) = r1.aq[m];
       }
       const bf16x4 dob = r1.ok ? __builtin_bit_cast(bf16x4, r1.o16) : bf16x4{0, 0, 0, 0};
 #pragma unroll

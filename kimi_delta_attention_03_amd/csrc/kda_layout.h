@@ -103,14 +103,15 @@ struct BwdSlab {
   // k and the gate cumsum are rebuilt where needed and not stored)
   size_t qg, kg, w, kb;              // [64][K]: s q e^G (bf16 inputs: its transpose [K][64] in bf16,
                                      // first half); k e^(Gl-G); A Kb; beta k e^G
-  size_t u, vb;                      // [64][V]: A Vb; beta v (bf16 inputs: W^T [K][64] in bf16, first half)
+  size_t u, vb;                      // [64][V]: A Vb; beta v (bf16 inputs: W^T [K][64] in bf16, then
+                                     // a bf16 copy of kg [64][K])
   size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
   size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
   // chunk-start state and the gradient of the chunk-end state
   size_t S, dS;                      // [K][V] (bf16, in the first half, for bf16 q/k/v)
   // per-chunk gradients
   size_t dO, vn, dvn, dvb;           // [64][V]
-  size_t dqg, dw, dkg, dkb;          // [64][K]
+  size_t dqg, dw, dkg, dkb;          // [64][K] (bf16 inputs: dqg holds Aqk^T [64][64] in bf16)
   size_t daqk, da, t1, dl;           // [64][64]
   size_t dgam;                       // [K]
   size_t floats;                     // slab size
