@@ -1292,6 +1292,28 @@ struct NatStage {
   }
 };
 
+// bf16 [ROWS][COLS] matrix as 16-byte pieces: piece q = t + kMT m is row
+// q / (COLS / 8), columns 8 (q % (COLS / 8)) .. + 7; copied to LDS with rows
+// padded to COLS + 8
+template <int ROWS, int COLS>
+struct PieceStage {
+  static constexpr int N = ROWS * COLS / 8 / kMT;
+  static_assert(N >= 1 && N * 8 * kMT == ROWS * COLS, "whole pieces per thread");
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 v[N];
+  __device__ void load(const bf16* src) {
+#pragma unroll
+    for (int m = 0; m < N; ++m) v[m] = *reinterpret_cast<const u32x4*>(src + 8 * ((int)threadIdx.x + kMT * m));
+  }
+  __device__ void store(bf16* dst) const {
+#pragma unroll
+    for (int m = 0; m < N; ++m) {
+      const int q = (int)threadIdx.x + kMT * m;
+      *reinterpret_cast<u32x4*>(dst + (q / (COLS / 8)) * (COLS + 8) + 8 * (q % (COLS / 8))) = v[m];
+    }
+  }
+};
+
 // fp32 [ROWS][COLS] matrix in 4 x 4 blocks: block b = t + kMT m holds rows
 // 4 (b / (COLS / 4)) + r, columns 4 (b % (COLS / 4)) .. + 3 in v[m][r]; stored
 // to LDS either as is or transposed ([COLS][ROWS + 8])
@@ -1413,8 +1435,11 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
 
   // loads of phase 2, issued with those of phase 1: Aqk, dO (bf16 rows of the
   // chunk; rows past its end are zeroed where they are staged), KG, dS'
-  BlkStage<C, C> rAq;
-  rAq.load(P.AQK);
+  // Aqk^T and KG come from their bf16 copies in the slab (the chunk-term kernel
+  // writes them for the state-gradient pass): the same values this kernel would
+  // round to bf16 itself
+  PieceStage<C, C> rAq;
+  rAq.load(reinterpret_cast<const bf16*>(P.DQG));
   constexpr int NDO = (C / 4) * (V / 4), PDO = (NDO + kMT - 1) / kMT;
   bf16x4 rdO[PDO][4];
   auto do_has = [&](int m) { return NDO % kMT == 0 || tid + kMT * m < NDO; };
@@ -1433,8 +1458,8 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
         }
       }
   }
-  NatStage<C, K> rKG;
-  rKG.load(P.KG);
+  PieceStage<C, K> rKG;
+  rKG.load(reinterpret_cast<const bf16*>(P.VB) + K * C);
   BlkStage<K, V> rdS;
   rdS.load(reinterpret_cast<const bf16*>(P.DS));
 
@@ -1453,7 +1478,7 @@ __global__ __launch_bounds__(kMT) void bwd_chunk_fused_kernel(BwdArgs a) {
   __syncthreads();
 
   // ---- phase 2: dVn = Aqk^T dO + KG dS'
-  rAq.store_t(smem + oAqT);
+  rAq.store(smem + oAqT);
 #pragma unroll
   for (int m = 0; m < PDO; ++m)
     if (do_has(m)) {
