@@ -326,7 +326,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
         const int ii = 16 * ib + 4 * gq + r, jj = 16 * jb + xi;
         const float aq = jj <= ii ? a.scale * accQ[r] : 0.f;
         const float mv = jj < ii ? accK[r] : 0.f;
-        sl[o.aqk + ii * C + jj] = aq;
+        if (qf32) sl[o.aqk + ii * C + jj] = aq;   // bf16 inputs read only the bf16 Aqk^T below
         sl[o.m + ii * C + jj] = mv;
         sL[ii * CP + jj] = sB[ii] * mv;
         aqv[r] = aq;
@@ -342,7 +342,7 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
     for (int e = tid; e < C * C; e += kBW) {
       const int ii = e / C, jj = e % C;
       if (jj / 16 > ii / 16) {
-        sl[o.aqk + e] = 0.f;
+        if (qf32) sl[o.aqk + e] = 0.f;
         sl[o.m + e] = 0.f;
         sL[ii * CP + jj] = 0.f;
         if (!qf32) reinterpret_cast<bf16*>(sl + o.dqg)[jj * C + ii] = bf16(0.f);

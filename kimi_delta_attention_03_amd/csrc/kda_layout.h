@@ -105,7 +105,7 @@ struct BwdSlab {
                                      // first half); k e^(Gl-G); A Kb; beta k e^G
   size_t u, vb;                      // [64][V]: A Vb; beta v (bf16 inputs: W^T [K][64] in bf16, then
                                      // a bf16 copy of kg [64][K])
-  size_t aqk, a, m;                  // [64][64]: Aqk (j <= i), (I + L)^-1, M = L / beta (j < i)
+  size_t aqk, a, m;                  // [64][64]: Aqk (j <= i; fp32 inputs only), (I + L)^-1, M = L / beta (j < i)
   size_t beta, gam, nq, nk;          // [64], [K], [64] row norms of q and k (before the eps clamp)
   // chunk-start state and the gradient of the chunk-end state
   size_t S, dS;                      // [K][V] (bf16, in the first half, for bf16 q/k/v)
