@@ -448,6 +448,15 @@ __global__ __launch_bounds__(kBW) void bwd_prep_kernel(BwdArgs a) {
   }
 }
 
+// 16 bytes per lane from global memory straight into LDS (lane l writes the
+// LDS base + 16 l; the base must be wave-uniform). The host pass, which only
+// emits the launch stub, does not accept the 16-byte form of the builtin.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define KDA_LDS_DMA16(gptr, ldsptr) __builtin_amdgcn_global_load_lds((gptr), (ldsptr), 16, 0, 0)
+#else
+#define KDA_LDS_DMA16(gptr, ldsptr) ((void)0)
+#endif
+
 // ---------------------------------------------------------- chunk-start states
 // One workgroup (8 waves) per (sequence, head, 16-column block) walks the
 // chunks in order. Compute wave w (0..3) keeps state rows [16 TPW w,
@@ -471,7 +480,8 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
   // that a lane reads 4 consecutive reduction indices at once
   constexpr int SP = K + 4, VP = C + 4;
   __shared__ __attribute__((aligned(16))) float sST[16 * SP], sVnT[16 * VP];
-  __shared__ float sGam[2][K];
+  // gamma padded to 1 KB: one direct-to-LDS instruction fills it
+  __shared__ __attribute__((aligned(16))) float sGam[2][256];
   const int tid = threadIdx.x;
   const int lane = tid & 63, gq = lane >> 4, xi = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -554,75 +564,114 @@ __global__ __launch_bounds__(2 * kBT) void bwd_states_fwd_kernel(BwdArgs a) {
     }
   } else {
     // ----------------------------------------------------------- loader waves
-    // thread lt loads W and KG as float4 (chunk-row-major), one float4 of the
-    // U block and one gamma, and copies K / 16 entries of the chunk-start
-    // state to the checkpoint as runs of four columns (rows lt / 4 + 64 m,
-    // columns 4 (lt % 4) .. + 3 of the block): one 8- or 16-byte store per run
-    // rather than four element stores, which cost the CU's vector-memory path
-    // as much as full ones
-    const int lt = tid - kBT;
-    constexpr int NSR = K / 64;   // runs per thread
-    struct Regs { floatx4 w[NF], kg[NF], u; float g; };
-    // two register sets: the loads of chunk c + 2 are issued while chunk c
-    // computes and staged one chunk later. The chunk index is clamped, so the
-    // loads are unconditional and the memory-counter waits stay exact.
-    auto fetch = [&](Regs& r, int cc) {
+    // The chunk operands go from the slab straight into LDS
+    // (global_load_lds_dwordx4: lane l of one instruction writes the 16 bytes at
+    // the LDS base + 16 l), with no register round trip and no LDS write
+    // instructions. One instruction fills 1 KB of a padded LDS array; a lane
+    // whose 16 bytes fall on a row's pad loads the row's first 16 bytes there
+    // (never read). The four loader waves split each array's instructions; the
+    // last one is issued by several waves (same bytes, same data), so every wave
+    // issues the same count and one memory-counter wait per barrier is exact
+    // (a wave's vector-memory loads and stores retire in issue order on this
+    // counter). W and U of chunk c (read before barrier B(c)) are loaded after
+    // B(c - 2), into the buffer chunk c - 2 has finished with; KG and gamma
+    // (read after B(c)) after A(c - 1). Chunk indices are clamped, so the
+    // loads are unconditional.
+    // Thread lt also copies K / 16 entries of the chunk-start state to the
+    // checkpoint as runs of four columns (rows lt / 4 + 64 m, columns
+    // 4 (lt % 4) .. + 3 of the block): one 8- or 16-byte store per run rather
+    // than four element stores, which cost the CU's vector-memory path as much
+    // as full ones.
+    const int lt = tid - kBT, ll = lt & 63, lw = __builtin_amdgcn_readfirstlane(lt >> 6);
+    constexpr int NSR = K / 64;                       // state runs per thread
+    constexpr int NIA = C * KP / 256, NJA = (NIA + 3) / 4;  // 1 KB pieces of W / KG; per wave
+    constexpr int NIU = C * 20 / 256, NJU = (NIU + 3) / 4;  // of the U block
+    constexpr int NKG = NJA + 1, NWU = NJA + NJU;     // DMA instructions per wave and group
+    // a barrier's wait leaves the instructions issued after its group in flight
+    constexpr int NW = NKG + NSR + NWU;
+    static_assert(C * KP % 256 == 0 && C * 20 % 256 == 0 && K <= 256, "LDS arrays must be whole 1 KB pieces");
+    static_assert(NW < 64, "vector-memory count is 6 bits");
+    // s_waitcnt immediates: vector-memory count n (bits 3:0 and 15:14), LDS
+    // count 0 (bits 11:8), export count at its maximum
+    constexpr int kWaitW = (NW & 15) | ((NW >> 4) << 14) | (7 << 4);
+    constexpr int kWaitWU = (NWU & 15) | ((NWU >> 4) << 14) | (7 << 4);
+    constexpr int kWait0 = 7 << 4;
+    // The loader's barriers are bare: the waits each one needs are the explicit
+    // ones before it, while a fenced barrier would also wait for the transfers
+    // of later chunks still in flight. The empty asm statements keep the
+    // compiler from moving memory accesses across the barrier.
+    auto barrier = [] {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    };
+    int offA[NJA], offU[NJU];
+#pragma unroll
+    for (int j = 0; j < NJA; ++j) {
+      const int x = 256 * min(lw + 4 * j, NIA - 1) + 4 * ll;  // float index in the padded array
+      const int r = x / KP, c = x % KP;
+      offA[j] = r * K + (c < K ? c : 0);
+    }
+#pragma unroll
+    for (int j = 0; j < NJU; ++j) {
+      const int x = 256 * min(lw + 4 * j, NIU - 1) + 4 * ll;
+      const int r = x / 20, c = x % 20;
+      offU[j] = r * V + 16 * vb + (c < 16 ? c : 0);
+    }
+    const int offG = ll < K / 4 ? 4 * ll : 0;  // lanes past gamma fill the array's unused tail
+    auto issue_wu = [&](int cc, int b) {
       cc = cc < nch - 1 ? cc : nch - 1;
       const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-      for (int m = 0; m < NF; ++m) {
-        r.w[m] = *reinterpret_cast<const floatx4*>(sl + o.w + 4 * (lt + kBT * m));
-        r.kg[m] = *reinterpret_cast<const floatx4*>(sl + o.kg + 4 * (lt + kBT * m));
-      }
-      r.u = *reinterpret_cast<const floatx4*>(sl + o.u + (lt >> 2) * V + 16 * vb + 4 * (lt & 3));
-      r.g = sl[o.gam + (lt < K ? lt : 0)];
+      for (int j = 0; j < NJA; ++j)
+        KDA_LDS_DMA16(sl + o.w + offA[j], &sW[b][256 * min(lw + 4 * j, NIA - 1)]);
+#pragma unroll
+      for (int j = 0; j < NJU; ++j)
+        KDA_LDS_DMA16(sl + o.u + offU[j], &sU[b][256 * min(lw + 4 * j, NIU - 1)]);
     };
-    auto stage = [&](const Regs& r, int b) {
+    auto issue_kg = [&](int cc, int b) {
+      cc = cc < nch - 1 ? cc : nch - 1;
+      const float* sl = slab_of(a, p0 + cc, h);
 #pragma unroll
-      for (int m = 0; m < NF; ++m) {
-        const int e = 4 * (lt + kBT * m), rr = e / K, d = e % K;
-        *reinterpret_cast<floatx4*>(&sW[b][rr * KP + d]) = r.w[m];
-        *reinterpret_cast<floatx4*>(&sKG[b][rr * KP + d]) = r.kg[m];
-      }
-      *reinterpret_cast<floatx4*>(&sU[b][(lt >> 2) * 20 + 4 * (lt & 3)]) = r.u;
-      if (lt < K) sGam[b][lt] = r.g;
-    };
-    // chunk cc: cur holds chunk cc + 1 (staged after barrier B), nxt receives chunk cc + 2
-    auto step = [&](int cc, Regs& cur, Regs& nxt) {
-      __syncthreads();  // A
-      fetch(nxt, cc + 2);
-      // sST is column-major (column c at c * SP): the 4 reads of a run hit 16
-      // rows x 4 column groups of distinct banks
-      floatx4 rS[NSR];
-#pragma unroll
-      for (int m = 0; m < NSR; ++m)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) rS[m][c] = sST[(4 * (lt & 3) + c) * SP + (lt >> 2) + 64 * m];
-      __syncthreads();  // B
-      float* sl = slab_of(a, p0 + cc, h);
-      // with bf16 q/k/v the product kernel reads S as bf16 (its MFMA operand
-      // type), so it is stored rounded, in the first half of its slab array
-      if (a.bf16_qkv) {
-#pragma unroll
-        for (int m = 0; m < NSR; ++m)
-          *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.S) + ((lt >> 2) + 64 * m) * V + 16 * vb +
-                                     4 * (lt & 3)) = to_bf16x4(rS[m]);
-      } else {
-#pragma unroll
-        for (int m = 0; m < NSR; ++m)
-          *reinterpret_cast<floatx4*>(sl + o.S + ((lt >> 2) + 64 * m) * V + 16 * vb + 4 * (lt & 3)) = rS[m];
-      }
-      if (cc + 1 < nch) stage(cur, (cc + 1) & 1);
+      for (int j = 0; j < NJA; ++j)
+        KDA_LDS_DMA16(sl + o.kg + offA[j], &sKG[b][256 * min(lw + 4 * j, NIA - 1)]);
+      KDA_LDS_DMA16(sl + o.gam + offG, &sGam[b][0]);
     };
     if (nch > 0) {
-      Regs R0, R1;
-      fetch(R0, 0);
-      fetch(R1, 1);
-      stage(R0, 0);
-      for (int cc = 0; cc < nch; cc += 2) {
-        step(cc, R1, R0);
-        if (cc + 1 < nch) step(cc + 1, R0, R1);
+      issue_wu(0, 0);
+      issue_kg(0, 0);
+      issue_wu(1, 1);
+      __builtin_amdgcn_s_waitcnt(kWaitWU);  // chunk 0 has landed
+      for (int cc = 0; cc < nch; ++cc) {
+        const int b = cc & 1;
+        barrier();  // A
+        issue_kg(cc + 1, b ^ 1);
+        // sST is column-major (column c at c * SP): the 4 reads of a run hit 16
+        // rows x 4 column groups of distinct banks
+        floatx4 rS[NSR];
+#pragma unroll
+        for (int m = 0; m < NSR; ++m)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) rS[m][c] = sST[(4 * (lt & 3) + c) * SP + (lt >> 2) + 64 * m];
+        __builtin_amdgcn_s_waitcnt(kWaitW);  // KG and gamma of chunk cc have landed
+        barrier();  // B
+        float* sl = slab_of(a, p0 + cc, h);
+        // with bf16 q/k/v the product kernel reads S as bf16 (its MFMA operand
+        // type), so it is stored rounded, in the first half of its slab array
+        if (a.bf16_qkv) {
+#pragma unroll
+          for (int m = 0; m < NSR; ++m)
+            *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16*>(sl + o.S) + ((lt >> 2) + 64 * m) * V + 16 * vb +
+                                       4 * (lt & 3)) = to_bf16x4(rS[m]);
+        } else {
+#pragma unroll
+          for (int m = 0; m < NSR; ++m)
+            *reinterpret_cast<floatx4*>(sl + o.S + ((lt >> 2) + 64 * m) * V + 16 * vb + 4 * (lt & 3)) = rS[m];
+        }
+        issue_wu(cc + 2, b);
+        __builtin_amdgcn_s_waitcnt(kWaitW);  // W and U of chunk cc + 1 have landed
       }
+      __builtin_amdgcn_s_waitcnt(kWait0);  // no transfer outlives the wave
     }
   }
 }
