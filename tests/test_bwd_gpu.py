@@ -116,6 +116,16 @@ def test_bwd_bf16_k64_varlen_l2norm():
     check(errs, TOL["bf16"])
 
 
+def test_bwd_bf16_k128_varlen_short_sequences():
+    """bf16, K=V=128, sequences of 1, 2 and 3 full chunks and one token: the state
+    passes' loaders prefetch two chunks ahead, so these exercise their clamped
+    loads at every position from the first chunk to past the last."""
+    _say("bwd bf16 K=V=128 varlen [64, 128, 192, 1]")
+    x = core_inputs(1, None, 2, 128, 128, dtype="bf16", seed=38, init_std=0.1, lengths=[64, 128, 192, 1])
+    errs, _ = run_case(x, seed=14)
+    check(errs, TOL["bf16"])
+
+
 def test_bwd_deterministic():
     """Two calls give bitwise-equal gradients."""
     import torch
